@@ -1,0 +1,129 @@
+"""Seeded synthetic inputs for the routed-MoE layer (test and benchmark infrastructure).
+
+Shared by the oracle and by the GPU path's tests and benchmark.  Holds none of
+the layer's arithmetic: every value is a function of (seed, tensor tag, logical
+index) only, so the oracle can regenerate any single expert matrix by index.
+The C implementation is ``gen/gen.c`` (SplitMix64 bits, twelve-uniform
+Irwin-Hall normals); this module is a ctypes wrapper around it.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import _build
+
+# Tensor tags: every logical tensor of a workload gets its own stream.
+TAG_X = 1
+TAG_WR = 2
+TAG_WG = 3
+TAG_WU = 4
+TAG_WD = 5
+TAG_LOGIT = 6
+TAG_RANK = 7
+TAG_MSTAY = 8
+TAG_MZIPF = 9
+TAG_MCHOSEN = 10
+TAG_MNOISE = 11
+TAG_MRANK = 12
+TAG_MISC = 13
+
+F32 = 0
+BF16 = 1
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        path = _build.lib_path()
+        if not os.path.exists(path):
+            _build.build()
+        L = ctypes.CDLL(path)
+        u64, i64, i32 = ctypes.c_uint64, ctypes.c_int64, ctypes.c_int
+        vp, fl, db = ctypes.c_void_p, ctypes.c_float, ctypes.c_double
+        L.gen_u64.argtypes = [u64, u64, u64]
+        L.gen_u64.restype = u64
+        L.gen_uniform.argtypes = [u64, u64, u64]
+        L.gen_uniform.restype = db
+        L.gen_normal.argtypes = [u64, u64, u64, fl]
+        L.gen_normal.restype = fl
+        L.gen_fill_normal.argtypes = [u64, u64, u64, i64, fl, i32, vp]
+        L.gen_fill_normal.restype = None
+        L.gen_fill_normal_segments.argtypes = [u64, u64, i64, vp, i64, fl, i32, vp, vp]
+        L.gen_fill_normal_segments.restype = None
+        L.gen_rank_perm.argtypes = [u64, u64, i32, vp]
+        L.gen_rank_perm.restype = None
+        L.gen_zipf_bias.argtypes = [u64, u64, i32, db, db, vp]
+        L.gen_zipf_bias.restype = None
+        L.gen_routing_logits.argtypes = [u64, u64, i32, i32, i32, vp, db, i32, vp]
+        L.gen_routing_logits.restype = i64
+        L.gen_markov_routing.argtypes = [u64, i32, i32, i32, i32, i32, db, db,
+                                         u64, u64, u64, u64, u64, vp, vp]
+        L.gen_markov_routing.restype = None
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def normal(seed, tag, i0, shape, sd=1.0, dtype=F32):
+    """Elements i0 .. i0+prod(shape)-1 of stream (seed, tag); bf16 is returned as uint16 bits."""
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.float32 if dtype == F32 else np.uint16)
+    lib().gen_fill_normal(seed, tag, i0, n, float(sd), dtype, _ptr(out))
+    return out.reshape(shape)
+
+
+def fill_normal_ptr(seed, tag, i0, n, sd, dtype, dst_ptr):
+    """Fill n elements at raw host address dst_ptr (for pinned buffers)."""
+    lib().gen_fill_normal(seed, tag, i0, int(n), float(sd), dtype, ctypes.c_void_p(dst_ptr))
+
+
+def fill_segments_ptr(seed, tag, src_i0, seg_len, sd, dtype, dst_ptr, dst_off):
+    """Fill len(src_i0) segments of seg_len elements into raw host address dst_ptr."""
+    src = np.ascontiguousarray(src_i0, dtype=np.uint64)
+    off = np.ascontiguousarray(dst_off, dtype=np.int64)
+    lib().gen_fill_normal_segments(seed, tag, len(src), _ptr(src), int(seg_len), float(sd), dtype,
+                                   ctypes.c_void_p(dst_ptr), _ptr(off))
+
+
+def bf16_bits_to_f32(u16):
+    """Exact upcast of bf16 bit patterns (uint16) to float32."""
+    return (np.asarray(u16, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def rank_perm(seed, tag, E):
+    out = np.empty(E, dtype=np.int32)
+    lib().gen_rank_perm(seed, tag, E, _ptr(out))
+    return out
+
+
+def zipf_bias(seed, tag, E, alpha, s=1.1):
+    out = np.empty(E, dtype=np.float32)
+    lib().gen_zipf_bias(seed, tag, E, float(alpha), float(s), _ptr(out))
+    return out
+
+
+def routing_logits(seed, tag, T, E, k, bias=None, min_gap=1e-3, max_attempts=64):
+    """[T, E] fp32 router logits, N(0,1) (+ bias), with the top-k margin guard."""
+    out = np.empty((T, E), dtype=np.float32)
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+    r = lib().gen_routing_logits(seed, tag, T, E, k, None if b is None else _ptr(b),
+                                 float(min_gap), max_attempts, _ptr(out))
+    if r < 0:
+        raise RuntimeError("routing_logits: a row kept a top-k gap below min_gap")
+    return out
+
+
+def markov_routing(seed, steps, L, B, E, k, p_stay=0.7, zipf_s=1.1):
+    """Multi-step decode routing trace: (ids [steps,L,B,k] int32, logits [steps,L,B,E] fp32)."""
+    ids = np.empty((steps, L, B, k), dtype=np.int32)
+    logits = np.empty((steps, L, B, E), dtype=np.float32)
+    lib().gen_markov_routing(seed, steps, L, B, E, k, float(p_stay), float(zipf_s),
+                             TAG_MRANK, TAG_MSTAY, TAG_MZIPF, TAG_MCHOSEN, TAG_MNOISE,
+                             _ptr(ids), _ptr(logits))
+    return ids, logits

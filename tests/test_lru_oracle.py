@@ -1,0 +1,137 @@
+"""Pins of the LRU simulator: a hand-traced sequence, a textbook LRU, invariants."""
+import os
+from collections import OrderedDict
+
+import numpy as np
+import pytest
+
+import gen
+from gen import configs
+import oracle
+from oracle import LruSim, CapacityError, StaticPlacement
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "lru_trace_s3.txt")
+
+
+def _parse_golden():
+    rows = []
+    for line in open(GOLDEN):
+        if line.startswith("#") or not line.strip():
+            continue
+        t, req, hits, fills, ev, keys, stamps = [c.strip() for c in line.split("|")]
+        fl = [] if fills == "-" else [tuple(int(v) for v in f.split("<-")) for f in fills.split()]
+        rows.append(dict(
+            t=int(t), req=[int(v) for v in req.split()],
+            hits=[] if hits == "-" else [int(v) for v in hits.split()],
+            fills=fl, evicted=[] if ev == "-" else [int(v) for v in ev.split()],
+            keys=[-1 if v == "-" else int(v) for v in keys.split()],
+            stamps=[int(v) for v in stamps.split()]))
+    return rows
+
+
+def test_hand_traced_sequence():
+    sim = LruSim(L=1, E=8, S=3)
+    evictions = []
+    for row in _parse_golden():
+        slot, fills = sim.step(0, row["req"])
+        assert sim.clock == row["t"]
+        assert [(s, e) for s, _, e, _ in fills] == row["fills"]
+        ev = [old for _, _, _, old in fills if old >= 0]
+        assert ev == row["evicted"]
+        evictions += ev
+        assert list(sim.key_of) == row["keys"]
+        assert list(sim.stamp) == row["stamps"]
+        assert sorted(e for e in row["req"] if e not in [f[1] for f in row["fills"]]) == row["hits"]
+        for e in row["req"]:
+            assert sim.key_of[slot[e]] == e
+    assert (sim.accesses, sim.misses, evictions) == (11, 7, [1, 2, 0, 3])
+
+
+def test_single_request_calls_equal_textbook_lru():
+    """One expert per call: no ties inside a call, so the hit/miss sequence and the
+    resident set must equal a textbook move-to-end LRU (collections.OrderedDict)."""
+    L, E, S = 3, 20, 7
+    r = np.random.default_rng(0)
+    sim = LruSim(L, E, S)
+    book = OrderedDict()
+    for _ in range(3000):
+        layer = int(r.integers(L))
+        e = int(min(r.zipf(1.3), E) - 1)
+        key = layer * E + e
+        hit_book = key in book
+        if hit_book:
+            book.move_to_end(key)
+        else:
+            if len(book) == S:
+                book.popitem(last=False)
+            book[key] = True
+        _, fills = sim.step(layer, [e])
+        assert (len(fills) == 0) == hit_book
+        assert sim.resident_keys() == set(book.keys())
+
+
+def test_capacity_error_leaves_state_unchanged():
+    sim = LruSim(1, 16, 4)
+    sim.step(0, [1, 2])
+    before = (sim.key_of.copy(), sim.slot_of.copy(), sim.stamp.copy(), sim.clock)
+    with pytest.raises(CapacityError):
+        sim.step(0, [0, 1, 2, 3, 4])
+    after = (sim.key_of, sim.slot_of, sim.stamp, sim.clock)
+    for a, b in zip(before, after):
+        np.testing.assert_array_equal(a, b)
+
+
+def _check_invariants(sim, t, U_keys, fills, before_stamp, before_key):
+    S = sim.S
+    for s in range(S):  # slot_of and key_of are mutual inverses
+        if sim.key_of[s] >= 0:
+            assert sim.slot_of[sim.key_of[s]] == s
+    assert np.count_nonzero(sim.slot_of >= 0) == np.count_nonzero(sim.key_of >= 0)
+    misses = [k for k in U_keys if k not in set(before_key[before_key >= 0])]
+    assert len(fills) == len(misses)
+    evicted_slots = [s for s, _, _, old in fills if old >= 0]
+    for s in evicted_slots:  # nothing stamped t is evicted at t
+        assert before_stamp[s] < t
+    if evicted_slots:  # nothing evicted was used more recently than anything kept
+        newest_evicted = max(before_stamp[s] for s in evicted_slots)
+        kept = [s for s in range(S) if before_key[s] >= 0 and s not in evicted_slots]
+        for s in kept:
+            assert sim.stamp[s] >= newest_evicted
+    for k in U_keys:  # every requested entry is resident after the call
+        assert sim.slot_of[k] >= 0 and sim.stamp[sim.slot_of[k]] == t
+
+
+def test_invariants_on_markov_trace_and_lru_beats_static_placement():
+    """Multi-layer Markov routing (p=0.7 re-pick, else Zipf(1.1)), 16 layers x 256 experts,
+    1024 slots.  Invariants every call; LRU misses less than a routing-agnostic static
+    placement of the same capacity (directional check of the pages' comparison of the
+    global LRU with a static split: RTX-4090 page, "Benchmarks, comparisons, trade-offs")."""
+    w = configs.LRU_DECODE
+    steps = 64
+    ids, logits = gen.markov_routing(w.seed, steps, w.L, w.T, w.E, w.k, w.p_stay, w.zipf_s)
+    sim = LruSim(w.L, w.E, w.S)
+    # static: the S/L most Zipf-popular experts of every layer, fixed
+    per_layer = w.S // w.L
+    static_keys = []
+    for layer in range(w.L):
+        rank = gen.rank_perm(w.seed, gen.TAG_MRANK + layer * 0x10000, w.E)
+        static_keys += [layer * w.E + int(e) for e in np.argsort(rank)[:per_layer]]
+    static = StaticPlacement(static_keys)
+    for s in range(steps):
+        for layer in range(w.L):
+            before_stamp, before_key = sim.stamp.copy(), sim.key_of.copy()
+            U = sorted(set(int(e) for e in ids[s, layer].ravel()))
+            _, fills = sim.step(layer, ids[s, layer])
+            _check_invariants(sim, sim.clock, [layer * w.E + e for e in U], fills, before_stamp,
+                              before_key)
+            static.step(layer, ids[s, layer], w.E)
+    assert sim.accesses == static.accesses
+    assert sim.misses < static.misses
+
+
+def test_markov_logits_route_back_to_generated_ids():
+    """The oracle's top-k of the synthesised logits reproduces the generated expert ids."""
+    w = configs.LRU_DECODE
+    ids, logits = gen.markov_routing(w.seed, 4, 3, w.T, w.E, w.k, w.p_stay, w.zipf_s)
+    got, _ = oracle.route(logits.reshape(-1, w.E), w.k)
+    np.testing.assert_array_equal(got, ids.reshape(-1, w.k))
