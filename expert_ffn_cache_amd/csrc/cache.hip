@@ -1,0 +1,226 @@
+// Global LRU cache of whole (layer, expert) entries, miss fills and
+// double-buffered layer streaming.
+//
+// FreeToken pages: decode keeps a shared LRU expert cache across layers and
+// tokens, so recent routing decides what stays resident (llama page, "Official
+// project overview"; RTX-4090 page, "How the MoE memory hierarchy works");
+// entries are complete (layer, expert) pairs under one logical mapping (same
+// RTX-4090 section); misses are moved over PCIe into the GPU cache (benchmark
+// page, runtime-tier table); prefill moves the next layer's experts while the
+// current layer computes (benchmark page, "How FreeToken serves large MoE
+// models"); control data stays on the device so routing-dependent decisions
+// remain graph-compatible (benchmark page, feature cards).
+//
+// The lookup runs as one 1024-thread workgroup, entirely on device tables:
+//   requested-set flags in LDS -> |U| (barrier count) -> capacity check ->
+//   hit detection through slot_of -> (stamp << 13 | slot) keys of all slots in
+//   LDS with hit slots pushed to the end -> bitonic sort -> the i-th miss
+//   (ascending id, block scan) takes the i-th smallest key -> table updates,
+//   fill records, counters, clock.
+#include <algorithm>
+
+#include "common.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr int kCacheThreads = 1024;
+constexpr int kMaxSlots = 4096;  // keys of all slots live in LDS (32 KB)
+constexpr int kSlotBits = 13;
+
+__global__ __launch_bounds__(256) void cache_init_kernel(moe_cache_t c) {
+  const long long nkeys = (long long)c.L * c.E;
+  const long long stride = (long long)gridDim.x * blockDim.x;
+  for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < nkeys; i += stride)
+    c.slot_of[i] = -1;
+  for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < c.S; i += stride) {
+    c.key_of[i] = -1;
+    c.stamp[i] = 0;
+  }
+  if (blockIdx.x == 0 && threadIdx.x < 4) c.stats[threadIdx.x] = 0;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    *c.clock = 0;
+    *c.status = 0;
+  }
+}
+
+__global__ __launch_bounds__(kCacheThreads) void lru_lookup_update(moe_cache_t c, int layer,
+                                                                   const int32_t* __restrict__ ids,
+                                                                   int A, int32_t* __restrict__ expert_slot,
+                                                                   moe_fill_t* __restrict__ fills,
+                                                                   int32_t* __restrict__ n_fills) {
+  __shared__ unsigned long long keys[kMaxSlots];
+  __shared__ int req[kMaxE];       // 1 = requested
+  __shared__ int miss_list[kMaxE];
+  __shared__ int s_wave[16];
+  __shared__ int s_err;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int E = c.E, S = c.S;
+  const long long t = *c.clock + 1;  // read before any thread can update the clock
+  if (tid < E) req[tid] = 0;
+  if (tid == 0) s_err = 0;
+  __syncthreads();
+  for (int a = tid; a < A; a += kCacheThreads) {
+    const int id = ids[a];
+    if (id >= 0 && id < E) req[id] = 1;
+    else s_err = 1;
+  }
+  __syncthreads();
+  const bool want = tid < E && req[tid];
+  int slot = -1;
+  if (want) {
+    slot = c.slot_of[(size_t)layer * E + tid];
+    if (slot >= S) s_err = 1;  // corrupted table
+  }
+  const int nU = __syncthreads_count(want);
+  if (s_err || nU > S) {
+    if (tid == 0) {
+      set_status(c.status, s_err ? MOE_ERANGE : MOE_ECAPACITY);
+      *n_fills = 0;
+    }
+    return;
+  }
+  const bool hit = want && slot >= 0;
+  const bool miss = want && slot < 0;
+  // keys of every slot; slots hit in this call sort after all candidates
+  int npow = 64;
+  while (npow < S) npow <<= 1;
+  for (int s = tid; s < npow; s += kCacheThreads)
+    keys[s] = s < S ? ((unsigned long long)c.stamp[s] << kSlotBits) | (unsigned)s : ~0ull;
+  __syncthreads();
+  if (hit) keys[slot] = ~0ull;
+  // miss ranks in ascending expert id (one expert per thread)
+  const unsigned long long mb = __ballot(miss);
+  if (lane == 0) s_wave[wave] = __popcll(mb);
+  __syncthreads();
+  int before = 0, nmiss = 0;
+  for (int w = 0; w < kCacheThreads / 64; ++w) {
+    before += w < wave ? s_wave[w] : 0;
+    nmiss += s_wave[w];
+  }
+  if (miss) miss_list[before + __popcll(mb & lanemask_lt(lane))] = tid;
+  // bitonic sort, ascending
+  for (int size = 2; size <= npow; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      __syncthreads();
+      for (int i = tid; i < (npow >> 1); i += kCacheThreads) {
+        const int lo = 2 * stride * (i / stride) + (i % stride);
+        const int hi = lo + stride;
+        const bool asc = (lo & size) == 0;
+        const unsigned long long x = keys[lo], y = keys[hi];
+        if ((x > y) == asc) {
+          keys[lo] = y;
+          keys[hi] = x;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < nmiss) {
+    const int s = (int)(keys[tid] & ((1u << kSlotBits) - 1));
+    const int e = miss_list[tid];
+    const int old = c.key_of[s];
+    const int key = layer * E + e;
+    if (old >= 0) c.slot_of[old] = -1;
+    c.key_of[s] = key;
+    c.slot_of[key] = s;
+    c.stamp[s] = t;
+    fills[tid] = moe_fill_t{s, layer, e, old};
+    expert_slot[e] = s;
+  }
+  if (tid < E) {
+    if (hit) {
+      c.stamp[slot] = t;
+      expert_slot[tid] = slot;
+    } else if (!miss) {
+      expert_slot[tid] = -1;
+    }
+  }
+  if (tid == 0) {
+    *c.clock = t;
+    *n_fills = nmiss;
+    c.stats[0] += nU;
+    c.stats[1] += nU - nmiss;
+    c.stats[2] += nmiss;
+    c.stats[3] += (long long)nmiss * (long long)c.entry_bytes;
+  }
+}
+
+bool cache_ok(const moe_cache_t* c) {
+  return c && c->L > 0 && c->E > 0 && c->E <= kMaxE && c->S > 0 && c->S <= kMaxSlots &&
+         (long long)c->L * c->E < (1ll << 31) && c->entry_bytes > 0 && c->slot_of && c->key_of &&
+         c->stamp && c->clock && c->stats && c->status;
+}
+
+}  // namespace
+
+extern "C" int cache_init(const moe_cache_t* cache, hipStream_t stream) {
+  if (!cache_ok(cache)) return MOE_EINVAL;
+  const long long n = std::max<long long>((long long)cache->L * cache->E, cache->S);
+  const int blocks = (int)std::min<long long>((n + 255) / 256, 4096);
+  hipLaunchKernelGGL(cache_init_kernel, dim3(blocks), dim3(256), 0, stream, *cache);
+  MOE_LAUNCH_CHECK();
+  return MOE_OK;
+}
+
+extern "C" int cache_lookup_update(const moe_cache_t* cache, int layer, const int32_t* topk_ids,
+                                   int T, int k, int32_t* expert_slot, moe_fill_t* fills,
+                                   int32_t* n_fills, hipStream_t stream) {
+  if (!cache_ok(cache)) return MOE_EINVAL;
+  if (layer < 0 || layer >= cache->L) return MOE_ERANGE;
+  if (T < 0 || k <= 0 || k > kMaxK || k > cache->E) return MOE_EINVAL;
+  if ((long long)T * k >= (1ll << 31)) return MOE_EINVAL;
+  if (!expert_slot || !fills || !n_fills || (T > 0 && !topk_ids)) return MOE_EINVAL;
+  hipLaunchKernelGGL(lru_lookup_update, dim3(1), dim3(kCacheThreads), 0, stream, *cache, layer,
+                     topk_ids, T * k, expert_slot, fills, n_fills);
+  MOE_LAUNCH_CHECK();
+  return MOE_OK;
+}
+
+extern "C" int cache_fill(const moe_cache_t* cache, const moe_fill_t* fills_host, int n_fills,
+                          hipStream_t copy_stream) {
+  if (!cache || !cache->arena || !cache->host_pool || cache->S <= 0 || cache->L <= 0 ||
+      cache->E <= 0 || cache->entry_bytes == 0)
+    return MOE_EINVAL;
+  if (n_fills < 0 || (n_fills > 0 && !fills_host)) return MOE_EINVAL;
+  for (int i = 0; i < n_fills; ++i) {
+    const moe_fill_t& f = fills_host[i];
+    if (f.slot < 0 || f.slot >= cache->S || f.layer < 0 || f.layer >= cache->L || f.expert < 0 ||
+        f.expert >= cache->E)
+      return MOE_ERANGE;
+  }
+  const size_t eb = cache->entry_bytes;
+  const char* pool = (const char*)cache->host_pool;
+  char* arena = (char*)cache->arena;
+  int i = 0;
+  while (i < n_fills) {
+    const long long src0 = (long long)fills_host[i].layer * cache->E + fills_host[i].expert;
+    const int dst0 = fills_host[i].slot;
+    int run = 1;
+    while (i + run < n_fills) {
+      const moe_fill_t& g = fills_host[i + run];
+      if ((long long)g.layer * cache->E + g.expert != src0 + run || g.slot != dst0 + run) break;
+      ++run;
+    }
+    MOE_HIP_CHECK(hipMemcpyAsync(arena + (size_t)dst0 * eb, pool + (size_t)src0 * eb,
+                                 (size_t)run * eb, hipMemcpyHostToDevice, copy_stream));
+    i += run;
+  }
+  return MOE_OK;
+}
+
+extern "C" int layer_stream_prefetch(const void* host_src, void* dst, size_t bytes, int n_chunks,
+                                     hipStream_t copy_stream, hipEvent_t wait_before,
+                                     hipEvent_t done) {
+  if (!host_src || !dst || n_chunks <= 0) return MOE_EINVAL;
+  if (wait_before) MOE_HIP_CHECK(hipStreamWaitEvent(copy_stream, wait_before, 0));
+  const size_t chunk = (bytes + (size_t)n_chunks - 1) / (size_t)n_chunks;
+  for (size_t off = 0; off < bytes; off += chunk) {
+    const size_t n = std::min(chunk, bytes - off);
+    MOE_HIP_CHECK(hipMemcpyAsync((char*)dst + off, (const char*)host_src + off, n,
+                                 hipMemcpyHostToDevice, copy_stream));
+  }
+  if (done) MOE_HIP_CHECK(hipEventRecord(done, copy_stream));
+  return MOE_OK;
+}

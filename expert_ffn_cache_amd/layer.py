@@ -1,0 +1,63 @@
+"""One routed-MoE layer forward as a sequence of library calls on caller-owned buffers.
+
+route -> permute -> expert FFN -> combine (each a libmoecache.so entry point).
+Device memory comes from torch; this class only allocates the intermediate
+buffers once and forwards pointers.
+"""
+import torch
+
+from . import (MOE_F32, MOE_BF16, MOE_PATH_AUTO, moe_route, moe_permute,
+               moe_permute_workspace_bytes, moe_expert_ffn, moe_expert_ffn_workspace_bytes,
+               moe_combine)
+
+
+def _tdtype(code):
+    return torch.float32 if code == MOE_F32 else torch.bfloat16
+
+
+class MoeLayer:
+    def __init__(self, T, E, k, d, f, dtype=MOE_BF16, y_dtype=MOE_F32, device="cuda"):
+        self.T, self.E, self.k, self.d, self.f = T, E, k, d, f
+        self.dtype, self.y_dtype = dtype, y_dtype
+        A = T * k
+        dev = torch.device(device)
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.ids = torch.empty((T, k), **i32)
+        self.w = torch.empty((T, k), dtype=torch.float32, device=dev)
+        self.counts = torch.empty(E, **i32)
+        self.offsets = torch.empty(E + 1, **i32)
+        self.perm = torch.empty(max(A, 1), **i32)
+        self.inv = torch.empty(max(A, 1), **i32)
+        self.status = torch.zeros(1, **i32)
+        self.perm_ws_bytes = moe_permute_workspace_bytes(T, k, E)
+        self.perm_ws = torch.empty(self.perm_ws_bytes, dtype=torch.uint8, device=dev)
+        self.ffn_ws_bytes = moe_expert_ffn_workspace_bytes(T, k, f, dtype)
+        self.ffn_ws = torch.empty(self.ffn_ws_bytes, dtype=torch.uint8, device=dev)
+        self.y_perm = torch.empty((max(A, 1), d), dtype=_tdtype(y_dtype), device=dev)
+        self.out = torch.empty((T, d), dtype=torch.float32, device=dev)
+
+    def route(self, logits, stream=None):
+        moe_route(logits, self.T, self.E, self.k, self.ids, self.w, stream)
+
+    def permute(self, stream=None):
+        moe_permute(self.ids, self.T, self.k, self.E, self.counts, self.offsets, self.perm,
+                    self.inv, self.perm_ws, self.perm_ws_bytes, self.status, stream)
+
+    def ffn(self, x, arena, entry_stride, expert_slot=None, mask=None, slot_key=None, key_base=0,
+            path=MOE_PATH_AUTO, stream=None):
+        moe_expert_ffn(x, self.dtype, self.perm, self.offsets, self.T, self.k, self.E, self.d,
+                       self.f, expert_slot, arena, entry_stride, self.dtype, mask, slot_key,
+                       key_base, self.ffn_ws, self.ffn_ws_bytes, self.y_perm, self.y_dtype, path,
+                       self.status, stream)
+
+    def combine(self, stream=None):
+        moe_combine(self.y_perm, self.y_dtype, self.inv, self.w, self.T, self.k, self.d,
+                    self.out, stream)
+
+    def forward(self, x, logits, arena, entry_stride, expert_slot=None, path=MOE_PATH_AUTO,
+                stream=None):
+        self.route(logits, stream)
+        self.permute(stream)
+        self.ffn(x, arena, entry_stride, expert_slot, path=path, stream=stream)
+        self.combine(stream)
+        return self.out

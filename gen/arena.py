@@ -1,0 +1,68 @@
+"""Writes generated expert weights into host or device buffers in the cache-entry layout.
+
+The entry layout is the library's documented one (include/moe_cache.h):
+[W_gate f x d][W_up f x d][W_down d x f], each row-major, one entry per
+(layer, expert).  This module only places generated values; it computes
+nothing of the layer.
+"""
+import numpy as np
+
+from . import TAG_WG, TAG_WU, TAG_WD, fill_segments_ptr
+from .configs import wg_index, wd_index
+
+
+def fill_entries_ptr(w, pairs, dst_ptr, entry_stride_elems):
+    """Entry q of dst (host address) <- weights of pairs[q] = (layer, expert)."""
+    pairs = list(pairs)
+    if not pairs:
+        return
+    fd = w.f * w.d
+    base = np.arange(len(pairs), dtype=np.int64) * entry_stride_elems
+    gidx = np.array([wg_index(w, l, e) for l, e in pairs], dtype=np.uint64)
+    didx = np.array([wd_index(w, l, e) for l, e in pairs], dtype=np.uint64)
+    fill_segments_ptr(w.seed, TAG_WG, gidx, fd, w.w_sd, w.dtype, dst_ptr, base)
+    fill_segments_ptr(w.seed, TAG_WU, gidx, fd, w.w_sd, w.dtype, dst_ptr, base + fd)
+    fill_segments_ptr(w.seed, TAG_WD, didx, fd, w.w_sd, w.dtype, dst_ptr, base + 2 * fd)
+
+
+def torch_dtype(w):
+    import torch
+    return torch.float32 if w.elem == 4 else torch.bfloat16
+
+
+def fill_device_entries(w, pairs, arena, slots, chunk=16, staging=None):
+    """arena[slots[q]] <- entry of pairs[q]; arena is a device tensor [S, entry_elems].
+
+    Generation happens on the host into a pinned staging buffer, chunk entries at a time."""
+    import torch
+    pairs, slots = list(pairs), list(slots)
+    n_el = w.entry_elems
+    if staging is None:
+        staging = torch.empty((chunk, n_el), dtype=arena.dtype, pin_memory=True)
+    for c0 in range(0, len(pairs), chunk):
+        sub = pairs[c0:c0 + chunk]
+        fill_entries_ptr(w, sub, staging.data_ptr(), n_el)
+        torch.cuda.synchronize()
+        for q, s in enumerate(slots[c0:c0 + chunk]):
+            arena[s].copy_(staging[q], non_blocking=True)
+        torch.cuda.synchronize()
+
+
+def device_arena_all_experts(w, layer=0):
+    """Device arena with all E experts of `layer` resident at slot e (identity slots)."""
+    import torch
+    arena = torch.empty((w.E, w.entry_elems), dtype=torch_dtype(w), device="cuda")
+    fill_device_entries(w, [(layer, e) for e in range(w.E)], arena, range(w.E))
+    return arena
+
+
+def host_pool(w, pin=True):
+    """Pinned host pool [L*E, entry_elems], layer-major, every (layer, expert) entry."""
+    import torch
+    pool = torch.empty((w.L * w.E, w.entry_elems), dtype=torch_dtype(w), pin_memory=pin)
+    step = 64
+    pairs = [(l, e) for l in range(w.L) for e in range(w.E)]
+    for c0 in range(0, len(pairs), step):
+        sub = pairs[c0:c0 + step]
+        fill_entries_ptr(w, sub, pool[c0].data_ptr(), w.entry_elems)
+    return pool

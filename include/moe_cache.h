@@ -1,0 +1,241 @@
+/*
+ * moe_cache.h -- C ABI of libmoecache.so: one routed-expert MoE layer forward
+ * on an AMD Instinct MI355X (gfx950), with expert weights reached through a
+ * GPU-resident LRU cache of whole (layer, expert) entries.
+ *
+ * What the FreeToken pages state, and this library implements:
+ *  - each token activates a subset of the experts; DeepSeek-V4-Flash picks 6
+ *    of 256 routed experts per layer (RTX-4090 page, "How the MoE memory
+ *    hierarchy works"); the runtime decides which weights stay on the GPU and
+ *    which stay in host memory (llama page, "Official project overview").
+ *  - the host holds the full routed-expert pool as ground truth; the GPU holds
+ *    a shared cache of complete (layer, expert) entries under the same logical
+ *    mapping (RTX-4090 page, "How the MoE memory hierarchy works"; benchmark
+ *    page, runtime-tier table).
+ *  - decode keeps one global LRU expert cache across layers and tokens; misses
+ *    move over PCIe into the GPU cache (llama page, "Official project
+ *    overview"; benchmark page, "How FreeToken serves large MoE models").
+ *  - prefill streams whole layers double-buffered: the next layer's experts
+ *    cross PCIe while the current layer computes (same sections).
+ *  - device-resident control data keeps routing-dependent decisions
+ *    compatible with captured graph execution (benchmark page, feature card
+ *    "graph compatibility").
+ * The layer math (softmax top-k gate, SwiGLU experts, weighted combine) is
+ * not on the pages; see the readings listed in the design notes.
+ *
+ * Conventions for every entry point:
+ *  - Returns an int status: MOE_OK or a negative MOE_E* code.  Nothing throws.
+ *  - Host-detected errors return before anything is enqueued.
+ *  - All work is asynchronous on the caller's stream; the library allocates
+ *    nothing and keeps no global mutable state.  The caller owns all memory.
+ *  - Device pointers must be 16-byte aligned.  Errors found on the device are
+ *    written to a caller-provided int32 device status word, sticky: the first
+ *    error code is kept (compare-and-swap from 0); the caller reads it after a
+ *    synchronisation.  This keeps the calls graph-capturable.
+ *  - Calls sharing a cache descriptor or workspace must be ordered on one
+ *    stream (not thread-safe on one descriptor).
+ *  - Capture-safe (no host sync, no allocation, launch shape depends only on
+ *    scalar arguments): every call except cache_fill, whose copy count is
+ *    data-dependent and read on the host.
+ *
+ * Limits: 1 <= E <= 1024, 1 <= k <= min(E, 16), T >= 0 (T = 0 is a no-op),
+ * T*k < 2^31, d and f positive multiples of 64.
+ */
+#ifndef MOE_CACHE_H
+#define MOE_CACHE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_OK 0
+#define MOE_EINVAL (-1)       /* null pointer, bad size, limit exceeded */
+#define MOE_EUNSUPPORTED (-2) /* dtype combination not implemented */
+#define MOE_EHIP (-3)         /* a HIP launch or copy failed */
+#define MOE_ECAPACITY (-4)    /* more unique experts requested than cache slots */
+#define MOE_ERANGE (-5)       /* id, layer or slot out of range; stale cache slot */
+
+#define MOE_F32 0  /* IEEE binary32 */
+#define MOE_BF16 1 /* bfloat16 (upper half of binary32) */
+
+/* Static text for a status code. */
+const char* moe_strerror(int status);
+
+/* ABI version of this header (increments on incompatible change). */
+int moe_abi_version(void);
+
+/* Router logits (helper for workloads that start from activations):
+ * logits[t][e] = sum_c x[t][c] * w_router[e][c], fp32 accumulate.
+ * x [T][d] and w_router [E][d] row-major in `dtype` (MOE_F32 only);
+ * logits [T][E] fp32.  The router itself is standard MoE practice: every
+ * token scores every routed expert before the top-k choice (RTX-4090 page,
+ * "How the MoE memory hierarchy works"). */
+int moe_router_logits(const void* x, const void* w_router, int dtype, int T, int d, int E,
+                      float* logits, hipStream_t stream);
+
+/* Top-k routing with a softmax gate over the selected logits (RTX-4090 page,
+ * "How the MoE memory hierarchy works": a token selects 6 of 256 experts).
+ * logits [T][E] fp32 row-major (device).  Writes topk_ids [T][k] int32: the k
+ * experts with the largest logits, in descending logit order, equal logits
+ * (compared by value, -0 == +0) ordered by ascending expert id; and
+ * topk_w [T][k] fp32 = exp(l_j - l_0) / sum_i exp(l_i - l_0) over the k
+ * selected logits.  NaN logits are not supported (unchecked). */
+int moe_route(const float* logits, int T, int E, int k, int32_t* topk_ids, float* topk_w,
+              hipStream_t stream);
+
+/* Workspace bytes moe_permute needs for (T, k, E). */
+size_t moe_permute_workspace_bytes(int T, int k, int E);
+
+/* Grouping tokens by expert: a stable counting sort of the T*k flat
+ * assignments a = t*k + j by expert id (the grouping step before the expert
+ * contraction; the pages describe experts running on the GPU for the tokens
+ * routed to them: RTX-4090 page, component table).
+ * topk_ids [T*k] int32 (device).  Writes counts [E], offsets [E+1] (exclusive
+ * prefix of counts, offsets[E] = T*k), perm [T*k] (sorted position p -> a,
+ * experts ascending, (t, j) order inside an expert) and inv [T*k] (a -> p).
+ * ws: device workspace of at least moe_permute_workspace_bytes(T, k, E).
+ * An id outside [0, E) sets *status = MOE_ERANGE (if status is not NULL) and
+ * leaves the outputs undefined.  Results are deterministic (no atomics decide
+ * an order). */
+int moe_permute(const int32_t* topk_ids, int T, int k, int E, int32_t* counts, int32_t* offsets,
+                int32_t* perm, int32_t* inv, void* ws, size_t ws_bytes, int32_t* status,
+                hipStream_t stream);
+
+/* Entry layout of one (layer, expert) cache entry, in w_dtype elements:
+ *   [ W_gate: f rows x d ][ W_up: f rows x d ][ W_down: d rows x f ]
+ * every matrix row-major with the contraction index contiguous (W_gate row i
+ * holds the d input weights of gate unit i; W_down row o holds the f weights
+ * of output channel o).  One entry is 3*d*f elements; entries sit at
+ * arena + slot * entry_stride bytes (entry_stride >= 3*d*f*elem, multiple of
+ * 16).  The same layout is used by the host pool, the device cache arena and
+ * the streaming buffers, so a fill is one contiguous copy. */
+
+/* Workspace bytes moe_expert_ffn needs (the SwiGLU intermediate, [T*k][f]). */
+size_t moe_expert_ffn_workspace_bytes(int T, int k, int f, int act_dtype);
+
+#define MOE_PATH_AUTO 0 /* chosen from T*k/E on the host */
+#define MOE_PATH_GEMV 1 /* weight-streaming skinny path (decode-shaped counts) */
+#define MOE_PATH_GEMM 2 /* LDS-tiled grouped GEMM (prefill-shaped counts) */
+
+/* Expert SwiGLU FFNs over the grouped rows (RTX-4090 page, component table:
+ * the GPU executes the experts it holds; the FFN form is a reading).
+ * For every expert e with n_e = offsets[e+1] - offsets[e] > 0 (and
+ * expert_mask[e] != 0 when expert_mask is not NULL), for p in
+ * [offsets[e], offsets[e+1]): with X = x[perm[p] / k],
+ *   h = SiLU(X W_gate^T) * (X W_up^T),  y_perm[p] = h W_down^T,
+ * SiLU(z) = z / (1 + exp(-z)), fp32 accumulation.
+ *  x: [T][d] in act_dtype; weights of e at arena + expert_slot[e]*entry_stride
+ *  (expert_slot NULL = identity slots); y_perm [T*k][d] in y_dtype.
+ *  MOE_F32 weights need MOE_F32 activations and y (fp32 arithmetic end to
+ *  end); MOE_BF16 weights need MOE_BF16 activations, y fp32 or bf16, and
+ *  round h to bf16 before the down projection.
+ *  slot_key (nullable, device, [S]): when given, a slot whose key is not
+ *  key_base + e, or a negative slot, sets *status = MOE_ERANGE and that
+ *  expert's rows are not written (stale-cache detection).
+ *  ws: at least moe_expert_ffn_workspace_bytes(T, k, f, act_dtype). */
+int moe_expert_ffn(const void* x, int act_dtype, const int32_t* perm, const int32_t* offsets,
+                   int T, int k, int E, int d, int f, const int32_t* expert_slot,
+                   const void* arena, size_t entry_stride, int w_dtype,
+                   const uint8_t* expert_mask, const int32_t* slot_key, int key_base, void* ws,
+                   size_t ws_bytes, void* y_perm, int y_dtype, int path, int32_t* status,
+                   hipStream_t stream);
+
+/* Weighted combine: out[t][:] = sum_{j=0..k-1} topk_w[t][j] * y_perm[inv[t*k+j]][:],
+ * j ascending, fp32, a gather (no atomics, deterministic).  y_perm [T*k][d]
+ * in y_dtype (MOE_F32 or MOE_BF16), out [T][d] fp32. */
+int moe_combine(const void* y_perm, int y_dtype, const int32_t* inv, const float* topk_w, int T,
+                int k, int d, float* out, hipStream_t stream);
+
+/* ---- global LRU expert cache over (layer, expert) entries ------------------ */
+
+/* Cache descriptor.  All pointers except host_pool are device memory owned by
+ * the caller.  Key of (layer, e) is layer*E + e.
+ *   slot_of [L*E] int32: slot holding a key, -1 = absent
+ *   key_of  [S]   int32: key in a slot, -1 = empty
+ *   stamp   [S]   int64: last use (clock value), 0 = never
+ *   clock   [1]   int64: number of completed lookups
+ *   stats   [4]   int64: accesses, hits, misses, fill bytes (accumulated)
+ *   status  [1]   int32: sticky device error word
+ *   arena: S entries of entry_bytes each (device)
+ *   host_pool: L*E entries, layer-major, pinned host memory (the ground-truth
+ *   copy of every routed expert: vram page, opening section) */
+typedef struct {
+  int32_t L, E, S;
+  int32_t reserved;
+  size_t entry_bytes;
+  int32_t* slot_of;
+  int32_t* key_of;
+  int64_t* stamp;
+  int64_t* clock;
+  int64_t* stats;
+  int32_t* status;
+  void* arena;
+  const void* host_pool;
+} moe_cache_t;
+
+/* One miss fill: copy pool entry (layer, expert) into slot; evicted_key = the
+ * key the slot held before (-1 if it was empty). */
+typedef struct {
+  int32_t slot, layer, expert, evicted_key;
+} moe_fill_t;
+
+/* Empty cache: slot_of = key_of = -1, stamp = clock = stats = 0, status = 0.
+ * Runs a fill kernel (no memset nodes), so it may be captured.  S <= 8192. */
+int cache_init(const moe_cache_t* cache, hipStream_t stream);
+
+/* One lookup/update of the global LRU for `layer` with the T*k requested ids
+ * (pages: shared LRU of whole (layer, expert) entries, recent routing decides
+ * residency; RTX-4090 page, "How the MoE memory hierarchy works").  One
+ * workgroup on the device:
+ *   t = clock + 1; U = sorted unique requested ids (a repeat is one access);
+ *   if |U| > S: *status = MOE_ECAPACITY, *n_fills = 0, nothing else changes;
+ *   every resident e in U gets stamp t (hit);
+ *   misses (U minus hits, ascending id) take the slots with stamp < t in
+ *   ascending (stamp, slot) order (empty slots first; entries used in this
+ *   call are never evicted by it); each evicts the slot's old key;
+ *   fills[i] = (slot, layer, expert, evicted key) in miss order; clock = t.
+ * expert_slot [E] (device): slot of each requested expert, -1 for the rest.
+ * fills: device array of at least min(E, T*k) records; n_fills: device int32.
+ * An id outside [0, E) sets MOE_ERANGE and changes nothing. */
+int cache_lookup_update(const moe_cache_t* cache, int layer, const int32_t* topk_ids, int T, int k,
+                        int32_t* expert_slot, moe_fill_t* fills, int32_t* n_fills,
+                        hipStream_t stream);
+
+/* Copy the n_fills missed entries from the pinned host pool into their slots
+ * over PCIe (benchmark page, runtime-tier table: the PCIe link moves selected
+ * experts into the GPU cache).  fills_host: host copy of the records written
+ * by cache_lookup_update.  Issues hipMemcpyAsync host-to-device on
+ * copy_stream, merging records whose slots and pool entries are both
+ * consecutive.  Returns MOE_ERANGE (nothing enqueued) for a record outside
+ * [0, S) x [0, L) x [0, E).  Not capture-safe (the count is host data). */
+int cache_fill(const moe_cache_t* cache, const moe_fill_t* fills_host, int n_fills,
+               hipStream_t copy_stream);
+
+/* Full-layer streaming for prefill (llama page, "Official project overview";
+ * benchmark page, "How FreeToken serves large MoE models"): waits on
+ * wait_before (nullable; the event that marks the end of the last compute
+ * reading dst), then copies `bytes` from host_src (pinned) to dst (device) in
+ * n_chunks hipMemcpyAsync calls on copy_stream, then records `done`
+ * (nullable).  Capture-safe. */
+int layer_stream_prefetch(const void* host_src, void* dst, size_t bytes, int n_chunks,
+                          hipStream_t copy_stream, hipEvent_t wait_before, hipEvent_t done);
+
+/* ---- measurement helpers ---------------------------------------------------- */
+
+/* Streams `bytes` (multiple of 16) from src and writes one word per
+ * workgroup to sink[0 .. 4096) (achievable HBM read bandwidth probe). */
+int moe_hbm_read_probe(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);
+
+/* Plain device copy of `bytes` (multiple of 16): reference kernel of known
+ * traffic for scaling hardware byte counters. */
+int moe_copy_probe(const void* src, void* dst, size_t bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_CACHE_H */

@@ -1,0 +1,87 @@
+"""CPU-side checks of the C ABI: the library loads, exports every declared entry point, and
+host-side argument validation returns the documented codes before touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import expert_ffn_cache_amd as moe
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "moe_cache.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("defined",)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared()
+    assert len(names) >= 15, names
+    lib = moe.lib()
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in moe_cache.h but not exported"
+    assert sorted(moe.EXPORTS) == names
+
+
+def test_strerror_and_version():
+    assert moe.strerror(moe.MOE_OK) == "ok"
+    for code in (moe.MOE_EINVAL, moe.MOE_EUNSUPPORTED, moe.MOE_EHIP, moe.MOE_ECAPACITY,
+                 moe.MOE_ERANGE):
+        assert moe.strerror(code) not in ("ok", "unknown status")
+    assert moe.abi_version() == 1
+
+
+def test_workspace_sizes():
+    assert moe.moe_permute_workspace_bytes(8192, 6, 256) >= 48 * 256 * 4
+    assert moe.moe_permute_workspace_bytes(8192, 6, 256) % 256 == 0
+    assert moe.moe_expert_ffn_workspace_bytes(8192, 6, 2048, moe.MOE_BF16) == 8192 * 6 * 2048 * 2
+    assert moe.moe_expert_ffn_workspace_bytes(16, 2, 512, moe.MOE_F32) == 16 * 2 * 512 * 4
+
+
+def _rc(fn, *args):
+    return getattr(moe.lib(), fn)(*args)
+
+
+def test_host_validation_codes():
+    L = moe.lib()
+    # k > E, E > 1024, k > 16, null pointers: rejected before any launch
+    assert L.moe_route(None, 4, 8, 9, None, None, None) == moe.MOE_EINVAL
+    assert L.moe_route(None, 4, 2000, 2, None, None, None) == moe.MOE_EINVAL
+    assert L.moe_route(None, 4, 64, 17, None, None, None) == moe.MOE_EINVAL
+    assert L.moe_route(None, 4, 64, 2, None, None, None) == moe.MOE_EINVAL
+    assert L.moe_router_logits(None, None, moe.MOE_BF16, 4, 64, 8, None, None) == moe.MOE_EUNSUPPORTED
+    assert L.moe_combine(None, 7, None, None, 4, 2, 64, None, None) == moe.MOE_EUNSUPPORTED
+    assert L.moe_combine(None, moe.MOE_F32, None, None, 4, 2, 100, None, None) == moe.MOE_EINVAL
+    # d, f must be multiples of 64; dtype pairs
+    args = [None, moe.MOE_BF16, None, None, 8, 6, 256, 4096, 2048, None, None, 3 * 4096 * 2048 * 2,
+            moe.MOE_BF16, None, None, 0, None, 0, None, moe.MOE_F32, 0, None, None]
+    bad_d = list(args); bad_d[6] = 4000
+    assert L.moe_expert_ffn(*bad_d) == moe.MOE_EINVAL
+    mixed = list(args); mixed[1] = moe.MOE_F32
+    assert L.moe_expert_ffn(*mixed) == moe.MOE_EUNSUPPORTED
+    short = list(args); short[11] = 100
+    assert L.moe_expert_ffn(*short) == moe.MOE_EINVAL
+    assert L.moe_expert_ffn(*args) == moe.MOE_EINVAL  # null buffers
+
+
+def test_cache_host_validation():
+    c = moe.moe_cache_t(2, 4, 8, 0, 64, 1, 1, 1, 1, 1, 1, 1, 1)  # dummy non-null addresses
+    assert moe.lib().cache_lookup_update(ctypes.byref(c), 2, 1, 1, 1, 1, 1, 1, None) == moe.MOE_ERANGE
+    assert moe.lib().cache_lookup_update(ctypes.byref(c), -1, 1, 1, 1, 1, 1, 1, None) == moe.MOE_ERANGE
+    big = moe.moe_cache_t(2, 4, 5000, 0, 64, 1, 1, 1, 1, 1, 1, 1, 1)
+    assert moe.lib().cache_init(ctypes.byref(big), None) == moe.MOE_EINVAL
+    bad = (moe.moe_fill_t * 2)(moe.moe_fill_t(0, 0, 1, -1), moe.moe_fill_t(8, 0, 1, -1))
+    assert moe.lib().cache_fill(ctypes.byref(c), ctypes.addressof(bad), 2, None) == moe.MOE_ERANGE
+    bad[1] = moe.moe_fill_t(1, 2, 1, -1)
+    assert moe.lib().cache_fill(ctypes.byref(c), ctypes.addressof(bad), 2, None) == moe.MOE_ERANGE
+    assert moe.lib().layer_stream_prefetch(None, None, 16, 1, None, None, None) == moe.MOE_EINVAL
+
+
+def test_python_binding_raises():
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_route(0, 4, 8, 9, 0, 0, stream=0)
+    assert ei.value.status == moe.MOE_EINVAL

@@ -1,0 +1,173 @@
+"""GPU parity of the device LRU (tables, fills, counters) against the sequential simulator,
+miss fills from a pinned host pool, stale-slot detection, and error paths."""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import gen
+from gen import configs
+from gen.arena import host_pool
+import oracle
+from oracle import LruSim
+import expert_ffn_cache_amd as moe
+from expert_ffn_cache_amd.layer import MoeLayer
+from tests._helpers import assert_close, bf16_tol, dev, x_device, oracle_table
+
+pytestmark = pytest.mark.gpu
+
+
+class DevCache:
+    """Device tables + descriptor for a cache of S slots over L x E entries."""
+
+    def __init__(self, L, E, S, entry_bytes, arena=None, pool=None):
+        i32 = dict(dtype=torch.int32, device="cuda")
+        i64 = dict(dtype=torch.int64, device="cuda")
+        self.slot_of = torch.empty(L * E, **i32)
+        self.key_of = torch.empty(S, **i32)
+        self.stamp = torch.empty(S, **i64)
+        self.clock = torch.empty(1, **i64)
+        self.stats = torch.empty(4, **i64)
+        self.status = torch.empty(1, **i32)
+        self.expert_slot = torch.empty(E, **i32)
+        self.fills = torch.empty((max(E, 1), 4), **i32)
+        self.n_fills = torch.empty(1, **i32)
+        self.arena, self.pool = arena, pool
+        self.desc = moe.moe_cache_t(
+            L, E, S, 0, entry_bytes, self.slot_of.data_ptr(), self.key_of.data_ptr(),
+            self.stamp.data_ptr(), self.clock.data_ptr(), self.stats.data_ptr(),
+            self.status.data_ptr(), 0 if arena is None else arena.data_ptr(),
+            0 if pool is None else pool.data_ptr())
+        moe.cache_init(self.desc)
+
+    def lookup(self, layer, ids_dev, T, k, stream=None):
+        moe.cache_lookup_update(self.desc, layer, ids_dev, T, k, self.expert_slot, self.fills,
+                                self.n_fills, stream)
+
+    def fills_host(self):
+        n = int(self.n_fills.item())
+        return [tuple(int(v) for v in r) for r in self.fills[:n].cpu().numpy()]
+
+
+def _compare_tables(dc, sim):
+    np.testing.assert_array_equal(dc.key_of.cpu().numpy(), sim.key_of)
+    np.testing.assert_array_equal(dc.slot_of.cpu().numpy(), sim.slot_of)
+    np.testing.assert_array_equal(dc.stamp.cpu().numpy(), sim.stamp)
+    assert int(dc.clock.item()) == sim.clock
+    st = dc.stats.cpu().numpy()
+    assert (st[0], st[1], st[2]) == (sim.accesses, sim.hits, sim.misses)
+
+
+def test_lru_hand_traced_sequence_on_device():
+    dc = DevCache(1, 8, 3, 64)
+    sim = LruSim(1, 8, 3)
+    for req in ([0, 1], [2], [0, 3], [1], [2, 3], [0, 1, 2]):
+        ids = np.array([req], dtype=np.int32)
+        dc.lookup(0, dev(ids), 1, len(req))
+        _, fills = sim.step(0, req)
+        assert dc.fills_host() == [tuple(f) for f in fills]
+        _compare_tables(dc, sim)
+    assert int(dc.status.item()) == 0
+
+
+@pytest.mark.parametrize("L,E,S,steps", [(4, 64, 32, 150), (16, 256, 1024, 512)])
+def test_lru_markov_trace_bit_exact(L, E, S, steps):
+    """Every call: expert_slot, fill records and (every 16 calls and at the end) all tables
+    equal the simulator's.  The second case is the full multi-layer decode workload
+    (16 layers x 256 experts, 1024 slots, 512 steps of batch 8, top-6)."""
+    w = configs.with_(configs.LRU_DECODE, L=L, E=E, S=S, steps=steps)
+    ids, _ = gen.markov_routing(w.seed, steps, L, w.T, E, w.k, w.p_stay, w.zipf_s)
+    ids_dev = dev(ids)
+    dc = DevCache(L, E, S, w.entry_bytes)
+    sim = LruSim(L, E, S)
+    calls = 0
+    for s in range(steps):
+        for layer in range(L):
+            dc.lookup(layer, ids_dev[s, layer], w.T, w.k)
+            slot_ref, fills = sim.step(layer, ids[s, layer])
+            assert dc.fills_host() == [tuple(f) for f in fills], (s, layer)
+            np.testing.assert_array_equal(dc.expert_slot.cpu().numpy(), slot_ref)
+            calls += 1
+            if calls % 16 == 0:
+                _compare_tables(dc, sim)
+    _compare_tables(dc, sim)
+    assert int(dc.stats[3].item()) == sim.misses * w.entry_bytes
+    assert int(dc.status.item()) == 0
+
+
+def test_lru_capacity_error_leaves_tables():
+    dc = DevCache(1, 16, 4, 64)
+    dc.lookup(0, dev(np.array([[1, 2]], dtype=np.int32)), 1, 2)
+    before = [t.clone() for t in (dc.key_of, dc.slot_of, dc.stamp, dc.clock, dc.stats)]
+    dc.lookup(0, dev(np.array([[0, 1, 2, 3, 4]], dtype=np.int32)), 1, 5)
+    torch.cuda.synchronize()
+    assert int(dc.status.item()) == moe.MOE_ECAPACITY
+    assert int(dc.n_fills.item()) == 0
+    for a, b in zip(before, (dc.key_of, dc.slot_of, dc.stamp, dc.clock, dc.stats)):
+        assert torch.equal(a, b)
+
+
+def test_lru_bad_id_and_layer():
+    dc = DevCache(2, 16, 4, 64)
+    with pytest.raises(moe.MoeError) as ei:
+        dc.lookup(2, dev(np.array([[1]], dtype=np.int32)), 1, 1)
+    assert ei.value.status == moe.MOE_ERANGE
+    dc.lookup(0, dev(np.array([[1, 16]], dtype=np.int32)), 1, 2)
+    torch.cuda.synchronize()
+    assert int(dc.status.item()) == moe.MOE_ERANGE
+    assert int(dc.clock.item()) == 0
+
+
+def test_fill_then_ffn_through_slots_and_stale_slot_detection():
+    """A small multi-layer cache: lookup -> D2H fill list -> cache_fill from the pinned pool ->
+    FFN reading weights through expert_slot with the key check -> combine; every step's
+    output equals the oracle.  Then a corrupted key makes the FFN report MOE_ERANGE."""
+    w = configs.Workload("lru_small", seed=31, T=4, d=256, E=16, k=3, f=192, dtype=gen.BF16,
+                         L=3, S=10, alpha=0.5)
+    pool = host_pool(w)
+    arena = torch.empty((w.S, w.entry_elems), dtype=torch.bfloat16, device="cuda")
+    dc = DevCache(w.L, w.E, w.S, w.entry_bytes, arena, pool)
+    lay = MoeLayer(w.T, w.E, w.k, w.d, w.f)
+    copy = torch.cuda.Stream()
+    fills_host = (moe.moe_fill_t * w.E)()
+    for step in range(6):
+        for layer in range(w.L):
+            x = configs.gen_x(w, layer, attempt=step)
+            lg = gen.routing_logits(w.seed, gen.TAG_LOGIT + layer * 0x10000 + step * 0x100, w.T,
+                                    w.E, w.k)
+            lay.route(dev(lg))
+            dc.lookup(layer, lay.ids, w.T, w.k)
+            f = dc.fills_host()  # synchronises: the one host read per layer
+            for i, (s, l, e, old) in enumerate(f):
+                fills_host[i] = moe.moe_fill_t(s, l, e, old)
+            copy.wait_stream(torch.cuda.current_stream())
+            moe.cache_fill(dc.desc, ctypes.addressof(fills_host), len(f), copy)
+            torch.cuda.current_stream().wait_stream(copy)
+            lay.permute()
+            lay.ffn(x_device(w, x), arena, w.entry_bytes, dc.expert_slot, slot_key=dc.key_of,
+                    key_base=layer * w.E)
+            lay.combine()
+            torch.cuda.synchronize()
+            ids, _, ref = oracle.moe_layer(x, lg, w.k, oracle_table(w, range(w.E), layer))
+            np.testing.assert_array_equal(lay.ids.cpu().numpy(), ids)
+            assert_close(lay.out.cpu().numpy(), ref, bf16_tol(ref), f"step {step} layer {layer}")
+    assert int(dc.status.item()) == 0 and int(lay.status.item()) == 0
+    # stale slot: overwrite the key of one slot used by the last layer's experts
+    used = int(lay.ids[0, 0].item())
+    s = int(dc.expert_slot[used].item())
+    dc.key_of[s] = -7
+    lay.ffn(x_device(w, x), arena, w.entry_bytes, dc.expert_slot, slot_key=dc.key_of,
+            key_base=(w.L - 1) * w.E)
+    torch.cuda.synchronize()
+    assert int(lay.status.item()) == moe.MOE_ERANGE
+
+
+def test_cache_fill_rejects_out_of_range_records():
+    pool = torch.zeros((4, 64), dtype=torch.uint8, pin_memory=True)
+    arena = torch.zeros((2, 64), dtype=torch.uint8, device="cuda")
+    dc = DevCache(2, 2, 2, 64, arena, pool)
+    bad = (moe.moe_fill_t * 1)(moe.moe_fill_t(2, 0, 0, -1))
+    with pytest.raises(moe.MoeError) as ei:
+        moe.cache_fill(dc.desc, ctypes.addressof(bad), 1)
+    assert ei.value.status == moe.MOE_ERANGE

@@ -1,0 +1,173 @@
+"""GPU parity of each entry point against the oracle on seeded inputs (small-to-medium sizes)."""
+import numpy as np
+import pytest
+import torch
+
+import gen
+from gen import configs
+from gen.arena import device_arena_all_experts
+import oracle
+import expert_ffn_cache_amd as moe
+from tests._helpers import (assert_close, f32_tol, bf16_tol, np_of, dev, x_device, oracle_table)
+
+pytestmark = pytest.mark.gpu
+
+
+def _i32(n):
+    return torch.empty(n, dtype=torch.int32, device="cuda")
+
+
+# ---------------------------------------------------------------- routing
+ROUTE_CASES = [  # (T, E, k, kind)
+    (16, 8, 2, "normal"), (1, 256, 6, "zipf"), (8, 256, 6, "zipf"), (8192, 256, 6, "zipf"),
+    (2047, 128, 8, "zipf"), (333, 1024, 16, "normal"), (61, 16, 16, "normal"),
+    (100, 300, 5, "ties"), (37, 65, 3, "zeros"), (5, 1, 1, "normal"),
+]
+
+
+def _route_logits(T, E, k, kind, seed):
+    if kind == "zipf":
+        w = configs.with_(configs.DECODE, T=T, E=E, k=k, seed=seed)
+        return configs.gen_logits(w)
+    if kind == "normal":
+        return gen.routing_logits(seed, gen.TAG_LOGIT, T, E, k)
+    r = np.random.default_rng(seed)
+    if kind == "ties":
+        return (r.integers(-2, 3, size=(T, E)) * 0.5).astype(np.float32)
+    lg = r.choice(np.array([0.0, -0.0, 1.0, -1.0], dtype=np.float32), size=(T, E))
+    return lg
+
+
+@pytest.mark.parametrize("T,E,k,kind", ROUTE_CASES)
+def test_route_parity(T, E, k, kind):
+    lg = _route_logits(T, E, k, kind, seed=T + E + k)
+    ids = _i32((T, k))
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    moe.moe_route(dev(lg), T, E, k, ids, w)
+    torch.cuda.synchronize()
+    ref_ids, ref_w = oracle.route(lg, k)
+    np.testing.assert_array_equal(ids.cpu().numpy(), ref_ids)
+    assert_close(w.cpu().numpy(), ref_w, 1e-5 * float(np.abs(ref_w).max()), "topk_w")
+
+
+def test_route_empty_and_invalid_args():
+    moe.moe_route(None, 0, 8, 2, None, None)  # T = 0 is a no-op
+    with pytest.raises(moe.MoeError):
+        moe.moe_route(None, 4, 8, 2, None, None)
+    x = torch.zeros((4, 8), device="cuda")
+    with pytest.raises(moe.MoeError):
+        moe.moe_route(x, 4, 8, 9, _i32(36), torch.zeros(36, device="cuda"))  # k > E
+
+
+# ---------------------------------------------------------------- grouping
+PERM_CASES = [(1, 1, 1), (8, 6, 256), (64, 6, 256), (170, 6, 256), (171, 6, 256), (8192, 6, 256),
+              (2048, 8, 128), (3001, 16, 1024), (16, 2, 8), (500, 3, 7)]
+
+
+@pytest.mark.parametrize("T,k,E", PERM_CASES)
+def test_permute_parity(T, k, E):
+    r = np.random.default_rng(T * 31 + k * 7 + E)
+    p = np.exp(-0.01 * np.arange(E)) if E > 1 else np.ones(1)
+    ids = np.stack([r.choice(E, size=k, replace=False, p=p / p.sum()) for _ in range(T)]).astype(np.int32)
+    counts, offsets, perm, inv, status = _i32(E), _i32(E + 1), _i32(T * k), _i32(T * k), torch.zeros(1, dtype=torch.int32, device="cuda")
+    nws = moe.moe_permute_workspace_bytes(T, k, E)
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+    for _ in range(2):  # run twice: results must be identical (deterministic)
+        moe.moe_permute(dev(ids), T, k, E, counts, offsets, perm, inv, ws, nws, status)
+        torch.cuda.synchronize()
+        rc, ro, rp, ri = oracle.permute(ids, E)
+        np.testing.assert_array_equal(counts.cpu().numpy(), rc)
+        np.testing.assert_array_equal(offsets.cpu().numpy(), ro)
+        np.testing.assert_array_equal(perm.cpu().numpy(), rp)
+        np.testing.assert_array_equal(inv.cpu().numpy(), ri)
+    assert int(status.item()) == 0
+
+
+def test_permute_out_of_range_id_sets_status():
+    T, k, E = 300, 4, 16
+    ids = np.tile(np.arange(k, dtype=np.int32), (T, 1))
+    ids[123, 2] = E  # invalid
+    counts, offsets, perm, inv = _i32(E), _i32(E + 1), _i32(T * k), _i32(T * k)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    nws = moe.moe_permute_workspace_bytes(T, k, E)
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+    moe.moe_permute(dev(ids), T, k, E, counts, offsets, perm, inv, ws, nws, status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == moe.MOE_ERANGE
+
+
+# ---------------------------------------------------------------- combine
+@pytest.mark.parametrize("ydt", [moe.MOE_F32, moe.MOE_BF16])
+@pytest.mark.parametrize("T,k,d", [(16, 2, 256), (8, 6, 4096), (777, 8, 2048), (1, 1, 64)])
+def test_combine_parity(T, k, d, ydt):
+    r = np.random.default_rng(T + k + d)
+    y32 = gen.normal(11, gen.TAG_MISC, 0, (T * k, d))
+    if ydt == moe.MOE_BF16:
+        ybits = gen.normal(11, gen.TAG_MISC, 0, (T * k, d), 1.0, gen.BF16)
+        y_dev = torch.from_numpy(ybits.view(np.int16)).view(torch.bfloat16).cuda()
+        y_ref = gen.bf16_bits_to_f32(ybits)
+    else:
+        y_dev, y_ref = dev(y32), y32
+    inv = r.permutation(T * k).astype(np.int32)
+    w = r.random((T, k)).astype(np.float32)
+    out = torch.empty((T, d), dtype=torch.float32, device="cuda")
+    moe.moe_combine(y_dev, ydt, dev(inv), dev(w), T, k, d, out)
+    torch.cuda.synchronize()
+    ref = oracle.combine(y_ref.astype(np.float64), inv, w.astype(np.float64))
+    assert_close(out.cpu().numpy(), ref, f32_tol(ref), "combine")
+
+
+# ---------------------------------------------------------------- expert FFN
+def _ffn_case(w, path, ydt=moe.MOE_F32):
+    """Route, group (oracle) and run the GPU FFN over all-resident experts; compare y_perm."""
+    x = configs.gen_x(w)
+    lg = configs.gen_logits(w) if w.alpha else gen.routing_logits(w.seed, gen.TAG_LOGIT, w.T, w.E, w.k)
+    ids, _ = oracle.route(lg, w.k)
+    counts, offsets, perm, inv = oracle.permute(ids, w.E)
+    arena = device_arena_all_experts(w)
+    A = w.T * w.k
+    nws = moe.moe_expert_ffn_workspace_bytes(w.T, w.k, w.f, w.dtype)
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+    ytd = torch.float32 if ydt == moe.MOE_F32 else torch.bfloat16
+    y = torch.full((A, w.d), float("nan"), dtype=ytd, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    moe.moe_expert_ffn(x_device(w, x), w.dtype, dev(perm), dev(offsets), w.T, w.k, w.E, w.d, w.f,
+                       None, arena, w.entry_bytes, w.dtype, None, None, 0, ws, nws, y, ydt, path,
+                       status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    table = oracle_table(w, sorted(set(ids.ravel().tolist())))
+    ref = oracle.expert_ffn(x, ids, table, perm)
+    return np_of(y), ref
+
+
+def test_ffn_fp32_tiny_parity():
+    w = configs.TINY
+    y, ref = _ffn_case(w, moe.MOE_PATH_AUTO)
+    assert_close(y, ref, f32_tol(ref), "y_perm fp32")
+
+
+SMALL_BF16 = configs.Workload("small_bf16", seed=21, T=150, d=256, E=12, k=3, f=320,
+                              dtype=gen.BF16, alpha=0.5)
+
+
+@pytest.mark.parametrize("path", [moe.MOE_PATH_GEMV, moe.MOE_PATH_GEMM])
+@pytest.mark.parametrize("ydt", [moe.MOE_F32, moe.MOE_BF16])
+def test_ffn_bf16_paths_parity(path, ydt):
+    """Several tiles in every direction and ragged m-tiles (counts not multiples of 16/128)."""
+    y, ref = _ffn_case(SMALL_BF16, path, ydt)
+    assert_close(y, ref, bf16_tol(ref), f"y_perm path={path}")
+
+
+@pytest.mark.parametrize("T", [1, 8, 40])
+def test_ffn_gemv_decode_shapes(T):
+    w = configs.with_(configs.DECODE, T=T, E=16, d=512, f=256)
+    y, ref = _ffn_case(w, moe.MOE_PATH_GEMV)
+    assert_close(y, ref, bf16_tol(ref), "y_perm gemv")
+
+
+def test_ffn_gemm_wide_n_tiles():
+    w = configs.Workload("gemm_wide", seed=22, T=400, d=384, E=6, k=2, f=448, dtype=gen.BF16,
+                         alpha=1.0)
+    y, ref = _ffn_case(w, moe.MOE_PATH_GEMM)
+    assert_close(y, ref, bf16_tol(ref), "y_perm gemm")

@@ -1,0 +1,134 @@
+"""Whole-layer GPU parity (route -> permute -> FFN -> combine) on the five workload shapes."""
+import numpy as np
+import pytest
+import torch
+
+import gen
+from gen import configs
+from gen.arena import device_arena_all_experts
+import oracle
+import expert_ffn_cache_amd as moe
+from expert_ffn_cache_amd.layer import MoeLayer
+from tests._helpers import assert_close, f32_tol, bf16_tol, dev, x_device, oracle_table
+
+pytestmark = pytest.mark.gpu
+
+
+def _tiny_inputs(w):
+    """x and router weight with the top-k margin guard applied to the fp64 router logits:
+    a token row whose k-th/(k+1)-th gap is below 1e-3 is redrawn (next attempt index)."""
+    wr = configs.gen_router_weight(w)
+    x = configs.gen_x(w)
+    for t in range(w.T):
+        for attempt in range(1, 64):
+            lg = np.sort(x[t].astype(np.float64) @ wr.astype(np.float64).T)[::-1]
+            if lg[w.k - 1] - lg[w.k] >= 1e-3:
+                break
+            x[t] = gen.normal(w.seed, gen.TAG_X, configs.x_index(w, 0, attempt) + t * w.d, (w.d,))
+    return x, wr
+
+
+def test_tiny_fp32_layer_end_to_end():
+    """All fp32: router logits, routing, grouping, fp32 SwiGLU experts, combine."""
+    w = configs.TINY
+    x, wr = _tiny_inputs(w)
+    arena = device_arena_all_experts(w)
+    L = MoeLayer(w.T, w.E, w.k, w.d, w.f, dtype=moe.MOE_F32, y_dtype=moe.MOE_F32)
+    logits = torch.empty((w.T, w.E), dtype=torch.float32, device="cuda")
+    moe.moe_router_logits(dev(x), dev(wr), moe.MOE_F32, w.T, w.d, w.E, logits)
+    out = L.forward(dev(x), logits, arena, w.entry_bytes)
+    torch.cuda.synchronize()
+    ref_lg = oracle.router_logits(x, wr)
+    assert_close(logits.cpu().numpy(), ref_lg, 1e-5 * np.abs(ref_lg).max(), "router logits")
+    ids, wt, ref = oracle.moe_layer(x, ref_lg, w.k, oracle_table(w, range(w.E)))
+    np.testing.assert_array_equal(L.ids.cpu().numpy(), ids)
+    assert_close(L.w.cpu().numpy(), wt, 1e-5, "gate weights")
+    assert_close(out.cpu().numpy(), ref, f32_tol(ref), "layer output")
+    assert int(L.status.item()) == 0
+
+
+def _run_layer(w, rotation=0, y_dtype=moe.MOE_F32, arena=None):
+    x = configs.gen_x(w)
+    lg = configs.gen_logits(w, rotation=rotation)
+    if arena is None:
+        arena = device_arena_all_experts(w)
+    L = MoeLayer(w.T, w.E, w.k, w.d, w.f, dtype=w.dtype, y_dtype=y_dtype)
+    L.forward(x_device(w, x), dev(lg), arena, w.entry_bytes)
+    torch.cuda.synchronize()
+    return x, lg, L, arena
+
+
+@pytest.fixture(scope="module")
+def decode_arena():
+    w = configs.DECODE
+    arena = device_arena_all_experts(w)
+    yield arena
+    del arena
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("T", [1, 8, 64])
+def test_decode_layer_full_size(T, decode_arena):
+    """E=256, k=6, d=4096, f=2048, bf16, all experts resident: every output element."""
+    w = configs.with_(configs.DECODE, T=T)
+    x, lg, L, _ = _run_layer(w, arena=decode_arena)
+    ids, wt, ref = oracle.moe_layer(x, lg, w.k, oracle_table(w, sorted(set(oracle.route(lg, w.k)[0].ravel().tolist()))))
+    np.testing.assert_array_equal(L.ids.cpu().numpy(), ids)
+    assert_close(L.out.cpu().numpy(), ref, bf16_tol(ref), f"decode T={T}")
+    assert int(L.status.item()) == 0
+
+
+@pytest.mark.parametrize("alpha", [0.2, 1.0])
+def test_prefill_layer_full_size_sampled(alpha, decode_arena):
+    """T=8192 prefill (GEMM path): ids, counts, perm bit-exact for all tokens; outputs of
+    sampled tokens (first, last, and spread over the most and least loaded experts)."""
+    w = configs.with_(configs.PREFILL, alpha=alpha)
+    # PREFILL uses its own seed; its weights differ from the decode arena's, so regenerate
+    x, lg, L, arena = _run_layer(w)
+    ids, wt = oracle.route(lg, w.k)
+    np.testing.assert_array_equal(L.ids.cpu().numpy(), ids)
+    counts, offsets, perm, inv = oracle.permute(ids, w.E)
+    np.testing.assert_array_equal(L.counts.cpu().numpy(), counts)
+    np.testing.assert_array_equal(L.perm.cpu().numpy(), perm)
+    r = np.random.default_rng(int(alpha * 10))
+    big = int(np.argmax(counts))
+    toks = set([0, w.T - 1]) | set(r.choice(w.T, 10, replace=False).tolist())
+    toks |= set((perm[offsets[big]:offsets[big + 1]][:4] // w.k).tolist())
+    toks = np.array(sorted(toks), dtype=np.int32)
+    need = sorted(set(ids[toks].ravel().tolist()))
+    _, _, ref = oracle.moe_layer(x, lg, w.k, oracle_table(w, need), tokens=toks)
+    out = L.out.cpu().numpy()[toks]
+    assert_close(out, ref, bf16_tol(ref), f"prefill alpha={alpha}")
+    assert int(L.status.item()) == 0
+    del arena
+
+
+def test_layer_is_deterministic_and_graph_replayable():
+    """Two eager runs are bit-identical; a captured graph replayed on new logits matches eager."""
+    w = configs.with_(configs.DECODE, T=8, E=32, d=512, f=256)
+    x = x_device(w, configs.gen_x(w))
+    arena = device_arena_all_experts(w)
+    L = MoeLayer(w.T, w.E, w.k, w.d, w.f)
+    lg_in = torch.empty((w.T, w.E), dtype=torch.float32, device="cuda")
+    outs = []
+    for rot in range(3):
+        lg_in.copy_(dev(configs.gen_logits(w, rotation=rot)))
+        outs.append(L.forward(x, lg_in, arena, w.entry_bytes).clone())
+    again = L.forward(x, lg_in, arena, w.entry_bytes).clone()
+    assert torch.equal(again, outs[-1])
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        L.forward(x, lg_in, arena, w.entry_bytes, stream=s)  # warm-up on the capture stream
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            L.forward(x, lg_in, arena, w.entry_bytes, stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(2):
+        for rot in range(3):
+            lg_in.copy_(dev(configs.gen_logits(w, rotation=rot)))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(L.out, outs[rot]), (rep, rot)
