@@ -71,7 +71,7 @@ def test_lru_hand_traced_sequence_on_device():
     assert int(dc.status.item()) == 0
 
 
-@pytest.mark.parametrize("L,E,S,steps", [(4, 64, 32, 150), (16, 256, 1024, 512)])
+@pytest.mark.parametrize("L,E,S,steps", [(4, 64, 48, 150), (16, 256, 1024, 512)])
 def test_lru_markov_trace_bit_exact(L, E, S, steps):
     """Every call: expert_slot, fill records and (every 16 calls and at the end) all tables
     equal the simulator's.  The second case is the full multi-layer decode workload
@@ -124,7 +124,7 @@ def test_fill_then_ffn_through_slots_and_stale_slot_detection():
     FFN reading weights through expert_slot with the key check -> combine; every step's
     output equals the oracle.  Then a corrupted key makes the FFN report MOE_ERANGE."""
     w = configs.Workload("lru_small", seed=31, T=4, d=256, E=16, k=3, f=192, dtype=gen.BF16,
-                         L=3, S=10, alpha=0.5)
+                         L=3, S=14, alpha=0.5)  # S >= T*k; 3 layers x ~11 unique ids evict
     pool = host_pool(w)
     arena = torch.empty((w.S, w.entry_elems), dtype=torch.bfloat16, device="cuda")
     dc = DevCache(w.L, w.E, w.S, w.entry_bytes, arena, pool)
@@ -139,6 +139,7 @@ def test_fill_then_ffn_through_slots_and_stale_slot_detection():
             lay.route(dev(lg))
             dc.lookup(layer, lay.ids, w.T, w.k)
             f = dc.fills_host()  # synchronises: the one host read per layer
+            assert int(dc.status.item()) == 0, (step, layer)
             for i, (s, l, e, old) in enumerate(f):
                 fills_host[i] = moe.moe_fill_t(s, l, e, old)
             copy.wait_stream(torch.cuda.current_stream())
