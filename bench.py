@@ -1,0 +1,458 @@
+"""Benchmark of the routed-MoE layer hot path on one MI355X.
+
+Primary line: one decode-shaped MoE layer forward (E=256 experts, top-6,
+d=4096, f=2048, bf16 weights, T=8 tokens, all experts resident in HBM):
+route -> permute -> expert FFN (weight-streaming path) -> combine, replayed
+from captured HIP graphs over 16 pre-drawn routing sets.  value = tokens/s.
+
+Extra measurements in the same JSON line ("extra"): the T=8192 prefill
+layer (grouped-GEMM path), the 16-layer decode loop through the bounded LRU
+expert cache with PCIe miss fills, and the 8-layer prefill with full-layer
+double-buffered streaming.  All inputs are seeded synthetic tensors shaped
+like the FreeToken pages' models; weights are random.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload all|decode|prefill|lru|stream]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, TFLOP/s
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def _events(torch, n):
+    return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+
+def _mk_event(torch, stream, timing=False):
+    """A torch event whose HIP handle exists (recorded once), so it can be passed to the C ABI."""
+    ev = torch.cuda.Event(enable_timing=timing)
+    ev.record(stream)
+    return ev
+
+
+def _ffn_bytes(w, U):
+    """Algorithmic HBM bytes of one expert-FFN call: every used expert entry once, token rows
+    gathered once per assignment, h written and read once (bf16), y written once (fp32)."""
+    A = w.T * w.k
+    return U * w.entry_bytes + A * w.d * 2 + 2 * A * w.f * 2 + A * w.d * 4
+
+
+def _ffn_flops(w):
+    return 2.0 * w.T * w.k * 3 * w.d * w.f
+
+
+def _counter_traffic(kernel_src, name):
+    """HBM bytes per FFN call from the committed rocprofv3 counter summary, if it was taken
+    on the current kernel source (sha256 match); else None."""
+    path = os.path.join(PROFILES, name)
+    if not os.path.exists(path):
+        return None
+    sha = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.lstrip().startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256") != sha or "hbm_bytes_per_call" not in vals:
+        return None
+    return float(vals["hbm_bytes_per_call"])
+
+
+# ------------------------------------------------------------------------ decode layer
+def bench_decode(args, torch, moe):
+    from gen import configs
+    from gen.arena import device_arena_all_experts
+    from expert_ffn_cache_amd.layer import MoeLayer
+
+    w = configs.with_(configs.DECODE, T=args.decode_T, alpha=args.alpha)
+    R = 16
+    t0 = time.time()
+    arena = device_arena_all_experts(w)
+    log(f"[decode] arena {w.E} x {w.entry_bytes / 1e6:.1f} MB generated in {time.time() - t0:.1f}s")
+    x = torch.from_numpy(configs.gen_x(w).view(np.int16)).view(torch.bfloat16).cuda()
+    logits = [torch.from_numpy(configs.gen_logits(w, rotation=r)).cuda() for r in range(R)]
+    layers = [MoeLayer(w.T, w.E, w.k, w.d, w.f) for _ in range(R)]
+    s = torch.cuda.Stream()
+    graphs = []
+    with torch.cuda.stream(s):
+        for r in range(R):
+            layers[r].forward(x, logits[r], arena, w.entry_bytes, stream=s)
+        s.synchronize()
+        U = [int((layers[r].counts > 0).sum().item()) for r in range(R)]
+        for r in range(R):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                layers[r].forward(x, logits[r], arena, w.entry_bytes, stream=s)
+            graphs.append(g)
+        for i in range(args.warmup):
+            graphs[i % R].replay()
+        s.synchronize()
+        e0, e1 = _events(torch, 2)
+        torch.cuda.synchronize()
+        e0.record(s)
+        for i in range(args.steps):
+            graphs[i % R].replay()
+        e1.record(s)
+        torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    # the dominant entry point (expert FFN: gate/up + down weight-streaming kernels), timed
+    # per call with events on its stream
+    ffn_ms = []
+    with torch.cuda.stream(s):
+        n = max(args.steps, 2 * R)
+        starts, ends = _events(torch, n), _events(torch, n)
+        for i in range(n):
+            r = i % R
+            starts[i].record(s)
+            layers[r].ffn(x, arena, w.entry_bytes, stream=s)
+            ends[i].record(s)
+        torch.cuda.synchronize()
+        ffn_ms = [starts[i].elapsed_time(ends[i]) for i in range(n)]
+        byts = [_ffn_bytes(w, U[i % R]) for i in range(n)]
+    status = max(int(layers[r].status.item()) for r in range(R))
+    if status != 0:
+        raise RuntimeError(f"decode: device status {status}")
+    ffn_avg_ms = float(np.mean(ffn_ms))
+    achieved = float(np.sum(byts) / (np.sum(ffn_ms) * 1e-3) / 1e9)
+    traffic = _counter_traffic(os.path.join(ROOT, "expert_ffn_cache_amd", "csrc", "ffn.hip"),
+                               "ffn_gemv_decode_e256_k6_d4096_f2048_T8_counters.txt")
+    del graphs, arena
+    torch.cuda.empty_cache()
+    return dict(
+        workload=w.name, T=w.T, ms_per_step=ms, tok_s=w.T / (ms * 1e-3), U_mean=float(np.mean(U)),
+        ffn_ms=ffn_avg_ms,
+        roofline=dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
+                      frac=achieved / HBM_PEAK_GBS,
+                      traffic=None if traffic is None else traffic),
+        algorithmic_bytes_per_call=float(np.mean(byts)))
+
+
+# ------------------------------------------------------------------------ prefill layer
+def bench_prefill(args, torch, moe):
+    from gen import configs
+    from gen.arena import device_arena_all_experts
+    from expert_ffn_cache_amd.layer import MoeLayer
+
+    out = {}
+    t0 = time.time()
+    base = configs.PREFILL
+    arena = device_arena_all_experts(base)
+    log(f"[prefill] arena generated in {time.time() - t0:.1f}s")
+    x = torch.from_numpy(configs.gen_x(base).view(np.int16)).view(torch.bfloat16).cuda()
+    for alpha in (0.2, 1.0):
+        w = configs.with_(base, alpha=alpha)
+        R = 2
+        logits = [torch.from_numpy(configs.gen_logits(w, rotation=r)).cuda() for r in range(R)]
+        layers = [MoeLayer(w.T, w.E, w.k, w.d, w.f, y_dtype=moe.MOE_BF16) for _ in range(R)]
+        s = torch.cuda.Stream()
+        steps = max(4, args.steps // 5)
+        with torch.cuda.stream(s):
+            for r in range(R):
+                layers[r].forward(x, logits[r], arena, w.entry_bytes, stream=s)
+            s.synchronize()
+            U = [int((layers[r].counts > 0).sum().item()) for r in range(R)]
+            maxc = [int(layers[r].counts.max().item()) for r in range(R)]
+            graphs = []
+            for r in range(R):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=s):
+                    layers[r].forward(x, logits[r], arena, w.entry_bytes, stream=s)
+                graphs.append(g)
+            for i in range(2):
+                graphs[i % R].replay()
+            e0, e1 = _events(torch, 2)
+            torch.cuda.synchronize()
+            e0.record(s)
+            for i in range(steps):
+                graphs[i % R].replay()
+            e1.record(s)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / steps
+            starts, ends = _events(torch, steps), _events(torch, steps)
+            for i in range(steps):
+                starts[i].record(s)
+                layers[i % R].ffn(x, arena, w.entry_bytes, stream=s)
+                ends[i].record(s)
+            torch.cuda.synchronize()
+        ffn_ms = float(np.mean([starts[i].elapsed_time(ends[i]) for i in range(steps)]))
+        status = max(int(l.status.item()) for l in layers)
+        if status != 0:
+            raise RuntimeError(f"prefill: device status {status}")
+        fl = _ffn_flops(w)
+        byts = float(np.mean([_ffn_bytes(w, u) for u in U]))
+        out[f"alpha_{alpha}"] = dict(
+            T=w.T, ms_per_step=ms, tok_s=w.T / (ms * 1e-3), ffn_ms=ffn_ms, U_mean=float(np.mean(U)),
+            max_tokens_per_expert=int(np.max(maxc)),
+            ffn_tflops=fl / (ffn_ms * 1e-3) / 1e12, mfma_frac=fl / (ffn_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            ffn_weight_gbs=byts / (ffn_ms * 1e-3) / 1e9,
+            hbm_frac=byts / (ffn_ms * 1e-3) / 1e9 / HBM_PEAK_GBS)
+        del graphs, layers
+    out["workload"] = base.name
+    del arena
+    torch.cuda.empty_cache()
+    return out
+
+
+# ------------------------------------------------------------------------ multi-layer LRU decode
+def bench_lru(args, torch, moe):
+    import ctypes
+    from gen import configs
+    import gen
+    from gen.arena import host_pool
+    from expert_ffn_cache_amd.layer import MoeLayer
+
+    w = configs.LRU_DECODE
+    steps = args.lru_steps
+    t0 = time.time()
+    pool = host_pool(w)
+    log(f"[lru] pinned pool {pool.numel() * 2 / 1e9:.1f} GB in {time.time() - t0:.1f}s")
+    _, lg = gen.markov_routing(w.seed, steps, w.L, w.T, w.E, w.k, w.p_stay, w.zipf_s)
+    logits = torch.from_numpy(lg).cuda()
+    xs = [torch.from_numpy(configs.gen_x(w, l).view(np.int16)).view(torch.bfloat16).cuda()
+          for l in range(w.L)]
+    arena = torch.empty((w.S, w.entry_elems), dtype=torch.bfloat16, device="cuda")
+    i32 = dict(dtype=torch.int32, device="cuda")
+    i64 = dict(dtype=torch.int64, device="cuda")
+    slot_of, key_of = torch.empty(w.L * w.E, **i32), torch.empty(w.S, **i32)
+    stamp, clock, stats = torch.empty(w.S, **i64), torch.empty(1, **i64), torch.empty(4, **i64)
+    status = torch.zeros(1, **i32)
+    desc = moe.moe_cache_t(w.L, w.E, w.S, 0, w.entry_bytes, slot_of.data_ptr(), key_of.data_ptr(),
+                           stamp.data_ptr(), clock.data_ptr(), stats.data_ptr(), status.data_ptr(),
+                           arena.data_ptr(), pool.data_ptr())
+    expert_slot = torch.empty(w.E, **i32)
+    fills_dev = torch.empty((w.E + 1) * 4, **i32)  # records, then n_fills in the last word
+    n_fills_dev = fills_dev[w.E * 4:]
+    mirror = torch.empty((w.E + 1) * 4, dtype=torch.int32, pin_memory=True)
+    masks = torch.zeros((2, 2, w.E), dtype=torch.uint8, pin_memory=True)
+    masks_dev = torch.zeros((w.L, 2, w.E), dtype=torch.uint8, device="cuda")
+    lay = MoeLayer(w.T, w.E, w.k, w.d, w.f)
+    comp, copy = torch.cuda.Stream(), torch.cuda.Stream()
+    last_ffn = _mk_event(torch, comp)
+    fill_done = _mk_event(torch, copy)
+    got = torch.cuda.Event()
+    with torch.cuda.stream(comp):
+        moe.cache_init(desc, comp)
+        torch.cuda.synchronize()
+        t_start = time.time()
+        for s in range(steps):
+            for l in range(w.L):
+                lay.route(logits[s, l], comp)
+                moe.cache_lookup_update(desc, l, lay.ids, w.T, w.k, expert_slot, fills_dev,
+                                        n_fills_dev, comp)
+                mirror.copy_(fills_dev, non_blocking=True)
+                got.record(comp)
+                lay.permute(comp)
+                got.synchronize()  # the one host read per layer: the fill list
+                n = int(mirror[w.E * 4])
+                miss = mirror[:n * 4].view(n, 4).numpy()[:, 2] if n else np.zeros(0, np.int64)
+                mk = masks[l % 2].numpy()
+                mk[0, :] = 1
+                mk[0, miss] = 0     # hits (experts with no tokens are skipped anyway)
+                mk[1, :] = 0
+                mk[1, miss] = 1     # misses
+                masks_dev[l].copy_(masks[l % 2], non_blocking=True)
+                if n:
+                    copy.wait_event(last_ffn)  # WAR: earlier readers of the victim slots
+                    moe.cache_fill(desc, mirror.data_ptr(), n, copy)
+                    fill_done.record(copy)
+                lay.ffn(xs[l], arena, w.entry_bytes, expert_slot, mask=masks_dev[l, 0],
+                        slot_key=key_of, key_base=l * w.E, stream=comp)
+                if n:
+                    comp.wait_event(fill_done)
+                    lay.ffn(xs[l], arena, w.entry_bytes, expert_slot, mask=masks_dev[l, 1],
+                            slot_key=key_of, key_base=l * w.E, stream=comp)
+                lay.combine(comp)
+                last_ffn.record(comp)
+        torch.cuda.synchronize()
+        wall = time.time() - t_start
+    st = stats.cpu().numpy()
+    if int(status.item()) != 0 or int(lay.status.item()) != 0:
+        raise RuntimeError(f"lru: status {int(status.item())} / {int(lay.status.item())}")
+    del pool, arena
+    torch.cuda.empty_cache()
+    return dict(workload=w.name, steps=steps, tok_s=steps * w.T / wall, wall_s=wall,
+                miss_rate=float(st[2] / st[0]), hits=int(st[1]), misses=int(st[2]),
+                fill_gb=float(st[3] / 1e9), fill_gb_per_step=float(st[3] / 1e9 / steps))
+
+
+# ------------------------------------------------------------------------ streamed prefill
+def bench_stream(args, torch, moe):
+    from gen import configs
+    from gen.arena import host_pool
+    from expert_ffn_cache_amd.layer import MoeLayer
+
+    w = configs.STREAM_PREFILL
+    t0 = time.time()
+    pool = host_pool(w)
+    log(f"[stream] pinned pool {pool.numel() * 2 / 1e9:.2f} GB in {time.time() - t0:.1f}s")
+    layer_bytes = w.E * w.entry_bytes
+    bufs = [torch.empty((w.E, w.entry_elems), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    xs = [torch.from_numpy(configs.gen_x(w, l).view(np.int16)).view(torch.bfloat16).cuda()
+          for l in range(w.L)]
+    lgs = [torch.from_numpy(configs.gen_logits(w, layer=l)).cuda() for l in range(w.L)]
+    layers = [MoeLayer(w.T, w.E, w.k, w.d, w.f, y_dtype=moe.MOE_BF16) for _ in range(w.L)]
+    comp, copy = torch.cuda.Stream(), torch.cuda.Stream()
+    # measured pinned H2D bandwidth (one layer block)
+    with torch.cuda.stream(copy):
+        a, b = _events(torch, 2)
+        bufs[0].copy_(pool[:w.E], non_blocking=True)
+        torch.cuda.synchronize()
+        a.record(copy)
+        for _ in range(3):
+            bufs[0].copy_(pool[:w.E], non_blocking=True)
+        b.record(copy)
+        torch.cuda.synchronize()
+    h2d_gbs = 3 * layer_bytes / (a.elapsed_time(b) * 1e-3) / 1e9
+    runs = []
+    for rep in range(3):
+        ready = [_mk_event(torch, copy, timing=True) for _ in range(w.L)]
+        cstart = _events(torch, w.L)
+        cend = _events(torch, w.L)
+        pstart = _events(torch, w.L)
+        free = [_mk_event(torch, comp) for _ in range(2)]
+        torch.cuda.synchronize()
+        t_start = _events(torch, 1)[0]
+        t_start.record(copy)
+        pstart[0].record(copy)
+        moe.layer_stream_prefetch(pool[0].data_ptr(), bufs[0], layer_bytes, 1, copy, None, ready[0])
+        for l in range(w.L):
+            if l + 1 < w.L:
+                nb = (l + 1) % 2
+                if l >= 1:
+                    copy.wait_event(free[nb])  # compute of layer l-1 released this buffer
+                pstart[l + 1].record(copy)
+                moe.layer_stream_prefetch(pool[(l + 1) * w.E].data_ptr(), bufs[nb], layer_bytes,
+                                          1, copy, None, ready[l + 1])
+            comp.wait_event(ready[l])
+            cstart[l].record(comp)
+            layers[l].forward(xs[l], lgs[l], bufs[l % 2], w.entry_bytes, stream=comp)
+            cend[l].record(comp)
+            free[l % 2].record(comp)
+        torch.cuda.synchronize()
+        wall_ms = t_start.elapsed_time(cend[-1])
+        copies = [(t_start.elapsed_time(pstart[l]), t_start.elapsed_time(ready[l])) for l in range(w.L)]
+        comps = [(t_start.elapsed_time(cstart[l]), t_start.elapsed_time(cend[l])) for l in range(w.L)]
+        ov = 0.0
+        for c0, c1 in comps:
+            for p0, p1 in copies:
+                ov += max(0.0, min(c1, p1) - max(c0, p0))
+        runs.append((wall_ms, copies, comps, ov / sum(c1 - c0 for c0, c1 in comps)))
+    wall_ms, copies, comps, overlap = min(runs, key=lambda r: r[0])
+    status = max(int(l.status.item()) for l in layers)
+    if status != 0:
+        raise RuntimeError(f"stream: device status {status}")
+    ideal_ms = w.L * layer_bytes / (h2d_gbs * 1e9) * 1e3
+    del pool, bufs
+    torch.cuda.empty_cache()
+    return dict(workload=w.name, tok_s=w.T / (wall_ms * 1e-3), wall_ms=wall_ms,
+                h2d_gbs=h2d_gbs, ideal_ms=ideal_ms, efficiency=ideal_ms / wall_ms,
+                overlap=overlap, copy_ms_per_layer=float(np.mean([b - a for a, b in copies])),
+                compute_ms_per_layer=float(np.mean([b - a for a, b in comps])))
+
+
+# ------------------------------------------------------------------------ CPU baseline
+def cpu_baseline(args):
+    """The oracle (plain double-precision C, OpenMP over tokens) on the decode layer, timed on
+    the host cores for whole T=8 layers over rotated routing sets, about 10-20 s in total."""
+    from gen import configs
+    import oracle
+
+    w = configs.with_(configs.DECODE, T=args.decode_T, alpha=args.alpha)
+    x = configs.gen_x(w)
+    spent, tokens, layers = 0.0, 0, 0
+    for r in range(16):
+        lg = configs.gen_logits(w, rotation=r)
+        ids, _ = oracle.route(lg, w.k)
+        table = oracle.ExpertTable(w.E, {e: configs.gen_expert(w, 0, e)
+                                         for e in sorted(set(ids.ravel().tolist()))})
+        t0 = time.perf_counter()
+        oracle.moe_layer(x, lg, w.k, table)
+        spent += time.perf_counter() - t0
+        tokens += w.T
+        layers += 1
+        if spent > args.cpu_seconds:
+            break
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return dict(value=tokens / spent, unit="tokens/s", cores=min(w.T, threads), kind="oracle",
+                sample=f"{layers} whole decode layers (T={w.T}, E={w.E}, k={w.k}, d={w.d}, "
+                       f"f={w.f}, bf16 weights) over rotated routing sets, {spent:.1f} s")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="all", choices=["all", "decode", "prefill", "lru", "stream"])
+    ap.add_argument("--decode-T", type=int, default=8)
+    ap.add_argument("--alpha", type=float, default=0.2)
+    ap.add_argument("--lru-steps", type=int, default=512)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build has no "
+              "multi-GPU path; see the sharding notes in DESIGN.md.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import expert_ffn_cache_amd as moe
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    moe.lib()
+    wl = args.workload
+    extra = {}
+    dec = bench_decode(args, torch, moe) if wl in ("all", "decode") else None
+    if dec:
+        log(f"[decode] {dec['tok_s']:.0f} tok/s, {dec['ms_per_step'] * 1e3:.1f} us/layer, "
+            f"ffn {dec['ffn_ms'] * 1e3:.1f} us, {dec['roofline']['achieved']:.0f} GB/s")
+    if wl in ("all", "prefill"):
+        extra["prefill"] = bench_prefill(args, torch, moe)
+        log(f"[prefill] {json.dumps(extra['prefill'])}")
+    if wl in ("all", "stream"):
+        extra["stream_prefill"] = bench_stream(args, torch, moe)
+        log(f"[stream] {json.dumps(extra['stream_prefill'])}")
+    if wl in ("all", "lru"):
+        extra["lru_decode"] = bench_lru(args, torch, moe)
+        log(f"[lru] {json.dumps(extra['lru_decode'])}")
+    cpu = None
+    if dec and not args.no_cpu_baseline:
+        cpu = cpu_baseline(args)
+        log(f"[cpu] {json.dumps(cpu)}")
+    if dec is None:
+        print(json.dumps(extra))
+        return
+    line = {
+        "metric": "MoE-layer tokens/s at decode T=8 & prefill T=8192; % HBM/MFMA peak",
+        "value": dec["tok_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": dec["ms_per_step"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": dec["workload"], "T": dec["T"], "E": 256, "k": 6, "d": 4096,
+                   "f": 2048, "zipf_alpha": args.alpha, "experts_resident": 256,
+                   "graph_replay": True},
+        "roofline": dec["roofline"],
+        "cpu_baseline": cpu,
+        "extra": dict(decode_ffn_ms=dec["ffn_ms"], decode_unique_experts=dec["U_mean"],
+                      decode_algorithmic_bytes_per_ffn=dec["algorithmic_bytes_per_call"], **extra),
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -29,9 +29,31 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return (uint16_t)(u >> 16);
 }
 
-__device__ __forceinline__ u32x4 ldg16(const void* p) { return *(const u32x4*)p; }
+typedef const __attribute__((address_space(1))) u32x4* gptr16;
+
+// 16-byte global load (global_load_dwordx4, not a flat load).
+__device__ __forceinline__ u32x4 ldg16(const void* p) { return *(gptr16)p; }
+
+// Compiler-only fence: memory operations are not moved across it.  Placed after
+// prefetch loads so they are issued where written instead of being sunk to their use.
+__device__ __forceinline__ void issue_fence() { asm volatile("" ::: "memory"); }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// s_waitcnt immediate (gfx9 encoding): vmcnt in [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8].
+constexpr int waitcnt_imm(int vm, int exp, int lgkm) {
+  return (vm & 0xF) | ((vm >> 4) << 14) | ((exp & 0x7) << 4) | ((lgkm & 0xF) << 8);
+}
+
+// Workgroup barrier for LDS hand-off only: waits for this wave's LDS operations, then
+// s_barrier.  Unlike __syncthreads() it does not drain outstanding global loads, so
+// prefetches issued before the barrier stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 7, 0));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 // Sticky device status: keep the first error code.
 __device__ __forceinline__ void set_status(int32_t* status, int code) {

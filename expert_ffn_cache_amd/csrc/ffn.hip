@@ -28,6 +28,7 @@
 // 64-wide step (A and B fragments use the same permutation), which is what
 // lets each lane load 32 contiguous bytes per row.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 
@@ -144,6 +145,45 @@ __device__ __forceinline__ GemvItem gemv_item(const FfnArgs& p, int a) {
 }
 
 // Gate/up: wave owns units i0..i0+15 of W_gate and W_up; MC chunks of 16 tokens.
+// Two register sets alternate (no register rotation), so the next step's loads stay in
+// flight while the current step's MFMAs run.  Token rows beyond the expert load a valid
+// row and their (unused) output rows are not stored: an MFMA output row depends only
+// on its own input row.
+template <int MC>
+struct GuStage {
+  u32x4 g0, g1, u0, u1;
+  u32x4 a0[MC], a1[MC];
+};
+
+template <int MC>
+__device__ __forceinline__ void gu_load(GuStage<MC>& s, const uint16_t* pg, const uint16_t* pu,
+                                        const uint16_t* const (&px)[MC], int kk) {
+  s.g0 = ldg16(pg + kk);
+  s.g1 = ldg16(pg + kk + 8);
+  s.u0 = ldg16(pu + kk);
+  s.u1 = ldg16(pu + kk + 8);
+#pragma unroll
+  for (int mc = 0; mc < MC; ++mc) {
+    s.a0[mc] = ldg16(px[mc] + kk);
+    s.a1[mc] = ldg16(px[mc] + kk + 8);
+  }
+  issue_fence();
+}
+
+template <int MC>
+__device__ __forceinline__ void gu_mma(const GuStage<MC>& s, f32x4 (&ag)[MC], f32x4 (&au)[MC],
+                                       int live) {
+#pragma unroll
+  for (int mc = 0; mc < MC; ++mc) {
+    if (mc < live) {
+      ag[mc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(s.a0[mc]), as_bf16x8(s.g0), ag[mc], 0, 0, 0);
+      au[mc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(s.a0[mc]), as_bf16x8(s.u0), au[mc], 0, 0, 0);
+      ag[mc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(s.a1[mc]), as_bf16x8(s.g1), ag[mc], 0, 0, 0);
+      au[mc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(s.a1[mc]), as_bf16x8(s.u1), au[mc], 0, 0, 0);
+    }
+  }
+}
+
 template <int MC>
 __global__ __launch_bounds__(256) void gemv_gateup(FfnArgs p) {
   const int nrb = p.f >> 6;
@@ -154,64 +194,33 @@ __global__ __launch_bounds__(256) void gemv_gateup(FfnArgs p) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, kg = lane >> 4;
   const int i0 = rb * 64 + wave * 16;
-  const int d = p.d;
+  const int d = p.d, nst = d >> 6;
   const uint16_t* pg = it.w + (size_t)(i0 + col) * d + kg * 16;
   const uint16_t* pu = pg + (size_t)p.f * d;
   const uint16_t* X = (const uint16_t*)p.x;
   uint16_t* H = (uint16_t*)p.h;
-  const u32x4 zero = {0u, 0u, 0u, 0u};
 
   for (int m0 = 0; m0 < n; m0 += 16 * MC) {
     const uint16_t* px[MC];
-    bool vx[MC];
 #pragma unroll
     for (int mc = 0; mc < MC; ++mc) {
-      const int r = m0 + mc * 16 + col;
-      vx[mc] = r < n;
-      px[mc] = X + (size_t)(vx[mc] ? p.perm[n0 + r] / p.k : 0) * d + kg * 16;
+      const int r = min(m0 + mc * 16 + col, n - 1);
+      px[mc] = X + (size_t)(p.perm[n0 + r] / p.k) * d + kg * 16;
     }
+    const int live = (n - m0 + 15) >> 4;  // 16-row chunks with tokens
     f32x4 ag[MC], au[MC];
 #pragma unroll
     for (int mc = 0; mc < MC; ++mc) {
       ag[mc] = f32x4{0.f, 0.f, 0.f, 0.f};
       au[mc] = ag[mc];
     }
-    u32x4 bg0 = ldg16(pg), bg1 = ldg16(pg + 8), bu0 = ldg16(pu), bu1 = ldg16(pu + 8);
-    u32x4 ax0[MC], ax1[MC];
-#pragma unroll
-    for (int mc = 0; mc < MC; ++mc) {
-      ax0[mc] = vx[mc] ? ldg16(px[mc]) : zero;
-      ax1[mc] = vx[mc] ? ldg16(px[mc] + 8) : zero;
-    }
-    for (int kk = 0; kk < d; kk += 64) {
-      u32x4 nbg0 = zero, nbg1 = zero, nbu0 = zero, nbu1 = zero, nax0[MC], nax1[MC];
-      const int kn = kk + 64;
-      if (kn < d) {
-        nbg0 = ldg16(pg + kn);
-        nbg1 = ldg16(pg + kn + 8);
-        nbu0 = ldg16(pu + kn);
-        nbu1 = ldg16(pu + kn + 8);
-      }
-#pragma unroll
-      for (int mc = 0; mc < MC; ++mc) {
-        nax0[mc] = (kn < d && vx[mc]) ? ldg16(px[mc] + kn) : zero;
-        nax1[mc] = (kn < d && vx[mc]) ? ldg16(px[mc] + kn + 8) : zero;
-      }
-#pragma unroll
-      for (int mc = 0; mc < MC; ++mc) {
-        if (m0 + mc * 16 < n) {
-          ag[mc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ax0[mc]), as_bf16x8(bg0), ag[mc], 0, 0, 0);
-          au[mc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ax0[mc]), as_bf16x8(bu0), au[mc], 0, 0, 0);
-          ag[mc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ax1[mc]), as_bf16x8(bg1), ag[mc], 0, 0, 0);
-          au[mc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ax1[mc]), as_bf16x8(bu1), au[mc], 0, 0, 0);
-        }
-      }
-      bg0 = nbg0; bg1 = nbg1; bu0 = nbu0; bu1 = nbu1;
-#pragma unroll
-      for (int mc = 0; mc < MC; ++mc) {
-        ax0[mc] = nax0[mc];
-        ax1[mc] = nax1[mc];
-      }
+    GuStage<MC> s0, s1;
+    gu_load(s0, pg, pu, px, 0);
+    for (int st = 0; st < nst; st += 2) {
+      gu_load(s1, pg, pu, px, min(st + 1, nst - 1) * 64);
+      gu_mma(s0, ag, au, live);
+      gu_load(s0, pg, pu, px, min(st + 2, nst - 1) * 64);
+      if (st + 1 < nst) gu_mma(s1, ag, au, live);
     }
     // lane holds C[4*kg + i][col] of each 16x16 tile: token rows, unit columns
 #pragma unroll
@@ -227,6 +236,36 @@ __global__ __launch_bounds__(256) void gemv_gateup(FfnArgs p) {
 }
 
 // Down: wave owns output channels o0..o0+15 of W_down; rows of h are contiguous.
+template <int MC>
+struct DnStage {
+  u32x4 b0, b1;
+  u32x4 a0[MC], a1[MC];
+};
+
+template <int MC>
+__device__ __forceinline__ void dn_load(DnStage<MC>& s, const uint16_t* pw,
+                                        const uint16_t* const (&ph)[MC], int kk) {
+  s.b0 = ldg16(pw + kk);
+  s.b1 = ldg16(pw + kk + 8);
+#pragma unroll
+  for (int mc = 0; mc < MC; ++mc) {
+    s.a0[mc] = ldg16(ph[mc] + kk);
+    s.a1[mc] = ldg16(ph[mc] + kk + 8);
+  }
+  issue_fence();
+}
+
+template <int MC>
+__device__ __forceinline__ void dn_mma(const DnStage<MC>& s, f32x4 (&acc)[MC], int live) {
+#pragma unroll
+  for (int mc = 0; mc < MC; ++mc) {
+    if (mc < live) {
+      acc[mc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(s.a0[mc]), as_bf16x8(s.b0), acc[mc], 0, 0, 0);
+      acc[mc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(s.a1[mc]), as_bf16x8(s.b1), acc[mc], 0, 0, 0);
+    }
+  }
+}
+
 template <int MC, int YDT>
 __global__ __launch_bounds__(256) void gemv_down(FfnArgs p) {
   const int nrb = p.d >> 6;
@@ -237,55 +276,28 @@ __global__ __launch_bounds__(256) void gemv_down(FfnArgs p) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, kg = lane >> 4;
   const int o0 = rb * 64 + wave * 16;
-  const int f = p.f;
+  const int f = p.f, nst = f >> 6;
   const uint16_t* pw = it.w + 2 * (size_t)f * p.d + (size_t)(o0 + col) * f + kg * 16;
   const uint16_t* H = (const uint16_t*)p.h;
-  const u32x4 zero = {0u, 0u, 0u, 0u};
 
   for (int m0 = 0; m0 < n; m0 += 16 * MC) {
     const uint16_t* ph[MC];
-    bool vh[MC];
 #pragma unroll
     for (int mc = 0; mc < MC; ++mc) {
-      const int r = m0 + mc * 16 + col;
-      vh[mc] = r < n;
-      ph[mc] = H + (size_t)(n0 + (vh[mc] ? r : 0)) * f + kg * 16;
+      const int r = min(m0 + mc * 16 + col, n - 1);
+      ph[mc] = H + (size_t)(n0 + r) * f + kg * 16;
     }
+    const int live = (n - m0 + 15) >> 4;
     f32x4 acc[MC];
 #pragma unroll
     for (int mc = 0; mc < MC; ++mc) acc[mc] = f32x4{0.f, 0.f, 0.f, 0.f};
-    u32x4 b0 = ldg16(pw), b1 = ldg16(pw + 8);
-    u32x4 a0[MC], a1[MC];
-#pragma unroll
-    for (int mc = 0; mc < MC; ++mc) {
-      a0[mc] = vh[mc] ? ldg16(ph[mc]) : zero;
-      a1[mc] = vh[mc] ? ldg16(ph[mc] + 8) : zero;
-    }
-    for (int kk = 0; kk < f; kk += 64) {
-      const int kn = kk + 64;
-      u32x4 nb0 = zero, nb1 = zero, na0[MC], na1[MC];
-      if (kn < f) {
-        nb0 = ldg16(pw + kn);
-        nb1 = ldg16(pw + kn + 8);
-      }
-#pragma unroll
-      for (int mc = 0; mc < MC; ++mc) {
-        na0[mc] = (kn < f && vh[mc]) ? ldg16(ph[mc] + kn) : zero;
-        na1[mc] = (kn < f && vh[mc]) ? ldg16(ph[mc] + kn + 8) : zero;
-      }
-#pragma unroll
-      for (int mc = 0; mc < MC; ++mc) {
-        if (m0 + mc * 16 < n) {
-          acc[mc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a0[mc]), as_bf16x8(b0), acc[mc], 0, 0, 0);
-          acc[mc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a1[mc]), as_bf16x8(b1), acc[mc], 0, 0, 0);
-        }
-      }
-      b0 = nb0; b1 = nb1;
-#pragma unroll
-      for (int mc = 0; mc < MC; ++mc) {
-        a0[mc] = na0[mc];
-        a1[mc] = na1[mc];
-      }
+    DnStage<MC> s0, s1;
+    dn_load(s0, pw, ph, 0);
+    for (int st = 0; st < nst; st += 2) {
+      dn_load(s1, pw, ph, min(st + 1, nst - 1) * 64);
+      dn_mma(s0, acc, live);
+      dn_load(s0, pw, ph, min(st + 2, nst - 1) * 64);
+      if (st + 1 < nst) dn_mma(s1, acc, live);
     }
 #pragma unroll
     for (int mc = 0; mc < MC; ++mc) {
@@ -303,28 +315,67 @@ __global__ __launch_bounds__(256) void gemv_down(FfnArgs p) {
 }
 
 // ------------------------------------------------------------------ GEMM path
-constexpr int GBM = 128, GBN = 128, GBK = 64;
+// Tile: 256 grouped token rows x 256 weight rows per workgroup of 8 waves (two per SIMD,
+// so one wave's LDS-read latency is covered by the other's MFMAs), k in steps of 32.
+// Both operands go global -> LDS with direct loads (global_load_lds_dwordx4: lane i
+// lands at LDS base + 16 i) into a 4-stage ring of 32 KB stages
+// [256 token rows x 64 B | 256 weight rows x 64 B]: three k-steps of loads are in flight
+// while one is consumed, and no VGPR holds staging data.  Each wave's own counter
+// (s_waitcnt vmcnt) says when its part of a stage has landed; one LDS barrier per step
+// publishes the stage and frees the oldest one.
+// Wave (wm, wn) computes token rows wm*128 + [0,128) (four 32-row m-tiles) against weight
+// rows wn*64 + [0,64) (two 32-row n-tiles; for gate/up, 32 gate units and the same 32 up
+// units, so SiLU(g)*u is formed in registers) with v_mfma_f32_32x32x16_bf16.
+// Token rows are gathered through perm (gate/up) or read contiguously (down); rows past
+// the expert repeat a valid row and their outputs are not stored.  Workgroups are
+// persistent; the (expert, n-tile, m-tile) list is derived on the device from offsets
+// and dealt XCD-major so consecutive items (sharing weight rows or token rows) run at
+// the same time on one XCD's L2.
+constexpr int QBM = 256, QBN = 256, QBK = 32;
 constexpr int kGateUp = 0, kDown = 1;
 
-__device__ __forceinline__ int swz(int r, int c) { return r * GBK + ((c ^ (r & 7)) << 3); }
+// Element index of 16-byte chunk c (0..3) of row r in a 64-byte-row tile; the XOR spreads
+// the 16 rows served by one ds_read_b128 cycle over all LDS banks.
+__device__ __forceinline__ int qswz(int r, int c) { return r * QBK + ((c ^ ((r >> 2) & 3)) << 3); }
+
+// 16 bytes per lane, global -> LDS (lane i lands at lds_wave_base + 16 i).  Issued from
+// inline assembly so the compiler does not drain every outstanding load before each LDS
+// read (it cannot tell which stage a direct load writes); stage readiness is tracked
+// with explicit s_waitcnt vmcnt below.  Sets M0 itself (nothing else in these kernels
+// uses M0); has no output registers.
+__device__ __forceinline__ void g2lds16(const uint16_t* g, const uint16_t* lds_wave_base) {
+  const uint32_t l = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_wave_base;
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(__builtin_amdgcn_readfirstlane(l)), "v"(g) : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(N, 7, 15));
+  asm volatile("" ::: "memory");
+}
 
 template <int MODE, int YDT>
-__global__ __launch_bounds__(256, 2) void gemm_grouped(FfnArgs p, int n_ntiles) {
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][GBM * GBK];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][GBN * GBK];
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemm_tile256(FfnArgs p, int n_ntiles) {
+  // one array per ring stage: [token rows | weight rows], 32 KB each
+  __shared__ __attribute__((aligned(1024))) uint16_t sm0[2 * QBM * QBK];
+  __shared__ __attribute__((aligned(1024))) uint16_t sm1[2 * QBM * QBK];
+  __shared__ __attribute__((aligned(1024))) uint16_t sm2[2 * QBM * QBK];
+  __shared__ __attribute__((aligned(1024))) uint16_t sm3[2 * QBM * QBK];
   __shared__ int s_pref[kMaxE + 1];
-  __shared__ int s_wave[4];
+  __shared__ int s_wave[8];
   __shared__ int s_total;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // m-tiles per expert, prefix over experts (4 experts per thread, E <= 1024)
-  {
-    int c[4], tot = 0;
+  {  // 256-row m-tiles per expert and their prefix (2 experts per thread, E <= 1024)
+    int c[2], tot = 0;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = tid * 4 + q;
+    for (int q = 0; q < 2; ++q) {
+      const int e = tid * 2 + q;
       c[q] = 0;
-      if (e < p.E && active(p, e)) c[q] = (p.offsets[e + 1] - p.offsets[e] + GBM - 1) / GBM;
+      if (e < p.E && active(p, e)) c[q] = (p.offsets[e + 1] - p.offsets[e] + QBM - 1) / QBM;
       tot += c[q];
     }
     int x = tot;
@@ -337,14 +388,14 @@ __global__ __launch_bounds__(256, 2) void gemm_grouped(FfnArgs p, int n_ntiles) 
     __syncthreads();
     if (tid == 0) {
       int run = 0;
-      for (int w = 0; w < 4; ++w) { const int v = s_wave[w]; s_wave[w] = run; run += v; }
+      for (int w = 0; w < 8; ++w) { const int v = s_wave[w]; s_wave[w] = run; run += v; }
       s_total = run;
     }
     __syncthreads();
     int run = s_wave[wave] + x - tot;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = tid * 4 + q;
+    for (int q = 0; q < 2; ++q) {
+      const int e = tid * 2 + q;
       if (e < p.E) s_pref[e] = run;
       run += c[q];
     }
@@ -353,122 +404,140 @@ __global__ __launch_bounds__(256, 2) void gemm_grouped(FfnArgs p, int n_ntiles) 
   }
   const int total_items = s_total * n_ntiles;
   const int K = MODE == kGateUp ? p.d : p.f;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int cc = tid & 7, r0 = tid >> 3;  // loader: rows r0 + 32q, 16-byte chunk cc
+  const int nk = K / QBK;
+  const int G = gridDim.x, per_xcd = G >> 3;
+  const int pos = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);  // XCD-major dealing
+  const int g = lane >> 5, r32 = lane & 31;
+  const int wm = wave >> 2, wn = wave & 3;
+  // loader geometry: load instruction q (0..15) fills tile rows q*16 + lane/4, chunk lane&3
+  // of LDS, i.e. logical chunk lc of the source row; wave w issues q = 2w, 2w+1 for the
+  // token tile and for the weight tile
+  const int lrow = lane >> 2;
+  const int lc = (lane & 3) ^ ((lane >> 4) & 3);
 
-  for (int item = blockIdx.x; item < total_items; item += gridDim.x) {
-    const int q = item / n_ntiles;
+  for (int j = pos; j < total_items; j += G) {
+    const int q = j / n_ntiles;
     int lo = 0, hi = p.E;  // largest e with s_pref[e] <= q
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
       if (s_pref[mid] <= q) lo = mid; else hi = mid - 1;
     }
     const int e = lo;
-    const int mt_e = s_pref[e + 1] - s_pref[e];
-    const int local = item - s_pref[e] * n_ntiles;
-    const int nt = local / mt_e, mt = local - nt * mt_e;
+    const int m_e = s_pref[e + 1] - s_pref[e];
+    const int local = j - s_pref[e] * n_ntiles;
+    const int nt = local / m_e, mt = local - nt * m_e;
     const char* wbase = entry_of(p, e);
     if (!wbase) continue;
     const uint16_t* W = (const uint16_t*)wbase;
-    const int n0 = p.offsets[e] + mt * GBM;
-    const int rows = min(GBM, p.offsets[e + 1] - n0);
+    const int n0 = p.offsets[e] + mt * QBM;
+    const int rows = min(QBM, p.offsets[e + 1] - n0);
+    const int mtiles = (rows + 31) >> 5;
 
-    const uint16_t* srcA[4];
-    const uint16_t* srcB[4];
+    // per-lane source rows of this item (element offsets, + logical chunk)
+    const uint16_t* abase = MODE == kGateUp ? (const uint16_t*)p.x : (const uint16_t*)p.h;
+    uint32_t oa[2], ob[2];
 #pragma unroll
-    for (int qq = 0; qq < 4; ++qq) {
-      const int r = r0 + 32 * qq;
-      if (MODE == kGateUp) {
-        srcA[qq] = r < rows ? (const uint16_t*)p.x + (size_t)(p.perm[n0 + r] / p.k) * p.d + cc * 8 : nullptr;
-        const int unit = nt * 64 + (r & 63);
-        srcB[qq] = W + (r >= 64 ? (size_t)p.f * p.d : 0) + (size_t)unit * p.d + cc * 8;
+    for (int t = 0; t < 2; ++t) {
+      const int R = (2 * wave + t) * 16 + lrow;  // tile row 0..255
+      const int r = min(R, rows - 1);
+      oa[t] = (MODE == kGateUp ? (uint32_t)(p.perm[n0 + r] / p.k) * (uint32_t)p.d
+                               : (uint32_t)(n0 + r) * (uint32_t)p.f) + lc * 8;
+      if (MODE == kGateUp) {  // weight rows 64w'..64w'+31: gate units, +32..63: same up units
+        const int wq = R >> 6, rr = R & 63;
+        const int unit = nt * (QBN / 2) + wq * 32 + (rr & 31);
+        ob[t] = (uint32_t)((rr >> 5) * p.f + (unit < p.f ? unit : 0)) * (uint32_t)p.d + lc * 8;
       } else {
-        srcA[qq] = r < rows ? (const uint16_t*)p.h + (size_t)(n0 + r) * p.f + cc * 8 : nullptr;
-        const int o = nt * GBN + r;
-        srcB[qq] = o < p.d ? W + 2 * (size_t)p.f * p.d + (size_t)o * p.f + cc * 8 : nullptr;
+        const int o = nt * QBN + R;
+        ob[t] = (uint32_t)(2 * p.f * p.d) + (uint32_t)(o < p.d ? o : 0) * (uint32_t)p.f + lc * 8;
       }
     }
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    u32x4 ra[4], rb[4];
+    auto stage_ptr = [&](auto tag) -> uint16_t* {
+      constexpr int S = decltype(tag)::value;
+      return S == 0 ? sm0 : S == 1 ? sm1 : S == 2 ? sm2 : sm3;
+    };
+    auto issue = [&](auto tag, int ks) {
+      uint16_t* st = stage_ptr(tag);
+      const int kk = ks * QBK;
 #pragma unroll
-    for (int qq = 0; qq < 4; ++qq) {
-      ra[qq] = srcA[qq] ? ldg16(srcA[qq]) : zero;
-      rb[qq] = srcB[qq] ? ldg16(srcB[qq]) : zero;
-    }
-    f32x16 acc[2][2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+      for (int t = 0; t < 2; ++t) {
+        g2lds16(abase + oa[t] + kk, st + ((2 * wave + t) * 16) * QBK);
+        g2lds16(W + ob[t] + kk, st + QBM * QBK + ((2 * wave + t) * 16) * QBK);
+      }
+    };
 
-    __syncthreads();  // previous item's readers are done with buffer 0
+    f32x16 acc[4][2];
 #pragma unroll
-    for (int qq = 0; qq < 4; ++qq) {
-      *(u32x4*)&sA[0][swz(r0 + 32 * qq, cc)] = ra[qq];
-      *(u32x4*)&sB[0][swz(r0 + 32 * qq, cc)] = rb[qq];
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int jn = 0; jn < 2; ++jn)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][jn][v] = 0.f;
+
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    __syncthreads();  // the previous item's readers of the ring are done
+    issue(I0{}, 0);
+    if (nk > 1) issue(I1{}, 1);
+    if (nk > 2) issue(I2{}, 2);
+    // step ks on stage S = ks % 4: wait for this wave's part of the stage, publish it,
+    // refill the stage freed by step ks-1 with step ks+3, then 2 x 8 MFMAs
+    auto step = [&](auto tag, int ks) {
+      constexpr int S = decltype(tag)::value;
+      const int left = nk - 1 - ks;  // stages issued after this one
+      if (left >= 2) wait_vmcnt<8>();
+      else if (left == 1) wait_vmcnt<4>();
+      else wait_vmcnt<0>();
+      lds_barrier();
+      if (ks + 3 < nk) issue(std::integral_constant<int, (S + 3) & 3>{}, ks + 3);
+      const uint16_t* st = stage_ptr(tag);
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int ch = s * 2 + g;
+        bf16x8 bfr[2], af[4];
+#pragma unroll
+        for (int jn = 0; jn < 2; ++jn)
+          bfr[jn] = as_bf16x8(*(const u32x4*)&st[QBM * QBK + qswz(wn * 64 + jn * 32 + r32, ch)]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          af[i] = as_bf16x8(*(const u32x4*)&st[qswz(wm * 128 + i * 32 + r32, ch)]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[0], acc[i][0], 0, 0, 0);
+          acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[1], acc[i][1], 0, 0, 0);
+        }
+      }
+    };
+    for (int ks = 0; ks < nk; ks += 4) {
+      step(I0{}, ks);
+      if (ks + 1 < nk) step(I1{}, ks + 1);
+      if (ks + 2 < nk) step(I2{}, ks + 2);
+      if (ks + 3 < nk) step(I3{}, ks + 3);
     }
-    __syncthreads();
-    const int nk = K / GBK;
-    for (int ks = 0; ks < nk; ++ks) {
-      const int buf = ks & 1;
-      const bool more = ks + 1 < nk;
-      if (more) {
-        const int kn = (ks + 1) * GBK;
+
+    // epilogue: lane holds C[8*(v/4) + 4*g + v%4][r32] of each 32x32 tile
+    int ld = MODE == kGateUp ? p.f : p.d;
+    asm volatile("" : "+s"(ld));  // keep row-offset products inside the item loop
 #pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
-          ra[qq] = srcA[qq] ? ldg16(srcA[qq] + kn) : zero;
-          rb[qq] = srcB[qq] ? ldg16(srcB[qq] + kn) : zero;
-        }
-      }
-#pragma unroll
-      for (int s = 0; s < GBK / 16; ++s) {
-        const int ch = s * 2 + (lane >> 5);
-        bf16x8 af[2], bfr[2];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int r = wm * 64 + i * 32 + (lane & 31);
-          af[i] = as_bf16x8(*(const u32x4*)&sA[buf][swz(r, ch)]);
-        }
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int r = MODE == kGateUp ? j * 64 + wn * 32 + (lane & 31) : wn * 64 + j * 32 + (lane & 31);
-          bfr[j] = as_bf16x8(*(const u32x4*)&sB[buf][swz(r, ch)]);
-        }
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-      }
-      if (more) {
-#pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
-          *(u32x4*)&sA[buf ^ 1][swz(r0 + 32 * qq, cc)] = ra[qq];
-          *(u32x4*)&sB[buf ^ 1][swz(r0 + 32 * qq, cc)] = rb[qq];
-        }
-      }
-      __syncthreads();
-    }
-    // epilogue: lane holds C[8*(v/4) + 4*(lane/32) + v%4][lane%32] of each 32x32 tile
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < 4; ++i) {
+      if (wm * 4 + i >= mtiles) continue;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int m = wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        const int m = wm * 128 + i * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
         if (m >= rows) continue;
         if (MODE == kGateUp) {
-          const int unit = nt * 64 + wn * 32 + (lane & 31);
-          ((uint16_t*)p.h)[(size_t)(n0 + m) * p.f + unit] = f32_to_bf16(silu(acc[i][0][v]) * acc[i][1][v]);
+          const int unit = nt * (QBN / 2) + wn * 32 + r32;
+          if (unit < p.f)
+            ((uint16_t*)p.h)[(size_t)(n0 + m) * ld + unit] = f32_to_bf16(silu(acc[i][0][v]) * acc[i][1][v]);
         } else {
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const int o = nt * GBN + wn * 64 + j * 32 + (lane & 31);
+          for (int jn = 0; jn < 2; ++jn) {
+            const int o = nt * QBN + wn * 64 + jn * 32 + r32;
             if (o < p.d) {
-              const size_t idx = (size_t)(n0 + m) * p.d + o;
-              if (YDT == MOE_F32) ((float*)p.y)[idx] = acc[i][j][v];
-              else ((uint16_t*)p.y)[idx] = f32_to_bf16(acc[i][j][v]);
+              const size_t idx = (size_t)(n0 + m) * ld + o;
+              if (YDT == MOE_F32) ((float*)p.y)[idx] = acc[i][jn][v];
+              else ((uint16_t*)p.y)[idx] = f32_to_bf16(acc[i][jn][v]);
             }
           }
         }
@@ -557,14 +626,14 @@ extern "C" int moe_expert_ffn(const void* x, int act_dtype, const int32_t* perm,
     MOE_LAUNCH_CHECK();
     return MOE_OK;
   }
-  const dim3 grid(num_cus() * 2), blk(256);
-  hipLaunchKernelGGL((gemm_grouped<kGateUp, MOE_BF16>), grid, blk, 0, stream, p, f / 64);
+  const dim3 grid((num_cus() + 7) / 8 * 8), blk(512);
+  hipLaunchKernelGGL((gemm_tile256<kGateUp, MOE_BF16>), grid, blk, 0, stream, p, (f + QBN / 2 - 1) / (QBN / 2));
   MOE_LAUNCH_CHECK();
-  const int ntd = (d + GBN - 1) / GBN;
+  const int ntd = (d + QBN - 1) / QBN;
   if (y_dtype == MOE_F32)
-    hipLaunchKernelGGL((gemm_grouped<kDown, MOE_F32>), grid, blk, 0, stream, p, ntd);
+    hipLaunchKernelGGL((gemm_tile256<kDown, MOE_F32>), grid, blk, 0, stream, p, ntd);
   else
-    hipLaunchKernelGGL((gemm_grouped<kDown, MOE_BF16>), grid, blk, 0, stream, p, ntd);
+    hipLaunchKernelGGL((gemm_tile256<kDown, MOE_BF16>), grid, blk, 0, stream, p, ntd);
   MOE_LAUNCH_CHECK();
   return MOE_OK;
 }
