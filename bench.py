@@ -94,19 +94,26 @@ def bench_decode(args, torch, moe):
             layers[r].forward(x, logits[r], arena, w.entry_bytes, stream=s)
         s.synchronize()
         U = [int((layers[r].counts > 0).sum().item()) for r in range(R)]
-        for r in range(R):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=s):
-                layers[r].forward(x, logits[r], arena, w.entry_bytes, stream=s)
-            graphs.append(g)
+        if not args.no_graph:
+            for r in range(R):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=s):
+                    layers[r].forward(x, logits[r], arena, w.entry_bytes, stream=s)
+                graphs.append(g)
+
+        def run(i):
+            if args.no_graph:
+                layers[i % R].forward(x, logits[i % R], arena, w.entry_bytes, stream=s)
+            else:
+                graphs[i % R].replay()
         for i in range(args.warmup):
-            graphs[i % R].replay()
+            run(i)
         s.synchronize()
         e0, e1 = _events(torch, 2)
         torch.cuda.synchronize()
         e0.record(s)
         for i in range(args.steps):
-            graphs[i % R].replay()
+            run(i)
         e1.record(s)
         torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
@@ -220,7 +227,7 @@ def bench_lru(args, torch, moe):
     steps = args.lru_steps
     t0 = time.time()
     pool = host_pool(w)
-    log(f"[lru] pinned pool {pool.numel() * 2 / 1e9:.1f} GB in {time.time() - t0:.1f}s")
+    log(f"[lru] pinned pool {pool.nbytes / 1e9:.1f} GB in {time.time() - t0:.1f}s")
     _, lg = gen.markov_routing(w.seed, steps, w.L, w.T, w.E, w.k, w.p_stay, w.zipf_s)
     logits = torch.from_numpy(lg).cuda()
     xs = [torch.from_numpy(configs.gen_x(w, l).view(np.int16)).view(torch.bfloat16).cuda()
@@ -283,7 +290,8 @@ def bench_lru(args, torch, moe):
     st = stats.cpu().numpy()
     if int(status.item()) != 0 or int(lay.status.item()) != 0:
         raise RuntimeError(f"lru: status {int(status.item())} / {int(lay.status.item())}")
-    del pool, arena
+    pool.close()
+    del arena
     torch.cuda.empty_cache()
     return dict(workload=w.name, steps=steps, tok_s=steps * w.T / wall, wall_s=wall,
                 miss_rate=float(st[2] / st[0]), hits=int(st[1]), misses=int(st[2]),
@@ -299,7 +307,7 @@ def bench_stream(args, torch, moe):
     w = configs.STREAM_PREFILL
     t0 = time.time()
     pool = host_pool(w)
-    log(f"[stream] pinned pool {pool.numel() * 2 / 1e9:.2f} GB in {time.time() - t0:.1f}s")
+    log(f"[stream] pinned pool {pool.nbytes / 1e9:.2f} GB in {time.time() - t0:.1f}s")
     layer_bytes = w.E * w.entry_bytes
     bufs = [torch.empty((w.E, w.entry_elems), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
     xs = [torch.from_numpy(configs.gen_x(w, l).view(np.int16)).view(torch.bfloat16).cuda()
@@ -307,14 +315,14 @@ def bench_stream(args, torch, moe):
     lgs = [torch.from_numpy(configs.gen_logits(w, layer=l)).cuda() for l in range(w.L)]
     layers = [MoeLayer(w.T, w.E, w.k, w.d, w.f, y_dtype=moe.MOE_BF16) for _ in range(w.L)]
     comp, copy = torch.cuda.Stream(), torch.cuda.Stream()
-    # measured pinned H2D bandwidth (one layer block)
+    # measured pinned H2D bandwidth (one layer block through the same copy entry point)
     with torch.cuda.stream(copy):
         a, b = _events(torch, 2)
-        bufs[0].copy_(pool[:w.E], non_blocking=True)
+        moe.layer_stream_prefetch(pool.entry_ptr(0), bufs[0], layer_bytes, 1, copy, None, None)
         torch.cuda.synchronize()
         a.record(copy)
         for _ in range(3):
-            bufs[0].copy_(pool[:w.E], non_blocking=True)
+            moe.layer_stream_prefetch(pool.entry_ptr(0), bufs[0], layer_bytes, 1, copy, None, None)
         b.record(copy)
         torch.cuda.synchronize()
     h2d_gbs = 3 * layer_bytes / (a.elapsed_time(b) * 1e-3) / 1e9
@@ -329,14 +337,14 @@ def bench_stream(args, torch, moe):
         t_start = _events(torch, 1)[0]
         t_start.record(copy)
         pstart[0].record(copy)
-        moe.layer_stream_prefetch(pool[0].data_ptr(), bufs[0], layer_bytes, 1, copy, None, ready[0])
+        moe.layer_stream_prefetch(pool.entry_ptr(0), bufs[0], layer_bytes, 1, copy, None, ready[0])
         for l in range(w.L):
             if l + 1 < w.L:
                 nb = (l + 1) % 2
                 if l >= 1:
                     copy.wait_event(free[nb])  # compute of layer l-1 released this buffer
                 pstart[l + 1].record(copy)
-                moe.layer_stream_prefetch(pool[(l + 1) * w.E].data_ptr(), bufs[nb], layer_bytes,
+                moe.layer_stream_prefetch(pool.entry_ptr((l + 1) * w.E), bufs[nb], layer_bytes,
                                           1, copy, None, ready[l + 1])
             comp.wait_event(ready[l])
             cstart[l].record(comp)
@@ -357,12 +365,42 @@ def bench_stream(args, torch, moe):
     if status != 0:
         raise RuntimeError(f"stream: device status {status}")
     ideal_ms = w.L * layer_bytes / (h2d_gbs * 1e9) * 1e3
-    del pool, bufs
+    pool.close()
+    del bufs
     torch.cuda.empty_cache()
     return dict(workload=w.name, tok_s=w.T / (wall_ms * 1e-3), wall_ms=wall_ms,
                 h2d_gbs=h2d_gbs, ideal_ms=ideal_ms, efficiency=ideal_ms / wall_ms,
                 overlap=overlap, copy_ms_per_layer=float(np.mean([b - a for a, b in copies])),
                 compute_ms_per_layer=float(np.mean([b - a for a, b in comps])))
+
+
+# ------------------------------------------------------------------------ calibration probes
+def bench_probe(args, torch, moe):
+    """Achievable HBM read bandwidth (read probe) and a plain copy of known size (the
+    reference for scaling hardware byte counters: 1 GiB read + 1 GiB written per copy)."""
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    sink = torch.empty(4096, dtype=torch.int32, device="cuda")
+    s = torch.cuda.Stream()
+    reps = 10
+    with torch.cuda.stream(s):
+        moe.moe_hbm_read_probe(src, n, sink, s)
+        moe.moe_copy_probe(src, dst, n, s)
+        a, b, c = _events(torch, 3)
+        torch.cuda.synchronize()
+        a.record(s)
+        for _ in range(reps):
+            moe.moe_hbm_read_probe(src, n, sink, s)
+        b.record(s)
+        for _ in range(reps):
+            moe.moe_copy_probe(src, dst, n, s)
+        c.record(s)
+        torch.cuda.synchronize()
+    read_gbs = reps * n / (a.elapsed_time(b) * 1e-3) / 1e9
+    copy_gbs = reps * 2 * n / (b.elapsed_time(c) * 1e-3) / 1e9
+    return dict(bytes=n, read_gbs=read_gbs, copy_gbs=copy_gbs, read_frac=read_gbs / HBM_PEAK_GBS)
 
 
 # ------------------------------------------------------------------------ CPU baseline
@@ -398,7 +436,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="all", choices=["all", "decode", "prefill", "lru", "stream"])
+    ap.add_argument("--workload", default="all",
+                    choices=["all", "decode", "prefill", "lru", "stream", "probe"])
+    ap.add_argument("--no-graph", action="store_true", help="eager launches instead of graph replay")
     ap.add_argument("--decode-T", type=int, default=8)
     ap.add_argument("--alpha", type=float, default=0.2)
     ap.add_argument("--lru-steps", type=int, default=512)
@@ -428,6 +468,9 @@ def main():
     if wl in ("all", "stream"):
         extra["stream_prefill"] = bench_stream(args, torch, moe)
         log(f"[stream] {json.dumps(extra['stream_prefill'])}")
+    if wl in ("all", "probe"):
+        extra["hbm_probe"] = bench_probe(args, torch, moe)
+        log(f"[probe] {json.dumps(extra['hbm_probe'])}")
     if wl in ("all", "lru"):
         extra["lru_decode"] = bench_lru(args, torch, moe)
         log(f"[lru] {json.dumps(extra['lru_decode'])}")
@@ -445,7 +488,7 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": dec["workload"], "T": dec["T"], "E": 256, "k": 6, "d": 4096,
                    "f": 2048, "zipf_alpha": args.alpha, "experts_resident": 256,
-                   "graph_replay": True},
+                   "graph_replay": not args.no_graph},
         "roofline": dec["roofline"],
         "cpu_baseline": cpu,
         "extra": dict(decode_ffn_ms=dec["ffn_ms"], decode_unique_experts=dec["U_mean"],

@@ -10,16 +10,28 @@ namespace {
 
 constexpr int kProbeBlocks = 4096;
 
+// Each thread keeps 8 independent 16-byte loads in flight per iteration; full chunks are
+// loaded without per-load bounds checks so the loads issue back to back.
 __global__ __launch_bounds__(256) void hbm_read(const u32x4* __restrict__ src, size_t n16,
                                                 uint32_t* __restrict__ sink) {
   uint32_t acc = 0;
-  const size_t stride = (size_t)gridDim.x * 256 * 4;
-  for (size_t i = (size_t)blockIdx.x * 256 * 4 + threadIdx.x; i < n16; i += stride) {
-    u32x4 v[4];
+  const size_t chunk = (size_t)256 * 8;
+  const size_t stride = (size_t)gridDim.x * chunk;
+  for (size_t base = (size_t)blockIdx.x * chunk; base < n16; base += stride) {
+    const size_t i = base + threadIdx.x;
+    if (base + chunk <= n16) {
+      u32x4 v[8];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) v[q] = i + q * 256 < n16 ? src[i + q * 256] : u32x4{0u, 0u, 0u, 0u};
+      for (int q = 0; q < 8; ++q) v[q] = src[i + q * 256];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) acc ^= v[q][0] ^ v[q][1] ^ v[q][2] ^ v[q][3];
+      for (int q = 0; q < 8; ++q) acc ^= v[q][0] ^ v[q][1] ^ v[q][2] ^ v[q][3];
+    } else {
+      for (int q = 0; q < 8; ++q)
+        if (i + q * 256 < n16) {
+          const u32x4 v = src[i + q * 256];
+          acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+        }
+    }
   }
   for (int off = 32; off >= 1; off >>= 1) acc ^= __shfl_xor(acc, off);
   __shared__ uint32_t s[4];
@@ -40,7 +52,7 @@ extern "C" int moe_hbm_read_probe(const void* src, size_t bytes, uint32_t* sink,
   if (!src || !sink || bytes % 16 != 0 || !moe_aligned16(src)) return MOE_EINVAL;
   if (bytes == 0) return MOE_OK;
   const size_t n16 = bytes / 16;
-  const int blocks = (int)std::min<size_t>(kProbeBlocks, (n16 + 1023) / 1024);
+  const int blocks = (int)std::min<size_t>(kProbeBlocks, (n16 + 2047) / 2048);
   hipLaunchKernelGGL(hbm_read, dim3(blocks), dim3(256), 0, stream, (const u32x4*)src, n16, sink);
   MOE_LAUNCH_CHECK();
   return MOE_OK;

@@ -5,6 +5,8 @@ The entry layout is the library's documented one (include/moe_cache.h):
 (layer, expert).  This module only places generated values; it computes
 nothing of the layer.
 """
+import ctypes
+
 import numpy as np
 
 from . import TAG_WG, TAG_WU, TAG_WD, fill_segments_ptr
@@ -56,13 +58,53 @@ def device_arena_all_experts(w, layer=0):
     return arena
 
 
-def host_pool(w, pin=True):
-    """Pinned host pool [L*E, entry_elems], layer-major, every (layer, expert) entry."""
-    import torch
-    pool = torch.empty((w.L * w.E, w.entry_elems), dtype=torch_dtype(w), pin_memory=pin)
+class PinnedHostBuffer:
+    """Page-locked host memory of an exact size (hipHostMalloc; torch's pinned allocator
+    rounds large requests up to a power of two).  Freed with hipHostFree on close/GC."""
+
+    def __init__(self, nbytes):
+        import torch  # noqa: F401  (the HIP runtime is the one torch loaded)
+        self._hip = ctypes.CDLL("libamdhip64.so.7")
+        self._hip.hipHostMalloc.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_size_t,
+                                            ctypes.c_uint]
+        self._hip.hipHostFree.argtypes = [ctypes.c_void_p]
+        ptr = ctypes.c_void_p()
+        rc = self._hip.hipHostMalloc(ctypes.byref(ptr), int(nbytes), 0)
+        if rc != 0 or not ptr.value:
+            raise MemoryError(f"hipHostMalloc({nbytes}) failed with status {rc}")
+        self.ptr, self.nbytes = ptr.value, int(nbytes)
+
+    def data_ptr(self):
+        return self.ptr
+
+    def close(self):
+        if self.ptr:
+            self._hip.hipHostFree(ctypes.c_void_p(self.ptr))
+            self.ptr = 0
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class HostPool(PinnedHostBuffer):
+    """Pinned host pool of L*E entries, layer-major: entry (l, e) at l*E + e."""
+
+    def __init__(self, w):
+        super().__init__(w.L * w.E * w.entry_bytes)
+        self.w = w
+
+    def entry_ptr(self, i):
+        return self.ptr + i * self.w.entry_bytes
+
+
+def host_pool(w):
+    """Pinned host pool holding every (layer, expert) entry of workload w."""
+    pool = HostPool(w)
     step = 64
     pairs = [(l, e) for l in range(w.L) for e in range(w.E)]
     for c0 in range(0, len(pairs), step):
-        sub = pairs[c0:c0 + step]
-        fill_entries_ptr(w, sub, pool[c0].data_ptr(), w.entry_elems)
+        fill_entries_ptr(w, pairs[c0:c0 + step], pool.entry_ptr(c0), w.entry_elems)
     return pool
