@@ -316,27 +316,28 @@ __global__ __launch_bounds__(256) void gemv_down(FfnArgs p) {
 
 // ------------------------------------------------------------------ GEMM path
 // Tile: 256 grouped token rows x 256 weight rows per workgroup of 8 waves (two per SIMD,
-// so one wave's LDS-read latency is covered by the other's MFMAs), k in steps of 32.
-// Both operands go global -> LDS with direct loads (global_load_lds_dwordx4: lane i
-// lands at LDS base + 16 i) into a 4-stage ring of 32 KB stages
-// [256 token rows x 64 B | 256 weight rows x 64 B]: three k-steps of loads are in flight
-// while one is consumed, and no VGPR holds staging data.  Each wave's own counter
-// (s_waitcnt vmcnt) says when its part of a stage has landed; one LDS barrier per step
-// publishes the stage and frees the oldest one.
-// Wave (wm, wn) computes token rows wm*128 + [0,128) (four 32-row m-tiles) against weight
-// rows wn*64 + [0,64) (two 32-row n-tiles; for gate/up, 32 gate units and the same 32 up
-// units, so SiLU(g)*u is formed in registers) with v_mfma_f32_32x32x16_bf16.
-// Token rows are gathered through perm (gate/up) or read contiguously (down); rows past
-// the expert repeat a valid row and their outputs are not stored.  Workgroups are
-// persistent; the (expert, n-tile, m-tile) list is derived on the device from offsets
-// and dealt XCD-major so consecutive items (sharing weight rows or token rows) run at
-// the same time on one XCD's L2.
-constexpr int QBM = 256, QBN = 256, QBK = 32;
+// so one wave's LDS-read latency is covered by the other's MFMAs), k in steps of 64.
+// Both operands go global -> LDS with direct loads (global_load_lds_dwordx4: lane i lands
+// at LDS base + 16 i), one full 128-byte line per row per step, into a 2-stage ring of
+// 64 KB stages [256 token rows x 128 B | 256 weight rows x 128 B]: the next step's loads
+// are in flight while this step's MFMAs run, and no VGPR holds staging data.  A wave's own
+// counter (s_waitcnt vmcnt) says when its part of a stage has landed; one LDS-only barrier
+// per step publishes the stage and frees the other one.
+// Wave (wm, wn) computes token rows wm*128 + [0,128) (up to four 32-row m-tiles) against
+// weight rows wn*64 + [0,64) (two 32-row n-tiles; for gate/up, 32 gate units and the same
+// 32 up units, so SiLU(g)*u is formed in registers) with v_mfma_f32_32x32x16_bf16.  Only
+// m-tiles that hold expert rows are computed (the count is a compile-time parameter of the
+// k-loop, chosen per item, so the loop body stays branch-free).  Token rows are gathered
+// through perm (gate/up) or read contiguously (down); rows past the expert repeat a valid
+// row and their outputs are not stored.  Workgroups are persistent; the (expert, n-tile,
+// m-tile) list is derived on the device from offsets and dealt XCD-major so consecutive
+// items (sharing weight rows or token rows) run at the same time on one XCD's L2.
+constexpr int QBM = 256, QBN = 256, QBK = 64;
 constexpr int kGateUp = 0, kDown = 1;
 
 // Element index of 16-byte chunk c (0..3) of row r in a 64-byte-row tile; the XOR spreads
 // the 16 rows served by one ds_read_b128 cycle over all LDS banks.
-__device__ __forceinline__ int qswz(int r, int c) { return r * QBK + ((c ^ ((r >> 2) & 3)) << 3); }
+__device__ __forceinline__ int qswz(int r, int c) { return r * QBK + ((c ^ ((r >> 1) & 7)) << 3); }
 
 // 16 bytes per lane, global -> LDS (lane i lands at lds_wave_base + 16 i).  Issued from
 // inline assembly so the compiler does not drain every outstanding load before each LDS
@@ -362,8 +363,7 @@ void gemm_tile256(FfnArgs p, int n_ntiles) {
   // one array per ring stage: [token rows | weight rows], 32 KB each
   __shared__ __attribute__((aligned(1024))) uint16_t sm0[2 * QBM * QBK];
   __shared__ __attribute__((aligned(1024))) uint16_t sm1[2 * QBM * QBK];
-  __shared__ __attribute__((aligned(1024))) uint16_t sm2[2 * QBM * QBK];
-  __shared__ __attribute__((aligned(1024))) uint16_t sm3[2 * QBM * QBK];
+
   __shared__ int s_pref[kMaxE + 1];
   __shared__ int s_wave[8];
   __shared__ int s_total;
@@ -412,8 +412,7 @@ void gemm_tile256(FfnArgs p, int n_ntiles) {
   // loader geometry: load instruction q (0..15) fills tile rows q*16 + lane/4, chunk lane&3
   // of LDS, i.e. logical chunk lc of the source row; wave w issues q = 2w, 2w+1 for the
   // token tile and for the weight tile
-  const int lrow = lane >> 2;
-  const int lc = (lane & 3) ^ ((lane >> 4) & 3);
+  const int lrow = lane >> 3;  // 8 rows x 128 B per load instruction
 
   for (int j = pos; j < total_items; j += G) {
     const int q = j / n_ntiles;
@@ -435,10 +434,11 @@ void gemm_tile256(FfnArgs p, int n_ntiles) {
 
     // per-lane source rows of this item (element offsets, + logical chunk)
     const uint16_t* abase = MODE == kGateUp ? (const uint16_t*)p.x : (const uint16_t*)p.h;
-    uint32_t oa[2], ob[2];
+    uint32_t oa[4], ob[4];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int R = (2 * wave + t) * 16 + lrow;  // tile row 0..255
+    for (int t = 0; t < 4; ++t) {
+      const int R = (4 * wave + t) * 8 + lrow;  // tile row 0..255
+      const int lc = (lane & 7) ^ ((R >> 1) & 7);
       const int r = min(R, rows - 1);
       oa[t] = (MODE == kGateUp ? (uint32_t)(p.perm[n0 + r] / p.k) * (uint32_t)p.d
                                : (uint32_t)(n0 + r) * (uint32_t)p.f) + lc * 8;
@@ -453,16 +453,15 @@ void gemm_tile256(FfnArgs p, int n_ntiles) {
     }
     auto stage_ptr = [&](auto tag) -> uint16_t* {
       constexpr int S = decltype(tag)::value;
-      return S == 0 ? sm0 : S == 1 ? sm1 : S == 2 ? sm2 : sm3;
+      return S == 0 ? sm0 : sm1;
     };
     auto issue = [&](auto tag, int ks) {
       uint16_t* st = stage_ptr(tag);
       const int kk = ks * QBK;
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        g2lds16(abase + oa[t] + kk, st + ((2 * wave + t) * 16) * QBK);
-        g2lds16(W + ob[t] + kk, st + QBM * QBK + ((2 * wave + t) * 16) * QBK);
-      }
+      for (int t = 0; t < 4; ++t) g2lds16(abase + oa[t] + kk, st + ((4 * wave + t) * 8) * QBK);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) g2lds16(W + ob[t] + kk, st + QBM * QBK + ((4 * wave + t) * 8) * QBK);
     };
 
     f32x16 acc[4][2];
@@ -475,45 +474,49 @@ void gemm_tile256(FfnArgs p, int n_ntiles) {
 
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
-    using I2 = std::integral_constant<int, 2>;
-    using I3 = std::integral_constant<int, 3>;
     __syncthreads();  // the previous item's readers of the ring are done
     issue(I0{}, 0);
-    if (nk > 1) issue(I1{}, 1);
-    if (nk > 2) issue(I2{}, 2);
     // step ks on stage S = ks % 4: wait for this wave's part of the stage, publish it,
     // refill the stage freed by step ks-1 with step ks+3, then 2 x 8 MFMAs
-    auto step = [&](auto tag, int ks) {
+    auto step = [&](auto tag, auto am_tag, int ks) {
       constexpr int S = decltype(tag)::value;
-      const int left = nk - 1 - ks;  // stages issued after this one
-      if (left >= 2) wait_vmcnt<8>();
-      else if (left == 1) wait_vmcnt<4>();
-      else wait_vmcnt<0>();
-      lds_barrier();
-      if (ks + 3 < nk) issue(std::integral_constant<int, (S + 3) & 3>{}, ks + 3);
+      constexpr int AM = decltype(am_tag)::value;
+      wait_vmcnt<0>();  // this wave's part of stage ks has landed
+      lds_barrier();     // ... and every wave's; stage ks^1 is free again
+      if (ks + 1 < nk) issue(std::integral_constant<int, (S + 1) & 1>{}, ks + 1);
       const uint16_t* st = stage_ptr(tag);
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
+      for (int s = 0; s < 4; ++s) {
         const int ch = s * 2 + g;
         bf16x8 bfr[2], af[4];
 #pragma unroll
         for (int jn = 0; jn < 2; ++jn)
           bfr[jn] = as_bf16x8(*(const u32x4*)&st[QBM * QBK + qswz(wn * 64 + jn * 32 + r32, ch)]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < AM; ++i)
           af[i] = as_bf16x8(*(const u32x4*)&st[qswz(wm * 128 + i * 32 + r32, ch)]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < AM; ++i) {
           acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[0], acc[i][0], 0, 0, 0);
           acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[1], acc[i][1], 0, 0, 0);
         }
       }
     };
-    for (int ks = 0; ks < nk; ks += 4) {
-      step(I0{}, ks);
-      if (ks + 1 < nk) step(I1{}, ks + 1);
-      if (ks + 2 < nk) step(I2{}, ks + 2);
-      if (ks + 3 < nk) step(I3{}, ks + 3);
+    // only this wave's m-tiles that hold expert rows are computed (compile-time count,
+    // so the inner loop stays branch-free)
+    auto run_k = [&](auto am_tag) {
+      for (int ks = 0; ks < nk; ks += 2) {
+        step(I0{}, am_tag, ks);
+        if (ks + 1 < nk) step(I1{}, am_tag, ks + 1);
+      }
+    };
+    const int am = min(4, max(0, mtiles - wm * 4));
+    switch (am) {
+      case 0: run_k(std::integral_constant<int, 0>{}); break;
+      case 1: run_k(std::integral_constant<int, 1>{}); break;
+      case 2: run_k(std::integral_constant<int, 2>{}); break;
+      case 3: run_k(std::integral_constant<int, 3>{}); break;
+      default: run_k(std::integral_constant<int, 4>{}); break;
     }
 
     // epilogue: lane holds C[8*(v/4) + 4*g + v%4][r32] of each 32x32 tile
