@@ -56,13 +56,26 @@ def _ffn_flops(w):
     return 2.0 * w.T * w.k * 3 * w.d * w.f
 
 
-def _counter_traffic(kernel_src, name):
+CSRC = os.path.join(ROOT, "expert_ffn_cache_amd", "csrc")
+GEMV_SOURCES = [os.path.join(CSRC, n) for n in ("common.h", "ffn_args.h", "ffn_gemv.hip")]
+
+
+def sources_sha256(paths):
+    """sha256 over the concatenated bytes of the given kernel sources, in order."""
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def _counter_traffic(kernel_srcs, name):
     """HBM bytes per FFN call from the committed rocprofv3 counter summary, if it was taken
-    on the current kernel source (sha256 match); else None."""
+    on the current kernel sources (sha256 match); else None."""
     path = os.path.join(PROFILES, name)
     if not os.path.exists(path):
         return None
-    sha = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
+    sha = sources_sha256(kernel_srcs)
     vals = {}
     for line in open(path):
         if ":" in line and not line.lstrip().startswith("#"):
@@ -136,8 +149,7 @@ def bench_decode(args, torch, moe):
         raise RuntimeError(f"decode: device status {status}")
     ffn_avg_ms = float(np.mean(ffn_ms))
     achieved = float(np.sum(byts) / (np.sum(ffn_ms) * 1e-3) / 1e9)
-    traffic = _counter_traffic(os.path.join(ROOT, "expert_ffn_cache_amd", "csrc", "ffn.hip"),
-                               "ffn_gemv_decode_e256_k6_d4096_f2048_T8_counters.txt")
+    traffic = _counter_traffic(GEMV_SOURCES, "ffn_gemv_decode_e256_k6_d4096_f2048_T8_counters.txt")
     del graphs, arena
     torch.cuda.empty_cache()
     return dict(

@@ -1,0 +1,66 @@
+// Arguments and helpers shared by the expert FFN kernels (fp32, GEMV and GEMM paths).
+//
+// For every active expert e and its grouped rows p in [offsets[e], offsets[e+1]):
+//   h = SiLU(x[perm[p]/k] W_gate^T) * (x[perm[p]/k] W_up^T),   y_perm[p] = h W_down^T
+// with the weights of e read from the cache entry at arena + expert_slot[e] * stride,
+// laid out [W_gate f x d][W_up f x d][W_down d x f] (contraction index contiguous).
+#pragma once
+
+#include "common.h"
+
+namespace moe {
+
+struct FfnArgs {
+  const void* x;
+  const int32_t* perm;
+  const int32_t* offsets;
+  int k, E, d, f;
+  const int32_t* expert_slot;
+  const char* arena;
+  size_t stride;
+  const uint8_t* mask;
+  const int32_t* slot_key;
+  int key_base;
+  void* h;
+  void* y;
+  int32_t* status;
+};
+
+// Weights of expert e, or nullptr (and MOE_ERANGE) for a missing or stale slot.
+__device__ __forceinline__ const char* entry_of(const FfnArgs& p, int e) {
+  const int s = p.expert_slot ? p.expert_slot[e] : e;
+  if (s < 0 || (p.slot_key && p.slot_key[s] != p.key_base + e)) {
+    set_status(p.status, MOE_ERANGE);
+    return nullptr;
+  }
+  return p.arena + (size_t)s * p.stride;
+}
+
+__device__ __forceinline__ bool active(const FfnArgs& p, int e) {
+  return p.offsets[e + 1] > p.offsets[e] && (!p.mask || p.mask[e]);
+}
+
+// The a-th active expert in ascending id order, or -1; called by one full wave.
+__device__ __forceinline__ int nth_active_expert(const FfnArgs& p, int a) {
+  const int lane = threadIdx.x & 63;
+  int seen = 0;
+  for (int e0 = 0; e0 < p.E; e0 += 64) {
+    const int e = e0 + lane;
+    const bool act = e < p.E && active(p, e);
+    const unsigned long long m = __ballot(act);
+    const int c = __popcll(m);
+    if (a < seen + c) {
+      const bool mine = act && __popcll(m & lanemask_lt(lane)) == a - seen;
+      return e0 + __ffsll((long long)__ballot(mine)) - 1;
+    }
+    seen += c;
+  }
+  return -1;
+}
+
+
+// Launchers (argument checks are done by moe_expert_ffn).  Each returns MOE_OK or MOE_EHIP.
+int launch_ffn_gemv(const FfnArgs& p, int T, int y_dtype, hipStream_t stream);
+int launch_ffn_gemm(const FfnArgs& p, int y_dtype, hipStream_t stream);
+
+}  // namespace moe
