@@ -24,6 +24,8 @@ namespace {
 // row and their outputs are not stored.  Workgroups are persistent; the (expert, n-tile,
 // m-tile) list is derived on the device from offsets and dealt XCD-major so consecutive
 // items (sharing weight rows or token rows) run at the same time on one XCD's L2.
+// Inside a step, the fragments of the next 16-wide k substep are read from LDS while the
+// current substep's MFMAs run.
 constexpr int QBM = 256, QBN = 256, QBK = 64;
 constexpr int kGateUp = 0, kDown = 1;
 
@@ -31,15 +33,18 @@ constexpr int kGateUp = 0, kDown = 1;
 // the 16 rows served by one ds_read_b128 cycle over all LDS banks.
 __device__ __forceinline__ int qswz(int r, int c) { return r * QBK + ((c ^ ((r >> 1) & 7)) << 3); }
 
-// 16 bytes per lane, global -> LDS (lane i lands at lds_wave_base + 16 i).  Issued from
-// inline assembly so the compiler does not drain every outstanding load before each LDS
-// read (it cannot tell which stage a direct load writes); stage readiness is tracked
-// with explicit s_waitcnt vmcnt below.  Sets M0 itself (nothing else in these kernels
-// uses M0); has no output registers.
-__device__ __forceinline__ void g2lds16(const uint16_t* g, const uint16_t* lds_wave_base) {
-  const uint32_t l = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_wave_base;
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
-               :: "s"(__builtin_amdgcn_readfirstlane(l)), "v"(g) : "memory");
+// LDS byte address of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// 16 bytes per lane, global -> LDS (lane i lands at lds + 16 i; lds is wave-uniform).  Issued
+// from inline assembly so the compiler does not drain every outstanding load before each
+// LDS read (it cannot tell which stage a direct load writes); stage readiness is tracked
+// with explicit s_waitcnt vmcnt below.  Sets M0 itself (nothing else in these kernels uses
+// M0); has no output registers.
+__device__ __forceinline__ void g2lds16(const uint16_t* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" :: "s"(lds), "v"(g) : "memory");
 }
 
 template <int N>
@@ -60,7 +65,8 @@ void gemm_tile256(FfnArgs p, int n_ntiles) {
   __shared__ int s_wave[8];
   __shared__ int s_total;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS targets in SGPRs
   {  // 256-row m-tiles per expert and their prefix (2 experts per thread, E <= 1024)
     int c[2], tot = 0;
 #pragma unroll
@@ -104,7 +110,6 @@ void gemm_tile256(FfnArgs p, int n_ntiles) {
   // loader geometry: load instruction q (0..31) fills tile rows q*8 + lane/8, LDS chunk
   // lane&7, i.e. logical chunk lc of the source row; wave w issues q = 4w..4w+3 for the
   // token tile and for the weight tile
-  const int lrow = lane >> 3;  // 8 rows x 128 B per load instruction
 
   for (int j = pos; j < total_items; j += G) {
     const int q = j / n_ntiles;
@@ -127,10 +132,12 @@ void gemm_tile256(FfnArgs p, int n_ntiles) {
     // per-lane source rows of this item (element offsets, + logical chunk)
     const uint16_t* abase = MODE == kGateUp ? (const uint16_t*)p.x : (const uint16_t*)p.h;
     uint32_t oa[4], ob[4];
+    int ln = lane;
+    asm volatile("" : "+v"(ln));  // recomputed per item rather than held across the k-loop
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const int R = (4 * wave + t) * 8 + lrow;  // tile row 0..255
-      const int lc = (lane & 7) ^ ((R >> 1) & 7);
+      const int R = (4 * wave + t) * 8 + (ln >> 3);  // tile row 0..255
+      const int lc = (ln & 7) ^ ((R >> 1) & 7);
       const int r = min(R, rows - 1);
       oa[t] = (MODE == kGateUp ? (uint32_t)(p.perm[n0 + r] / p.k) * (uint32_t)p.d
                                : (uint32_t)(n0 + r) * (uint32_t)p.f) + lc * 8;
@@ -151,9 +158,10 @@ void gemm_tile256(FfnArgs p, int n_ntiles) {
       uint16_t* st = stage_ptr(tag);
       const int kk = ks * QBK;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) g2lds16(abase + oa[t] + kk, st + ((4 * wave + t) * 8) * QBK);
+      for (int t = 0; t < 4; ++t) g2lds16(abase + oa[t] + kk, lds_addr(st) + (4 * wave + t) * 8 * QBK * 2);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) g2lds16(W + ob[t] + kk, st + QBM * QBK + ((4 * wave + t) * 8) * QBK);
+      for (int t = 0; t < 4; ++t)
+        g2lds16(W + ob[t] + kk, lds_addr(st) + QBM * QBK * 2 + (4 * wave + t) * 8 * QBK * 2);
     };
 
     f32x16 acc[4][2];
@@ -178,21 +186,45 @@ void gemm_tile256(FfnArgs p, int n_ntiles) {
       lds_barrier();     // ... and every wave's; stage ks^1 is free again
       if (ks + 1 < nk) issue(std::integral_constant<int, (S + 1) & 1>{}, ks + 1);
       const uint16_t* st = stage_ptr(tag);
+      // fragments of substep s+1 are read while substep s's MFMAs run (two register sets)
+      bf16x8 bq[2][2], aq[2][4];
+#pragma unroll
+      for (int jn = 0; jn < 2; ++jn)
+        bq[0][jn] = as_bf16x8(*(const u32x4*)&st[QBM * QBK + qswz(wn * 64 + jn * 32 + r32, g)]);
+#pragma unroll
+      for (int i = 0; i < AM; ++i) aq[0][i] = as_bf16x8(*(const u32x4*)&st[qswz(wm * 128 + i * 32 + r32, g)]);
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const int ch = s * 2 + g;
-        bf16x8 bfr[2], af[4];
+        const int cur = s & 1, nxt = cur ^ 1;
+        if (s + 1 < 4) {
+          const int ch = (s + 1) * 2 + g;
 #pragma unroll
-        for (int jn = 0; jn < 2; ++jn)
-          bfr[jn] = as_bf16x8(*(const u32x4*)&st[QBM * QBK + qswz(wn * 64 + jn * 32 + r32, ch)]);
+          for (int jn = 0; jn < 2; ++jn)
+            bq[nxt][jn] = as_bf16x8(*(const u32x4*)&st[QBM * QBK + qswz(wn * 64 + jn * 32 + r32, ch)]);
 #pragma unroll
-        for (int i = 0; i < AM; ++i)
-          af[i] = as_bf16x8(*(const u32x4*)&st[qswz(wm * 128 + i * 32 + r32, ch)]);
+          for (int i = 0; i < AM; ++i)
+            aq[nxt][i] = as_bf16x8(*(const u32x4*)&st[qswz(wm * 128 + i * 32 + r32, ch)]);
+        }
 #pragma unroll
         for (int i = 0; i < AM; ++i) {
-          acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[0], acc[i][0], 0, 0, 0);
-          acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[1], acc[i][1], 0, 0, 0);
+          acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[cur][i], bq[cur][0], acc[i][0], 0, 0, 0);
+          acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[cur][i], bq[cur][1], acc[i][1], 0, 0, 0);
         }
+      }
+      // Pin that order for the scheduler (left alone it serialises each LDS read with the
+      // MFMA that consumes it): substep 0's reads, then each substep's MFMAs interleaved
+      // one-for-one with the next substep's reads (masks: 0x100 LDS read, 0x008 MFMA).
+      if constexpr (AM > 0) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 + AM, 0);
+#pragma unroll
+        for (int s = 0; s < 3; ++s) {
+#pragma unroll
+          for (int q = 0; q < 2 * AM || q < 2 + AM; ++q) {
+            if (q < 2 * AM) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (q < 2 + AM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * AM, 0);
       }
     };
     // only this wave's m-tiles that hold expert rows are computed (compile-time count,
