@@ -5,8 +5,8 @@ d=4096, f=2048, bf16 weights, T=8 tokens, all experts resident in HBM):
 route -> permute -> expert FFN (weight-streaming path) -> combine, replayed
 from captured HIP graphs over 16 pre-drawn routing sets.  value = tokens/s.
 
-Extra measurements in the same JSON line ("extra"): the T=8192 prefill
-layer (grouped-GEMM path), the 16-layer decode loop through the bounded LRU
+Extra measurements in the same JSON line ("extra"): the decode layer at
+T = 1 and 64 and at Zipf alpha 1, the T=8192 prefill layer (grouped-GEMM path), the 16-layer decode loop through the bounded LRU
 expert cache with PCIe miss fills, and the 8-layer prefill with full-layer
 double-buffered streaming.  All inputs are seeded synthetic tensors shaped
 like the FreeToken pages' models; weights are random.
@@ -87,16 +87,23 @@ def _counter_traffic(kernel_srcs, name):
 
 
 # ------------------------------------------------------------------------ decode layer
-def bench_decode(args, torch, moe):
+def decode_arena(torch):
+    """All 256 experts of the decode layer, resident (shared by every decode measurement)."""
     from gen import configs
     from gen.arena import device_arena_all_experts
+    t0 = time.time()
+    arena = device_arena_all_experts(configs.DECODE)
+    log(f"[decode] arena {configs.DECODE.E} x {configs.DECODE.entry_bytes / 1e6:.1f} MB generated "
+        f"in {time.time() - t0:.1f}s")
+    return arena
+
+
+def bench_decode(args, torch, moe, T, alpha, arena):
+    from gen import configs
     from expert_ffn_cache_amd.layer import MoeLayer
 
-    w = configs.with_(configs.DECODE, T=args.decode_T, alpha=args.alpha)
+    w = configs.with_(configs.DECODE, T=T, alpha=alpha)
     R = 16
-    t0 = time.time()
-    arena = device_arena_all_experts(w)
-    log(f"[decode] arena {w.E} x {w.entry_bytes / 1e6:.1f} MB generated in {time.time() - t0:.1f}s")
     x = torch.from_numpy(configs.gen_x(w).view(np.int16)).view(torch.bfloat16).cuda()
     logits = [torch.from_numpy(configs.gen_logits(w, rotation=r)).cuda() for r in range(R)]
     layers = [MoeLayer(w.T, w.E, w.k, w.d, w.f) for _ in range(R)]
@@ -149,8 +156,10 @@ def bench_decode(args, torch, moe):
         raise RuntimeError(f"decode: device status {status}")
     ffn_avg_ms = float(np.mean(ffn_ms))
     achieved = float(np.sum(byts) / (np.sum(ffn_ms) * 1e-3) / 1e9)
-    traffic = _counter_traffic(GEMV_SOURCES, "ffn_gemv_decode_e256_k6_d4096_f2048_T8_counters.txt")
-    del graphs, arena
+    traffic = None
+    if T == 8 and alpha == 0.2:  # the configuration the committed counter summary covers
+        traffic = _counter_traffic(GEMV_SOURCES, "ffn_gemv_decode_e256_k6_d4096_f2048_T8_counters.txt")
+    del graphs
     torch.cuda.empty_cache()
     return dict(
         workload=w.name, T=w.T, ms_per_step=ms, tok_s=w.T / (ms * 1e-3), U_mean=float(np.mean(U)),
@@ -454,6 +463,7 @@ def main():
     ap.add_argument("--lru-steps", type=int, default=512)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true", help="decode at the primary T and alpha only")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build has no "
@@ -468,10 +478,24 @@ def main():
     moe.lib()
     wl = args.workload
     extra = {}
-    dec = bench_decode(args, torch, moe) if wl in ("all", "decode") else None
-    if dec:
+    dec = None
+    if wl in ("all", "decode"):
+        arena = decode_arena(torch)
+        dec = bench_decode(args, torch, moe, args.decode_T, args.alpha, arena)
         log(f"[decode] {dec['tok_s']:.0f} tok/s, {dec['ms_per_step'] * 1e3:.1f} us/layer, "
             f"ffn {dec['ffn_ms'] * 1e3:.1f} us, {dec['roofline']['achieved']:.0f} GB/s")
+        if not args.no_sweep:
+            sweep = {}
+            for T, alpha in ((1, 0.2), (64, 0.2), (8, 1.0), (64, 1.0)):
+                r = bench_decode(args, torch, moe, T, alpha, arena)
+                sweep[f"T{T}_alpha{alpha}"] = dict(
+                    tok_s=r["tok_s"], us_per_layer=r["ms_per_step"] * 1e3, ffn_us=r["ffn_ms"] * 1e3,
+                    unique_experts=r["U_mean"], ffn_gbs=r["roofline"]["achieved"],
+                    hbm_frac=r["roofline"]["frac"])
+                log(f"[decode T={T} alpha={alpha}] {json.dumps(sweep[f'T{T}_alpha{alpha}'])}")
+            extra["decode_sweep"] = sweep
+        del arena
+        torch.cuda.empty_cache()
     if wl in ("all", "prefill"):
         extra["prefill"] = bench_prefill(args, torch, moe)
         log(f"[prefill] {json.dumps(extra['prefill'])}")
