@@ -311,10 +311,43 @@ def bench_lru(args, torch, moe):
     st = stats.cpu().numpy()
     if int(status.item()) != 0 or int(lay.status.item()) != 0:
         raise RuntimeError(f"lru: status {int(status.item())} / {int(lay.status.item())}")
+    out_host = lay.out.clone()
+
+    # the same loop with device-driven fills: one decode step (all layers, misses included)
+    # captured once as a graph and replayed per step; no host reads
+    lg_static = torch.empty((w.L, w.T, w.E), dtype=torch.float32, device="cuda")
+    with torch.cuda.stream(comp):
+        moe.cache_init(desc, comp)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=comp):
+            for l in range(w.L):
+                lay.route(lg_static[l], comp)
+                moe.cache_lookup_update(desc, l, lay.ids, w.T, w.k, expert_slot, fills_dev,
+                                        n_fills_dev, comp)
+                moe.cache_fill_device(desc, fills_dev, n_fills_dev, w.E, comp)
+                lay.permute(comp)
+                lay.ffn(xs[l], arena, w.entry_bytes, expert_slot, slot_key=key_of,
+                        key_base=l * w.E, stream=comp)
+                lay.combine(comp)
+        torch.cuda.synchronize()
+        t_start = time.time()
+        for s in range(steps):
+            lg_static.copy_(logits[s])
+            g.replay()
+        torch.cuda.synchronize()
+        wall_g = time.time() - t_start
+    st_g = stats.cpu().numpy()
+    if int(status.item()) != 0 or int(lay.status.item()) != 0:
+        raise RuntimeError(f"lru graph: status {int(status.item())} / {int(lay.status.item())}")
+    if not np.array_equal(st, st_g) or not torch.equal(out_host, lay.out):
+        raise RuntimeError("lru graph path disagrees with the host-driven path")
+    del g
     pool.close()
     del arena
     torch.cuda.empty_cache()
     return dict(workload=w.name, steps=steps, tok_s=steps * w.T / wall, wall_s=wall,
+                graph_device_fill_tok_s=steps * w.T / wall_g, graph_wall_s=wall_g,
                 miss_rate=float(st[2] / st[0]), hits=int(st[1]), misses=int(st[2]),
                 fill_gb=float(st[3] / 1e9), fill_gb_per_step=float(st[3] / 1e9 / steps))
 

@@ -33,7 +33,7 @@ EXPORTS = [
     "moe_strerror", "moe_abi_version", "moe_router_logits", "moe_route",
     "moe_permute_workspace_bytes", "moe_permute", "moe_expert_ffn_workspace_bytes",
     "moe_expert_ffn", "moe_combine", "cache_init", "cache_lookup_update", "cache_fill",
-    "layer_stream_prefetch", "moe_hbm_read_probe", "moe_copy_probe",
+    "cache_fill_device", "layer_stream_prefetch", "moe_hbm_read_probe", "moe_copy_probe",
 ]
 
 
@@ -85,6 +85,7 @@ def lib():
             "cache_lookup_update": ([ctypes.POINTER(moe_cache_t), i32, vp, i32, i32, vp, vp, vp,
                                      vp], i32),
             "cache_fill": ([ctypes.POINTER(moe_cache_t), vp, i32, vp], i32),
+            "cache_fill_device": ([ctypes.POINTER(moe_cache_t), vp, vp, i32, vp], i32),
             "layer_stream_prefetch": ([vp, vp, sz, i32, vp, vp, vp], i32),
             "moe_hbm_read_probe": ([vp, sz, vp, vp], i32),
             "moe_copy_probe": ([vp, vp, sz, vp], i32),
@@ -186,6 +187,11 @@ def cache_lookup_update(cache, layer, topk_ids, T, k, expert_slot, fills, n_fill
 def cache_fill(cache, fills_host, n_fills, copy_stream=None):
     _check("cache_fill", lib().cache_fill(ctypes.byref(cache), _p(fills_host), n_fills,
                                           _s(copy_stream)))
+
+
+def cache_fill_device(cache, fills, n_fills, max_fills, stream=None):
+    _check("cache_fill_device", lib().cache_fill_device(ctypes.byref(cache), _p(fills),
+                                                        _p(n_fills), max_fills, _s(stream)))
 
 
 def layer_stream_prefetch(host_src, dst, nbytes, n_chunks, copy_stream=None, wait_before=None,

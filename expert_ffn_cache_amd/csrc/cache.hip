@@ -9,7 +9,10 @@
 // page, runtime-tier table); prefill moves the next layer's experts while the
 // current layer computes (benchmark page, "How FreeToken serves large MoE
 // models"); control data stays on the device so routing-dependent decisions
-// remain graph-compatible (benchmark page, feature cards).
+// remain graph-compatible (benchmark page, feature cards).  Misses are filled either by
+// host-issued copies of the records read back after the lookup, or entirely on the device
+// by a copy kernel that reads the pinned pool over PCIe, so a decode step including its
+// misses can be captured and replayed as one graph.
 //
 // The lookup runs as one 1024-thread workgroup, entirely on device tables:
 //   requested-set flags in LDS -> |U| (barrier count) -> capacity check ->
@@ -147,6 +150,54 @@ __global__ __launch_bounds__(kCacheThreads) void lru_lookup_update(moe_cache_t c
   }
 }
 
+// Device-driven miss fills: the record count and the records are read on the device (as the
+// lookup left them), and each missed entry is copied from the pinned host pool, which the
+// GPU reads directly over PCIe, into its arena slot.  The grid is fixed, so the launch does
+// not depend on the count.  64 workgroups with 8 independent 16-byte loads per thread
+// (2 MB in flight) keep the host link saturated while leaving most CUs to other work.
+constexpr int kFillBlocks = 64, kFillThreads = 256, kFillUnroll = 8;
+
+__global__ __launch_bounds__(kFillThreads) void fill_from_pool(moe_cache_t c,
+                                                               const moe_fill_t* __restrict__ fills,
+                                                               const int32_t* __restrict__ n_fills,
+                                                               int max_fills) {
+  const int n = *n_fills;
+  if (n < 0 || n > max_fills) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) set_status(c.status, MOE_ERANGE);
+    return;
+  }
+  const size_t n16 = c.entry_bytes / 16;
+  constexpr size_t per_iter = (size_t)kFillThreads * kFillUnroll;
+  const size_t iters = (n16 + per_iter - 1) / per_iter;
+  const size_t total = (size_t)n * iters;
+  const u32x4* pool = (const u32x4*)c.host_pool;
+  u32x4* arena = (u32x4*)c.arena;
+  for (size_t w = blockIdx.x; w < total; w += gridDim.x) {
+    const int i = (int)(w / iters);
+    const size_t it = w - (size_t)i * iters;
+    const moe_fill_t f = fills[i];
+    if (f.slot < 0 || f.slot >= c.S || f.layer < 0 || f.layer >= c.L || f.expert < 0 ||
+        f.expert >= c.E) {
+      if (it == 0 && threadIdx.x == 0) set_status(c.status, MOE_ERANGE);
+      continue;
+    }
+    const u32x4* src = pool + ((size_t)f.layer * c.E + f.expert) * n16;
+    u32x4* dst = arena + (size_t)f.slot * n16;
+    const size_t base = it * per_iter + threadIdx.x;
+    u32x4 v[kFillUnroll];
+#pragma unroll
+    for (int q = 0; q < kFillUnroll; ++q) {
+      const size_t j = base + (size_t)q * kFillThreads;
+      if (j < n16) v[q] = src[j];
+    }
+#pragma unroll
+    for (int q = 0; q < kFillUnroll; ++q) {
+      const size_t j = base + (size_t)q * kFillThreads;
+      if (j < n16) dst[j] = v[q];
+    }
+  }
+}
+
 bool cache_ok(const moe_cache_t* c) {
   return c && c->L > 0 && c->E > 0 && c->E <= kMaxE && c->S > 0 && c->S <= kMaxSlots &&
          (long long)c->L * c->E < (1ll << 31) && c->entry_bytes > 0 && c->slot_of && c->key_of &&
@@ -207,6 +258,22 @@ extern "C" int cache_fill(const moe_cache_t* cache, const moe_fill_t* fills_host
                                  (size_t)run * eb, hipMemcpyHostToDevice, copy_stream));
     i += run;
   }
+  return MOE_OK;
+}
+
+extern "C" int cache_fill_device(const moe_cache_t* cache, const moe_fill_t* fills,
+                                 const int32_t* n_fills, int max_fills, hipStream_t stream) {
+  if (!cache || !cache->arena || !cache->host_pool || !cache->status || cache->S <= 0 ||
+      cache->L <= 0 || cache->E <= 0 || (long long)cache->L * cache->E >= (1ll << 31))
+    return MOE_EINVAL;
+  if (cache->entry_bytes == 0 || cache->entry_bytes % 16 != 0 || !moe_aligned16(cache->arena) ||
+      !moe_aligned16(cache->host_pool))
+    return MOE_EINVAL;
+  if (!fills || !n_fills || max_fills < 0) return MOE_EINVAL;
+  if (max_fills == 0) return MOE_OK;
+  hipLaunchKernelGGL(fill_from_pool, dim3(kFillBlocks), dim3(kFillThreads), 0, stream, *cache,
+                     fills, n_fills, max_fills);
+  MOE_LAUNCH_CHECK();
   return MOE_OK;
 }
 

@@ -36,7 +36,8 @@
  *    stream (not thread-safe on one descriptor).
  *  - Capture-safe (no host sync, no allocation, launch shape depends only on
  *    scalar arguments): every call except cache_fill, whose copy count is
- *    data-dependent and read on the host.
+ *    data-dependent and read on the host; cache_fill_device is its
+ *    capture-safe counterpart.
  *
  * Limits: 1 <= E <= 1024, 1 <= k <= min(E, 16), T >= 0 (T = 0 is a no-op),
  * T*k < 2^31, d and f positive multiples of 64.
@@ -214,6 +215,26 @@ int cache_lookup_update(const moe_cache_t* cache, int layer, const int32_t* topk
  * [0, S) x [0, L) x [0, E).  Not capture-safe (the count is host data). */
 int cache_fill(const moe_cache_t* cache, const moe_fill_t* fills_host, int n_fills,
                hipStream_t copy_stream);
+
+/* Device-driven miss fills, the graph-capturable form of cache_fill (benchmark
+ * page, feature cards: routing-dependent control data stays on the device so
+ * execution stays graph-compatible; runtime-tier table: the PCIe link moves
+ * selected experts into the GPU cache).  Reads *n_fills and fills[0 .. *n_fills)
+ * from device memory, as cache_lookup_update wrote them, and copies each entry
+ * (layer, expert) of cache->host_pool into arena slot `slot` with a kernel that
+ * reads the pool over PCIe.  The launch shape does not depend on the count, so
+ * lookup -> cache_fill_device -> FFN can be captured in one graph with no host
+ * synchronisation.
+ *   cache->host_pool: pinned host memory mapped for device access at its host
+ *   address (hipHostMalloc, or torch pin_memory); 16-byte aligned, as are the
+ *   arena and entry_bytes.
+ *   fills, n_fills: device memory; max_fills: capacity of fills (host int).
+ * Device errors (sticky, in cache->status): *n_fills outside [0, max_fills]
+ * sets MOE_ERANGE and copies nothing; a record outside [0, S) x [0, L) x [0, E)
+ * sets MOE_ERANGE and is skipped (the others are copied).  max_fills = 0 is a
+ * no-op.  Enqueued on `stream`; capture-safe. */
+int cache_fill_device(const moe_cache_t* cache, const moe_fill_t* fills, const int32_t* n_fills,
+                      int max_fills, hipStream_t stream);
 
 /* Full-layer streaming for prefill (llama page, "Official project overview";
  * benchmark page, "How FreeToken serves large MoE models"): waits on

@@ -79,6 +79,15 @@ def test_cache_host_validation():
     bad[1] = moe.moe_fill_t(1, 2, 1, -1)
     assert moe.lib().cache_fill(ctypes.byref(c), ctypes.addressof(bad), 2, None) == moe.MOE_ERANGE
     assert moe.lib().layer_stream_prefetch(None, None, 16, 1, None, None, None) == moe.MOE_EINVAL
+    # device-driven fills: aligned dummy addresses; max_fills = 0 returns before any launch
+    ok = moe.moe_cache_t(2, 4, 8, 0, 64, 4096, 4096, 4096, 4096, 4096, 4096, 4096, 4096)
+    fd = moe.lib().cache_fill_device
+    assert fd(ctypes.byref(ok), 4096, 4096, 0, None) == moe.MOE_OK
+    assert fd(ctypes.byref(ok), 4096, 4096, -1, None) == moe.MOE_EINVAL
+    assert fd(ctypes.byref(ok), None, 4096, 0, None) == moe.MOE_EINVAL
+    assert fd(ctypes.byref(c), 4096, 4096, 0, None) == moe.MOE_EINVAL  # unaligned arena
+    odd = moe.moe_cache_t(2, 4, 8, 0, 72, 4096, 4096, 4096, 4096, 4096, 4096, 4096, 4096)
+    assert fd(ctypes.byref(odd), 4096, 4096, 0, None) == moe.MOE_EINVAL  # entry_bytes % 16
 
 
 def test_python_binding_raises():

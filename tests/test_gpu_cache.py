@@ -172,3 +172,119 @@ def test_cache_fill_rejects_out_of_range_records():
     with pytest.raises(moe.MoeError) as ei:
         moe.cache_fill(dc.desc, ctypes.addressof(bad), 1)
     assert ei.value.status == moe.MOE_ERANGE
+
+
+def _small_lru_workload(seed):
+    # S >= T*k; 3 layers x ~11 unique ids per layer evict every step
+    return configs.Workload("lru_small", seed=seed, T=4, d=256, E=16, k=3, f=192, dtype=gen.BF16,
+                            L=3, S=14, alpha=0.5)
+
+
+def _pool_entry(pool, w, layer, e):
+    """Bytes of pool entry (layer, e) as uint16, read straight from the pinned buffer."""
+    n = w.entry_elems
+    buf = (ctypes.c_uint16 * n).from_address(pool.entry_ptr(layer * w.E + e))
+    return np.frombuffer(buf, dtype=np.uint16).copy()
+
+
+def test_device_fill_matches_host_fill_and_pool():
+    """Device-driven fills (records and count read on the GPU, pool read over PCIe) leave the
+    arena byte-identical to host-issued copies of the same records, and every filled slot
+    holds its pool entry."""
+    w = _small_lru_workload(33)
+    pool = host_pool(w)
+    arena_a = torch.zeros((w.S, w.entry_elems), dtype=torch.bfloat16, device="cuda")
+    arena_b = torch.zeros_like(arena_a)
+    dc = DevCache(w.L, w.E, w.S, w.entry_bytes, arena_a, pool)
+    desc_b = moe.moe_cache_t.from_buffer_copy(dc.desc)
+    desc_b.arena = arena_b.data_ptr()
+    steps = 5
+    ids, _ = gen.markov_routing(w.seed, steps, w.L, w.T, w.E, w.k, 0.5, 1.1)
+    ids_dev = dev(ids)
+    rec = (moe.moe_fill_t * w.E)()
+    filled = 0
+    for s in range(steps):
+        for layer in range(w.L):
+            dc.lookup(layer, ids_dev[s, layer], w.T, w.k)
+            moe.cache_fill_device(dc.desc, dc.fills, dc.n_fills, w.E)
+            f = dc.fills_host()
+            for i, (slot, l, e, old) in enumerate(f):
+                rec[i] = moe.moe_fill_t(slot, l, e, old)
+            moe.cache_fill(desc_b, ctypes.addressof(rec), len(f))
+            torch.cuda.synchronize()
+            assert torch.equal(arena_a.view(torch.int16), arena_b.view(torch.int16)), (s, layer)
+            for slot, l, e, _ in f:
+                got = arena_a[slot].view(torch.int16).cpu().numpy().view(np.uint16)
+                np.testing.assert_array_equal(got, _pool_entry(pool, w, l, e))
+            filled += len(f)
+    assert filled > steps * w.L  # evictions happened
+    assert int(dc.status.item()) == 0
+
+
+def test_decode_step_with_device_fills_replays_as_one_graph():
+    """route -> lookup -> device fill -> permute -> FFN through slots (key-checked) -> combine
+    for every layer, captured once and replayed over several steps with new routing written
+    into the captured input between replays: every layer's output equals the oracle and the
+    cache tables equal the sequential simulator's."""
+    w = _small_lru_workload(35)
+    pool = host_pool(w)
+    arena = torch.zeros((w.S, w.entry_elems), dtype=torch.bfloat16, device="cuda")
+    dc = DevCache(w.L, w.E, w.S, w.entry_bytes, arena, pool)
+    sim = LruSim(w.L, w.E, w.S)
+    layers = [MoeLayer(w.T, w.E, w.k, w.d, w.f) for _ in range(w.L)]
+    xs = [configs.gen_x(w, layer) for layer in range(w.L)]
+    xs_dev = [x_device(w, x) for x in xs]
+    tables = [oracle_table(w, range(w.E), layer) for layer in range(w.L)]
+    lg_buf = torch.zeros((w.L, w.T, w.E), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for layer, lay in enumerate(layers):
+            lay.route(lg_buf[layer])
+            dc.lookup(layer, lay.ids, w.T, w.k)
+            moe.cache_fill_device(dc.desc, dc.fills, dc.n_fills, w.E)
+            lay.permute()
+            lay.ffn(xs_dev[layer], arena, w.entry_bytes, dc.expert_slot, slot_key=dc.key_of,
+                    key_base=layer * w.E)
+            lay.combine()
+    for step in range(5):
+        lgs = [gen.routing_logits(w.seed, gen.TAG_LOGIT + layer * 0x10000 + step * 0x100, w.T,
+                                  w.E, w.k) for layer in range(w.L)]
+        lg_buf.copy_(torch.from_numpy(np.stack(lgs)))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for layer, lay in enumerate(layers):
+            ids, _, ref = oracle.moe_layer(xs[layer], lgs[layer], w.k, tables[layer])
+            np.testing.assert_array_equal(lay.ids.cpu().numpy(), ids)
+            assert_close(lay.out.cpu().numpy(), ref, bf16_tol(ref), f"step {step} layer {layer}")
+            sim.step(layer, ids.reshape(-1))
+        _compare_tables(dc, sim)
+        assert int(dc.status.item()) == 0
+        assert all(int(lay.status.item()) == 0 for lay in layers)
+
+
+def test_device_fill_error_records():
+    """A record outside the tables sets MOE_ERANGE and is skipped while the others are copied;
+    a count above max_fills sets MOE_ERANGE and copies nothing."""
+    w = configs.Workload("fill_err", seed=37, T=1, d=64, E=2, k=1, f=64, dtype=gen.BF16, L=2, S=2)
+    pool = host_pool(w)
+    arena = torch.zeros((w.S, w.entry_elems), dtype=torch.bfloat16, device="cuda")
+    dc = DevCache(w.L, w.E, w.S, w.entry_bytes, arena, pool)
+    dc.fills[0] = torch.tensor([w.S, 0, 0, -1], dtype=torch.int32)  # slot out of range
+    dc.fills[1] = torch.tensor([1, 1, 0, -1], dtype=torch.int32)    # good: (layer 1, expert 0)
+    dc.n_fills.fill_(2)
+    moe.cache_fill_device(dc.desc, dc.fills, dc.n_fills, 2)
+    torch.cuda.synchronize()
+    assert int(dc.status.item()) == moe.MOE_ERANGE
+    got = arena[1].view(torch.int16).cpu().numpy().view(np.uint16)
+    np.testing.assert_array_equal(got, _pool_entry(pool, w, 1, 0))
+    assert int(arena[0].view(torch.int16).abs().sum().item()) == 0
+    dc2 = DevCache(w.L, w.E, w.S, w.entry_bytes, torch.zeros_like(arena), pool)
+    dc2.fills[0] = torch.tensor([0, 0, 1, -1], dtype=torch.int32)
+    dc2.n_fills.fill_(2)
+    moe.cache_fill_device(dc2.desc, dc2.fills, dc2.n_fills, 1)
+    torch.cuda.synchronize()
+    assert int(dc2.status.item()) == moe.MOE_ERANGE
+    assert int(dc2.arena.view(torch.int16).abs().sum().item()) == 0
