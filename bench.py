@@ -314,40 +314,59 @@ def bench_lru(args, torch, moe):
     out_host = lay.out.clone()
 
     # the same loop with device-driven fills: one decode step (all layers, misses included)
-    # captured once as a graph and replayed per step; no host reads
+    # captured once as a graph and replayed per step; no host reads.  With overlap the graph
+    # forks after each lookup: the fill kernel runs on a side branch while the FFN of the
+    # hits runs, and the FFN of the misses follows the join.
     lg_static = torch.empty((w.L, w.T, w.E), dtype=torch.float32, device="cuda")
-    with torch.cuda.stream(comp):
-        moe.cache_init(desc, comp)
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=comp):
-            for l in range(w.L):
-                lay.route(lg_static[l], comp)
-                moe.cache_lookup_update(desc, l, lay.ids, w.T, w.k, expert_slot, fills_dev,
-                                        n_fills_dev, comp)
-                moe.cache_fill_device(desc, fills_dev, n_fills_dev, w.E, comp)
-                lay.permute(comp)
-                lay.ffn(xs[l], arena, w.entry_bytes, expert_slot, slot_key=key_of,
-                        key_base=l * w.E, stream=comp)
-                lay.combine(comp)
-        torch.cuda.synchronize()
-        t_start = time.time()
-        for s in range(steps):
-            lg_static.copy_(logits[s])
-            g.replay()
-        torch.cuda.synchronize()
-        wall_g = time.time() - t_start
-    st_g = stats.cpu().numpy()
-    if int(status.item()) != 0 or int(lay.status.item()) != 0:
-        raise RuntimeError(f"lru graph: status {int(status.item())} / {int(lay.status.item())}")
-    if not np.array_equal(st, st_g) or not torch.equal(out_host, lay.out):
-        raise RuntimeError("lru graph path disagrees with the host-driven path")
-    del g
+    side = torch.cuda.Stream()
+    walls = {}
+    for overlap in (False, True):
+        with torch.cuda.stream(comp):
+            moe.cache_init(desc, comp)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=comp):
+                for l in range(w.L):
+                    lay.route(lg_static[l], comp)
+                    moe.cache_lookup_update(desc, l, lay.ids, w.T, w.k, expert_slot, fills_dev,
+                                            n_fills_dev, comp)
+                    key = dict(slot_key=key_of, key_base=l * w.E, stream=comp)
+                    if overlap:
+                        hit, miss = masks_dev[l, 0], masks_dev[l, 1]
+                        moe.cache_fill_masks(expert_slot, fills_dev, n_fills_dev, w.E, hit, miss,
+                                             status, comp)
+                        side.wait_stream(comp)
+                        moe.cache_fill_device(desc, fills_dev, n_fills_dev, w.E, side)
+                        lay.permute(comp)
+                        lay.ffn(xs[l], arena, w.entry_bytes, expert_slot, mask=hit, **key)
+                        comp.wait_stream(side)
+                        lay.ffn(xs[l], arena, w.entry_bytes, expert_slot, mask=miss, **key)
+                    else:
+                        moe.cache_fill_device(desc, fills_dev, n_fills_dev, w.E, comp)
+                        lay.permute(comp)
+                        lay.ffn(xs[l], arena, w.entry_bytes, expert_slot, **key)
+                    lay.combine(comp)
+            torch.cuda.synchronize()
+            t_start = time.time()
+            for s in range(steps):
+                lg_static.copy_(logits[s])
+                g.replay()
+            torch.cuda.synchronize()
+            walls[overlap] = time.time() - t_start
+        st_g = stats.cpu().numpy()
+        if int(status.item()) != 0 or int(lay.status.item()) != 0:
+            raise RuntimeError(f"lru graph: status {int(status.item())} / {int(lay.status.item())}")
+        if not np.array_equal(st, st_g) or not torch.equal(out_host, lay.out):
+            raise RuntimeError("lru graph path disagrees with the host-driven path")
+        del g
+    wall_g = walls[False]
     pool.close()
     del arena
     torch.cuda.empty_cache()
     return dict(workload=w.name, steps=steps, tok_s=steps * w.T / wall, wall_s=wall,
                 graph_device_fill_tok_s=steps * w.T / wall_g, graph_wall_s=wall_g,
+                graph_overlap_tok_s=steps * w.T / walls[True], graph_overlap_wall_s=walls[True],
+                graph_overlap_fill_gbs=float(st[3]) / walls[True] / 1e9,
                 miss_rate=float(st[2] / st[0]), hits=int(st[1]), misses=int(st[2]),
                 fill_gb=float(st[3] / 1e9), fill_gb_per_step=float(st[3] / 1e9 / steps))
 

@@ -33,7 +33,7 @@ EXPORTS = [
     "moe_strerror", "moe_abi_version", "moe_router_logits", "moe_route",
     "moe_permute_workspace_bytes", "moe_permute", "moe_expert_ffn_workspace_bytes",
     "moe_expert_ffn", "moe_combine", "cache_init", "cache_lookup_update", "cache_fill",
-    "cache_fill_device", "layer_stream_prefetch", "moe_hbm_read_probe", "moe_copy_probe",
+    "cache_fill_device", "cache_fill_masks", "layer_stream_prefetch", "moe_hbm_read_probe", "moe_copy_probe",
 ]
 
 
@@ -86,6 +86,7 @@ def lib():
                                      vp], i32),
             "cache_fill": ([ctypes.POINTER(moe_cache_t), vp, i32, vp], i32),
             "cache_fill_device": ([ctypes.POINTER(moe_cache_t), vp, vp, i32, vp], i32),
+            "cache_fill_masks": ([vp, vp, vp, i32, vp, vp, vp, vp], i32),
             "layer_stream_prefetch": ([vp, vp, sz, i32, vp, vp, vp], i32),
             "moe_hbm_read_probe": ([vp, sz, vp, vp], i32),
             "moe_copy_probe": ([vp, vp, sz, vp], i32),
@@ -192,6 +193,13 @@ def cache_fill(cache, fills_host, n_fills, copy_stream=None):
 def cache_fill_device(cache, fills, n_fills, max_fills, stream=None):
     _check("cache_fill_device", lib().cache_fill_device(ctypes.byref(cache), _p(fills),
                                                         _p(n_fills), max_fills, _s(stream)))
+
+
+def cache_fill_masks(expert_slot, fills, n_fills, E, hit_mask, miss_mask, status=None,
+                     stream=None):
+    _check("cache_fill_masks", lib().cache_fill_masks(
+        _p(expert_slot), _p(fills), _p(n_fills), E, _p(hit_mask), _p(miss_mask), _p(status),
+        _s(stream)))
 
 
 def layer_stream_prefetch(host_src, dst, nbytes, n_chunks, copy_stream=None, wait_before=None,

@@ -198,6 +198,37 @@ __global__ __launch_bounds__(kFillThreads) void fill_from_pool(moe_cache_t c,
   }
 }
 
+// Hit / miss masks of the last lookup: requested experts (expert_slot >= 0) split by whether
+// a fill record names them.  One workgroup; E <= 1024.
+__global__ __launch_bounds__(kMaxE) void fill_masks_kernel(const int32_t* __restrict__ expert_slot,
+                                                           const moe_fill_t* __restrict__ fills,
+                                                           const int32_t* __restrict__ n_fills, int E,
+                                                           uint8_t* __restrict__ hit_mask,
+                                                           uint8_t* __restrict__ miss_mask,
+                                                           int32_t* __restrict__ status) {
+  __shared__ uint8_t missed[kMaxE];
+  const int tid = threadIdx.x;
+  if (tid < E) missed[tid] = 0;
+  __syncthreads();
+  const int n = *n_fills;
+  if (n < 0 || n > E) {
+    if (tid == 0) set_status(status, MOE_ERANGE);
+    if (tid < E) hit_mask[tid] = miss_mask[tid] = 0;
+    return;
+  }
+  if (tid < n) {
+    const int e = fills[tid].expert;
+    if (e >= 0 && e < E) missed[e] = 1;
+    else set_status(status, MOE_ERANGE);
+  }
+  __syncthreads();
+  if (tid < E) {
+    const bool req = expert_slot[tid] >= 0;
+    hit_mask[tid] = req && !missed[tid];
+    miss_mask[tid] = req && missed[tid];
+  }
+}
+
 bool cache_ok(const moe_cache_t* c) {
   return c && c->L > 0 && c->E > 0 && c->E <= kMaxE && c->S > 0 && c->S <= kMaxSlots &&
          (long long)c->L * c->E < (1ll << 31) && c->entry_bytes > 0 && c->slot_of && c->key_of &&
@@ -273,6 +304,17 @@ extern "C" int cache_fill_device(const moe_cache_t* cache, const moe_fill_t* fil
   if (max_fills == 0) return MOE_OK;
   hipLaunchKernelGGL(fill_from_pool, dim3(kFillBlocks), dim3(kFillThreads), 0, stream, *cache,
                      fills, n_fills, max_fills);
+  MOE_LAUNCH_CHECK();
+  return MOE_OK;
+}
+
+extern "C" int cache_fill_masks(const int32_t* expert_slot, const moe_fill_t* fills,
+                                const int32_t* n_fills, int E, uint8_t* hit_mask,
+                                uint8_t* miss_mask, int32_t* status, hipStream_t stream) {
+  if (E <= 0 || E > kMaxE) return MOE_EINVAL;
+  if (!expert_slot || !fills || !n_fills || !hit_mask || !miss_mask) return MOE_EINVAL;
+  hipLaunchKernelGGL(fill_masks_kernel, dim3(1), dim3(kMaxE), 0, stream, expert_slot, fills,
+                     n_fills, E, hit_mask, miss_mask, status);
   MOE_LAUNCH_CHECK();
   return MOE_OK;
 }

@@ -236,6 +236,23 @@ int cache_fill(const moe_cache_t* cache, const moe_fill_t* fills_host, int n_fil
 int cache_fill_device(const moe_cache_t* cache, const moe_fill_t* fills, const int32_t* n_fills,
                       int max_fills, hipStream_t stream);
 
+/* Hit and miss masks of the last lookup, so the FFN of resident experts can run
+ * while the misses are being copied in (RTX-4090 page, "How the MoE memory
+ * hierarchy works": hits run from VRAM; benchmark page, runtime-tier table:
+ * misses move over PCIe).  With n = *n_fills:
+ *   miss_mask[e] = 1 if expert_slot[e] >= 0 and some fills[i < n].expert == e,
+ *   hit_mask[e]  = 1 if expert_slot[e] >= 0 and no record names e, else 0.
+ * expert_slot, fills, n_fills as written by cache_lookup_update; masks are
+ * device arrays of E bytes, usable as moe_expert_ffn's expert_mask.  Hits and
+ * misses use disjoint slots, so moe_expert_ffn(hit_mask) may run concurrently
+ * with cache_fill / cache_fill_device, and moe_expert_ffn(miss_mask) after the
+ * fill.  Device errors (status nullable, sticky): n outside [0, E] (masks all 0)
+ * or a record's expert outside [0, E) set MOE_ERANGE.  1 <= E <= 1024.
+ * Capture-safe. */
+int cache_fill_masks(const int32_t* expert_slot, const moe_fill_t* fills, const int32_t* n_fills,
+                     int E, uint8_t* hit_mask, uint8_t* miss_mask, int32_t* status,
+                     hipStream_t stream);
+
 /* Full-layer streaming for prefill (llama page, "Official project overview";
  * benchmark page, "How FreeToken serves large MoE models"): waits on
  * wait_before (nullable; the event that marks the end of the last compute

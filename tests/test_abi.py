@@ -88,6 +88,10 @@ def test_cache_host_validation():
     assert fd(ctypes.byref(c), 4096, 4096, 0, None) == moe.MOE_EINVAL  # unaligned arena
     odd = moe.moe_cache_t(2, 4, 8, 0, 72, 4096, 4096, 4096, 4096, 4096, 4096, 4096, 4096)
     assert fd(ctypes.byref(odd), 4096, 4096, 0, None) == moe.MOE_EINVAL  # entry_bytes % 16
+    fm = moe.lib().cache_fill_masks
+    assert fm(4096, 4096, 4096, 0, 4096, 4096, None, None) == moe.MOE_EINVAL     # E = 0
+    assert fm(4096, 4096, 4096, 1025, 4096, 4096, None, None) == moe.MOE_EINVAL  # E > 1024
+    assert fm(4096, None, 4096, 8, 4096, 4096, None, None) == moe.MOE_EINVAL
 
 
 def test_python_binding_raises():

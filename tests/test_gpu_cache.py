@@ -221,11 +221,14 @@ def test_device_fill_matches_host_fill_and_pool():
     assert int(dc.status.item()) == 0
 
 
-def test_decode_step_with_device_fills_replays_as_one_graph():
+@pytest.mark.parametrize("overlap", [False, True])
+def test_decode_step_with_device_fills_replays_as_one_graph(overlap):
     """route -> lookup -> device fill -> permute -> FFN through slots (key-checked) -> combine
     for every layer, captured once and replayed over several steps with new routing written
     into the captured input between replays: every layer's output equals the oracle and the
-    cache tables equal the sequential simulator's."""
+    cache tables equal the sequential simulator's.  With overlap, the graph forks after the
+    lookup: the fill runs on a side branch while the FFN of the hits runs, and the FFN of
+    the misses follows the join."""
     w = _small_lru_workload(35)
     pool = host_pool(w)
     arena = torch.zeros((w.S, w.entry_elems), dtype=torch.bfloat16, device="cuda")
@@ -239,14 +242,27 @@ def test_decode_step_with_device_fills_replays_as_one_graph():
     torch.cuda.synchronize()
     s = torch.cuda.Stream()
     g = torch.cuda.CUDAGraph()
+    masks = torch.zeros((w.L, 2, w.E), dtype=torch.uint8, device="cuda")
+    side = torch.cuda.Stream()
     with torch.cuda.graph(g, stream=s):
         for layer, lay in enumerate(layers):
             lay.route(lg_buf[layer])
             dc.lookup(layer, lay.ids, w.T, w.k)
-            moe.cache_fill_device(dc.desc, dc.fills, dc.n_fills, w.E)
-            lay.permute()
-            lay.ffn(xs_dev[layer], arena, w.entry_bytes, dc.expert_slot, slot_key=dc.key_of,
-                    key_base=layer * w.E)
+            key = dict(slot_key=dc.key_of, key_base=layer * w.E)
+            if overlap:
+                hit, miss = masks[layer, 0], masks[layer, 1]
+                moe.cache_fill_masks(dc.expert_slot, dc.fills, dc.n_fills, w.E, hit, miss,
+                                     dc.status)
+                side.wait_stream(s)
+                moe.cache_fill_device(dc.desc, dc.fills, dc.n_fills, w.E, side)
+                lay.permute()
+                lay.ffn(xs_dev[layer], arena, w.entry_bytes, dc.expert_slot, mask=hit, **key)
+                s.wait_stream(side)
+                lay.ffn(xs_dev[layer], arena, w.entry_bytes, dc.expert_slot, mask=miss, **key)
+            else:
+                moe.cache_fill_device(dc.desc, dc.fills, dc.n_fills, w.E)
+                lay.permute()
+                lay.ffn(xs_dev[layer], arena, w.entry_bytes, dc.expert_slot, **key)
             lay.combine()
     for step in range(5):
         lgs = [gen.routing_logits(w.seed, gen.TAG_LOGIT + layer * 0x10000 + step * 0x100, w.T,
@@ -288,3 +304,35 @@ def test_device_fill_error_records():
     torch.cuda.synchronize()
     assert int(dc2.status.item()) == moe.MOE_ERANGE
     assert int(dc2.arena.view(torch.int16).abs().sum().item()) == 0
+
+
+def test_fill_masks_split_requested_experts():
+    """hit_mask / miss_mask after each lookup equal the split of the requested experts by the
+    fill records, and together cover exactly the requested set."""
+    w = configs.with_(_small_lru_workload(39), L=2, S=20)  # room for reuse: hits and misses
+    dc = DevCache(w.L, w.E, w.S, w.entry_bytes)
+    steps = 6
+    ids, _ = gen.markov_routing(w.seed, steps, w.L, w.T, w.E, w.k, 0.5, 1.1)
+    ids_dev = dev(ids)
+    hit = torch.empty(w.E, dtype=torch.uint8, device="cuda")
+    miss = torch.empty_like(hit)
+    saw_hit = saw_miss = False
+    for s in range(steps):
+        for layer in range(w.L):
+            dc.lookup(layer, ids_dev[s, layer], w.T, w.k)
+            moe.cache_fill_masks(dc.expert_slot, dc.fills, dc.n_fills, w.E, hit, miss, dc.status)
+            filled = {e for _, _, e, _ in dc.fills_host()}
+            req = set(int(e) for e in ids[s, layer].ravel())
+            want_miss = np.array([e in filled for e in range(w.E)], dtype=np.uint8)
+            want_hit = np.array([e in req and e not in filled for e in range(w.E)], dtype=np.uint8)
+            np.testing.assert_array_equal(miss.cpu().numpy(), want_miss)
+            np.testing.assert_array_equal(hit.cpu().numpy(), want_hit)
+            saw_hit |= bool(want_hit.any())
+            saw_miss |= bool(want_miss.any())
+    assert saw_hit and saw_miss
+    assert int(dc.status.item()) == 0
+    dc.n_fills.fill_(w.E + 1)
+    moe.cache_fill_masks(dc.expert_slot, dc.fills, dc.n_fills, w.E, hit, miss, dc.status)
+    torch.cuda.synchronize()
+    assert int(dc.status.item()) == moe.MOE_ERANGE
+    assert int(hit.sum().item()) == 0 and int(miss.sum().item()) == 0
