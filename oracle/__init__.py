@@ -12,7 +12,7 @@ import os
 import numpy as np
 
 from . import _build
-from .lru_sim import LruSim, CapacityError, StaticPlacement  # noqa: F401
+from .lru_sim import LruSim, CapacityError, StaticPlacement, qstar  # noqa: F401
 
 _lib = None
 

@@ -10,7 +10,8 @@ large MoE models"; RTX-4090 page, "How the MoE memory hierarchy works").  Cache
 entries are whole (layer, expert) pairs under one logical mapping (RTX-4090
 page, same section).  Misses are filled from the host-resident pool
 (benchmark page, runtime-tier table; all misses are filled here since the
-CPU-execution half of the miss split is out of scope).
+CPU-execution half of the miss split is out of scope; step_split decides only which
+misses are filled and which are left to the host).
 
 The pages give no tie rules.  Reading taken (one call per (step, layer)):
   t = ++clock
@@ -27,6 +28,30 @@ The pages give no tie rules.  Reading taken (one call per (step, layer)):
 import numpy as np
 
 
+def qstar(m, pcie_mbps, host_mbps):
+    """How many of m missed entries to fill over PCIe when the others run on the host.
+
+    FreeToken pages: the runtime profiles host-side expert throughput and pinned PCIe
+    bandwidth and uses the two measurements to decide how many misses move to the GPU and
+    how many execute on the CPU, so both links work at once (benchmark page, "How FreeToken
+    serves large MoE models", where the q-star policy is named, its runtime-tier table and
+    the "adaptive cache miss" feature card; RTX-4090 page, "Setup and tuning workflow",
+    step "Measure the system").  The pages give no formula.  Reading:
+    the two paths run concurrently, so the step waits for the slower one; q* minimises
+    max(q * B / P, (m - q) * B / H) over q = 0..m (B = entry bytes), ties to the larger q
+    (more fills keep the cache warm).  Compared as max(q * H, (m - q) * P) in integers
+    (bandwidths in MB/s), so no rounding decides the count.
+    """
+    if pcie_mbps < 0 or host_mbps < 0 or pcie_mbps + host_mbps == 0:
+        raise ValueError("bandwidths must be >= 0 and not both 0")
+    best_q, best_t = 0, None
+    for q in range(m + 1):
+        t = max(q * host_mbps, (m - q) * pcie_mbps)
+        if best_t is None or t <= best_t:
+            best_q, best_t = q, t
+    return best_q
+
+
 class LruSim:
     def __init__(self, L, E, S):
         self.L, self.E, self.S = L, E, S
@@ -35,6 +60,7 @@ class LruSim:
         self.stamp = np.zeros(S, dtype=np.int64)
         self.clock = 0
         self.accesses = self.hits = self.misses = 0
+        self.host_runs = 0  # misses left to the host by step_split
 
     def step(self, layer, ids):
         """One lookup/update for `layer` with requested expert ids (any shape).
@@ -42,6 +68,16 @@ class LruSim:
         Returns (expert_slot[E] with -1 for unrequested experts, fills list of
         (slot, layer, expert, evicted_key)), or raises CapacityError.
         """
+        expert_slot, fills, _ = self._step(layer, ids, None)
+        return expert_slot, fills
+
+    def step_split(self, layer, ids, pcie_mbps, host_mbps):
+        """As step, with the misses split by qstar: the first q* misses (ascending id) are
+        filled as in step; the rest run on the host, so they take no slot, are not inserted
+        and keep expert_slot -1.  Returns (expert_slot, fills, host_experts)."""
+        return self._step(layer, ids, (pcie_mbps, host_mbps))
+
+    def _step(self, layer, ids, split):
         U = sorted(set(int(e) for e in np.asarray(ids).ravel()))
         if len(U) > self.S:
             raise CapacityError(len(U), self.S)
@@ -56,10 +92,12 @@ class LruSim:
                 expert_slot[e] = s
             else:
                 misses.append(e)
+        n_fill = len(misses) if split is None else qstar(len(misses), *split)
+        to_host = misses[n_fill:]
         free = np.nonzero(self.stamp < t)[0]
         cand = free[np.lexsort((free, self.stamp[free]))]  # by (stamp, slot)
         fills = []
-        for i, e in enumerate(misses):
+        for i, e in enumerate(misses[:n_fill]):
             s = int(cand[i])
             old = int(self.key_of[s])
             if old >= 0:
@@ -73,7 +111,8 @@ class LruSim:
         self.accesses += len(U)
         self.hits += len(U) - len(misses)
         self.misses += len(misses)
-        return expert_slot, fills
+        self.host_runs += len(to_host)
+        return expert_slot, fills, to_host
 
     def resident_keys(self):
         return set(int(k) for k in self.key_of if k >= 0)

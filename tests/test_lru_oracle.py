@@ -135,3 +135,77 @@ def test_markov_logits_route_back_to_generated_ids():
     ids, logits = gen.markov_routing(w.seed, 4, 3, w.T, w.E, w.k, w.p_stay, w.zipf_s)
     got, _ = oracle.route(logits.reshape(-1, w.E), w.k)
     np.testing.assert_array_equal(got, ids.reshape(-1, w.k))
+
+
+def test_qstar_closed_forms_and_hand_values():
+    """q* (misses filled over PCIe, the rest run on the host) against what the balance fixes:
+    no host bandwidth -> fill all; no PCIe -> fill none; equal bandwidths -> half, ties to
+    the larger count; two hand-computed cases."""
+    for m in range(0, 12):
+        assert oracle.qstar(m, 1000, 0) == m
+        assert oracle.qstar(m, 0, 1000) == 0
+        assert oracle.qstar(m, 777, 777) == (m + 1) // 2
+    # m=10, P=3, H=1: max(q*H, (m-q)*P) is 9 at q=7, 8 at q=8, 9 at q=9, so q*=8
+    assert oracle.qstar(10, 3, 1) == 8
+    # m=6 misses, PCIe 57 GB/s, host 100 GB/s: optimum 6*57/157 = 2.18; q=2 -> max(200000,
+    # 228000), q=3 -> max(300000, 171000): q*=2
+    assert oracle.qstar(6, 57000, 100000) == 2
+    with pytest.raises(ValueError):
+        oracle.qstar(3, 0, 0)
+
+
+def test_qstar_is_a_neighbour_of_the_continuous_balance():
+    """The integer optimum is floor or ceil of m*P/(P+H) (the balance point of the two
+    linear times), chosen by the smaller max-time, ties to the larger: checked with exact
+    fractions over a grid."""
+    from fractions import Fraction
+    for m in range(0, 17):
+        for P in (0, 1, 2, 3, 5, 8, 57, 100):
+            for H in (0, 1, 2, 3, 5, 8, 57, 100):
+                if P + H == 0:
+                    continue
+                q0 = Fraction(m * P, P + H)
+                lo, hi = int(q0), min(m, int(q0) + (q0.denominator != 1))
+                t = lambda q: max(Fraction(q, P) if P else (0 if q == 0 else Fraction(10**9)),
+                                  Fraction(m - q, H) if H else (0 if q == m else Fraction(10**9)))
+                want = hi if t(hi) <= t(lo) else lo
+                assert oracle.qstar(m, P, H) == want, (m, P, H)
+
+
+def test_split_step_invariants_on_markov_trace():
+    """step_split: with no host bandwidth it is step; otherwise the first q* misses (ascending
+    id) are filled exactly as step fills them, the rest stay out of the cache, and the tables
+    stay mutually consistent."""
+    w = configs.with_(configs.LRU_DECODE, L=4, E=64, S=48)
+    steps = 40
+    ids, _ = gen.markov_routing(w.seed, steps, w.L, w.T, w.E, w.k, w.p_stay, w.zipf_s)
+    plain, same = LruSim(w.L, w.E, w.S), LruSim(w.L, w.E, w.S)
+    split = LruSim(w.L, w.E, w.S)
+    P, H = 57000, 30000
+    saw_host, n_host = False, 0
+    for s in range(steps):
+        for layer in range(w.L):
+            a = plain.step(layer, ids[s, layer])
+            b = same.step_split(layer, ids[s, layer], 1000, 0)
+            np.testing.assert_array_equal(a[0], b[0])
+            assert a[1] == b[1] and b[2] == []
+            resident = split.resident_keys()
+            U = sorted(set(int(e) for e in ids[s, layer].ravel()))
+            misses = [e for e in U if layer * w.E + e not in resident]
+            slot, fills, host = split.step_split(layer, ids[s, layer], P, H)
+            q = oracle.qstar(len(misses), P, H)
+            assert [e for _, _, e, _ in fills] == misses[:q]
+            assert host == misses[q:]
+            saw_host |= bool(host)
+            n_host += len(host)
+            for e in host:
+                assert slot[e] == -1 and split.slot_of[layer * w.E + e] == -1
+            for e in U:
+                if e not in host:
+                    assert split.key_of[slot[e]] == layer * w.E + e
+            for sl in range(w.S):
+                if split.key_of[sl] >= 0:
+                    assert split.slot_of[split.key_of[sl]] == sl
+    assert saw_host
+    assert split.host_runs == n_host
+    assert (plain.accesses, plain.hits, plain.misses) == (same.accesses, same.hits, same.misses)
