@@ -32,7 +32,8 @@ MOE_PATH_GEMM = 2
 EXPORTS = [
     "moe_strerror", "moe_abi_version", "moe_router_logits", "moe_route",
     "moe_permute_workspace_bytes", "moe_permute", "moe_expert_ffn_workspace_bytes",
-    "moe_expert_ffn", "moe_combine", "cache_init", "cache_lookup_update", "cache_fill",
+    "moe_expert_ffn", "moe_combine", "cache_init", "cache_lookup_update",
+    "cache_lookup_update_split", "cache_fill",
     "cache_fill_device", "cache_fill_masks", "layer_stream_prefetch", "moe_hbm_read_probe", "moe_copy_probe",
 ]
 
@@ -84,6 +85,8 @@ def lib():
             "cache_init": ([ctypes.POINTER(moe_cache_t), vp], i32),
             "cache_lookup_update": ([ctypes.POINTER(moe_cache_t), i32, vp, i32, i32, vp, vp, vp,
                                      vp], i32),
+            "cache_lookup_update_split": ([ctypes.POINTER(moe_cache_t), i32, vp, i32, i32, i32, i32,
+                                           vp, vp, vp, vp, vp], i32),
             "cache_fill": ([ctypes.POINTER(moe_cache_t), vp, i32, vp], i32),
             "cache_fill_device": ([ctypes.POINTER(moe_cache_t), vp, vp, i32, vp], i32),
             "cache_fill_masks": ([vp, vp, vp, i32, vp, vp, vp, vp], i32),
@@ -183,6 +186,13 @@ def cache_lookup_update(cache, layer, topk_ids, T, k, expert_slot, fills, n_fill
     _check("cache_lookup_update", lib().cache_lookup_update(
         ctypes.byref(cache), layer, _p(topk_ids), T, k, _p(expert_slot), _p(fills), _p(n_fills),
         _s(stream)))
+
+
+def cache_lookup_update_split(cache, layer, topk_ids, T, k, pcie_mbps, host_mbps, expert_slot,
+                              fills, n_fills, host_mask, stream=None):
+    _check("cache_lookup_update_split", lib().cache_lookup_update_split(
+        ctypes.byref(cache), layer, _p(topk_ids), T, k, pcie_mbps, host_mbps, _p(expert_slot),
+        _p(fills), _p(n_fills), _p(host_mask), _s(stream)))
 
 
 def cache_fill(cache, fills_host, n_fills, copy_stream=None):

@@ -48,16 +48,24 @@ __global__ __launch_bounds__(256) void cache_init_kernel(moe_cache_t c) {
   }
 }
 
+// SPLIT: only the first q* misses (ascending id) are filled, q* minimising
+// max(q * host_mbps, (m - q) * pcie_mbps) over q = 0..m with ties to the larger q (the two
+// paths' times for m misses of equal size, in integers); the others are left to the host
+// (host_mask = 1), take no slot and are not inserted.
+template <bool SPLIT>
 __global__ __launch_bounds__(kCacheThreads) void lru_lookup_update(moe_cache_t c, int layer,
                                                                    const int32_t* __restrict__ ids,
                                                                    int A, int32_t* __restrict__ expert_slot,
                                                                    moe_fill_t* __restrict__ fills,
-                                                                   int32_t* __restrict__ n_fills) {
+                                                                   int32_t* __restrict__ n_fills,
+                                                                   int pcie_mbps, int host_mbps,
+                                                                   uint8_t* __restrict__ host_mask) {
   __shared__ unsigned long long keys[kMaxSlots];
   __shared__ int req[kMaxE];       // 1 = requested
   __shared__ int miss_list[kMaxE];
   __shared__ int s_wave[16];
   __shared__ int s_err;
+  __shared__ int s_q;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = c.E, S = c.S;
   const long long t = *c.clock + 1;  // read before any thread can update the clock
@@ -102,7 +110,26 @@ __global__ __launch_bounds__(kCacheThreads) void lru_lookup_update(moe_cache_t c
     before += w < wave ? s_wave[w] : 0;
     nmiss += s_wave[w];
   }
-  if (miss) miss_list[before + __popcll(mb & lanemask_lt(lane))] = tid;
+  const int my_rank = before + __popcll(mb & lanemask_lt(lane));
+  if (miss) miss_list[my_rank] = tid;
+  int q = nmiss;  // misses filled in this call
+  if (SPLIT) {
+    if (tid == 0) {
+      long long best_t = -1;
+      int best_q = 0;
+      for (int qq = 0; qq <= nmiss; ++qq) {
+        const long long tt = max((long long)qq * host_mbps, (long long)(nmiss - qq) * pcie_mbps);
+        if (best_t < 0 || tt <= best_t) {
+          best_q = qq;
+          best_t = tt;
+        }
+      }
+      s_q = best_q;
+    }
+    __syncthreads();
+    q = s_q;
+  }
+  const bool to_host = miss && my_rank >= q;
   // bitonic sort, ascending
   for (int size = 2; size <= npow; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
@@ -120,7 +147,7 @@ __global__ __launch_bounds__(kCacheThreads) void lru_lookup_update(moe_cache_t c
     }
   }
   __syncthreads();
-  if (tid < nmiss) {
+  if (tid < q) {
     const int s = (int)(keys[tid] & ((1u << kSlotBits) - 1));
     const int e = miss_list[tid];
     const int old = c.key_of[s];
@@ -136,17 +163,18 @@ __global__ __launch_bounds__(kCacheThreads) void lru_lookup_update(moe_cache_t c
     if (hit) {
       c.stamp[slot] = t;
       expert_slot[tid] = slot;
-    } else if (!miss) {
+    } else if (!miss || to_host) {
       expert_slot[tid] = -1;
     }
+    if (SPLIT) host_mask[tid] = to_host;
   }
   if (tid == 0) {
     *c.clock = t;
-    *n_fills = nmiss;
+    *n_fills = q;
     c.stats[0] += nU;
     c.stats[1] += nU - nmiss;
     c.stats[2] += nmiss;
-    c.stats[3] += (long long)nmiss * (long long)c.entry_bytes;
+    c.stats[3] += (long long)q * (long long)c.entry_bytes;
   }
 }
 
@@ -254,8 +282,25 @@ extern "C" int cache_lookup_update(const moe_cache_t* cache, int layer, const in
   if (T < 0 || k <= 0 || k > kMaxK || k > cache->E) return MOE_EINVAL;
   if ((long long)T * k >= (1ll << 31)) return MOE_EINVAL;
   if (!expert_slot || !fills || !n_fills || (T > 0 && !topk_ids)) return MOE_EINVAL;
-  hipLaunchKernelGGL(lru_lookup_update, dim3(1), dim3(kCacheThreads), 0, stream, *cache, layer,
-                     topk_ids, T * k, expert_slot, fills, n_fills);
+  hipLaunchKernelGGL(lru_lookup_update<false>, dim3(1), dim3(kCacheThreads), 0, stream, *cache,
+                     layer, topk_ids, T * k, expert_slot, fills, n_fills, 0, 0, (uint8_t*)nullptr);
+  MOE_LAUNCH_CHECK();
+  return MOE_OK;
+}
+
+extern "C" int cache_lookup_update_split(const moe_cache_t* cache, int layer,
+                                         const int32_t* topk_ids, int T, int k, int pcie_mbps,
+                                         int host_mbps, int32_t* expert_slot, moe_fill_t* fills,
+                                         int32_t* n_fills, uint8_t* host_mask, hipStream_t stream) {
+  if (!cache_ok(cache)) return MOE_EINVAL;
+  if (layer < 0 || layer >= cache->L) return MOE_ERANGE;
+  if (T < 0 || k <= 0 || k > kMaxK || k > cache->E) return MOE_EINVAL;
+  if ((long long)T * k >= (1ll << 31)) return MOE_EINVAL;
+  if (pcie_mbps < 0 || host_mbps < 0 || (long long)pcie_mbps + host_mbps == 0) return MOE_EINVAL;
+  if (!expert_slot || !fills || !n_fills || !host_mask || (T > 0 && !topk_ids)) return MOE_EINVAL;
+  hipLaunchKernelGGL(lru_lookup_update<true>, dim3(1), dim3(kCacheThreads), 0, stream, *cache,
+                     layer, topk_ids, T * k, expert_slot, fills, n_fills, pcie_mbps, host_mbps,
+                     host_mask);
   MOE_LAUNCH_CHECK();
   return MOE_OK;
 }

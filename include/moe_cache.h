@@ -206,6 +206,28 @@ int cache_lookup_update(const moe_cache_t* cache, int layer, const int32_t* topk
                         int32_t* expert_slot, moe_fill_t* fills, int32_t* n_fills,
                         hipStream_t stream);
 
+/* cache_lookup_update with the misses split between PCIe fills and host
+ * execution (the q-star policy: the runtime measures host-side expert
+ * throughput and pinned PCIe bandwidth and decides from them how many misses
+ * move to the GPU and how many run on the CPU; benchmark page, "How FreeToken
+ * serves large MoE models", its runtime-tier table and "adaptive cache miss"
+ * card; RTX-4090 page, "Setup and tuning workflow", "Measure the system").
+ * With m misses this call fills q* of them, q* minimising
+ * max(q * host_mbps, (m - q) * pcie_mbps) over q = 0..m (the two concurrent
+ * paths' times for entries of equal size), ties to the larger q: the first q*
+ * misses in ascending id are handled exactly as cache_lookup_update handles
+ * misses; the others get host_mask[e] = 1 and expert_slot[e] = -1, take no
+ * slot and are not inserted (their FFN is the host's to run; host execution is
+ * not part of this library).  *n_fills = q*; stats count all m misses and
+ * q* * entry_bytes of fills.  pcie_mbps, host_mbps: measured bandwidths in
+ * MB/s, >= 0, not both 0 (host_mbps = 0 gives cache_lookup_update).
+ * host_mask: device array of E bytes.  Capacity and id errors as in
+ * cache_lookup_update (on error only status and *n_fills = 0 are written). */
+int cache_lookup_update_split(const moe_cache_t* cache, int layer, const int32_t* topk_ids, int T,
+                              int k, int pcie_mbps, int host_mbps, int32_t* expert_slot,
+                              moe_fill_t* fills, int32_t* n_fills, uint8_t* host_mask,
+                              hipStream_t stream);
+
 /* Copy the n_fills missed entries from the pinned host pool into their slots
  * over PCIe (benchmark page, runtime-tier table: the PCIe link moves selected
  * experts into the GPU cache).  fills_host: host copy of the records written

@@ -88,6 +88,17 @@ def test_cache_host_validation():
     assert fd(ctypes.byref(c), 4096, 4096, 0, None) == moe.MOE_EINVAL  # unaligned arena
     odd = moe.moe_cache_t(2, 4, 8, 0, 72, 4096, 4096, 4096, 4096, 4096, 4096, 4096, 4096)
     assert fd(ctypes.byref(odd), 4096, 4096, 0, None) == moe.MOE_EINVAL  # entry_bytes % 16
+    ls = moe.lib().cache_lookup_update_split
+    args = [ctypes.byref(c), 0, 1, 1, 1, 57000, 30000, 1, 1, 1, 1, None]
+    for i, v in ((5, -1), (6, -1)):
+        bad = list(args); bad[i] = v
+        assert ls(*bad) == moe.MOE_EINVAL
+    both0 = list(args); both0[5] = 0; both0[6] = 0
+    assert ls(*both0) == moe.MOE_EINVAL
+    nomask = list(args); nomask[10] = None
+    assert ls(*nomask) == moe.MOE_EINVAL
+    badlayer = list(args); badlayer[1] = 2
+    assert ls(*badlayer) == moe.MOE_ERANGE
     fm = moe.lib().cache_fill_masks
     assert fm(4096, 4096, 4096, 0, 4096, 4096, None, None) == moe.MOE_EINVAL     # E = 0
     assert fm(4096, 4096, 4096, 1025, 4096, 4096, None, None) == moe.MOE_EINVAL  # E > 1024

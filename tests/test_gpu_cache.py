@@ -336,3 +336,82 @@ def test_fill_masks_split_requested_experts():
     torch.cuda.synchronize()
     assert int(dc.status.item()) == moe.MOE_ERANGE
     assert int(hit.sum().item()) == 0 and int(miss.sum().item()) == 0
+
+
+@pytest.mark.parametrize("pcie,host", [(1000, 0), (0, 1000), (57000, 30000), (20000, 60000)])
+def test_split_lookup_trace_bit_exact(pcie, host):
+    """cache_lookup_update_split against LruSim.step_split on a Markov trace: expert_slot,
+    fill records, host mask every call; all tables every 16 calls; counters at the end."""
+    w = configs.with_(configs.LRU_DECODE, L=4, E=64, S=48, steps=60)
+    ids, _ = gen.markov_routing(w.seed, w.steps, w.L, w.T, w.E, w.k, w.p_stay, w.zipf_s)
+    ids_dev = dev(ids)
+    dc = DevCache(w.L, w.E, w.S, w.entry_bytes)
+    sim = LruSim(w.L, w.E, w.S)
+    host_mask = torch.empty(w.E, dtype=torch.uint8, device="cuda")
+    calls = fills_total = 0
+    for s in range(w.steps):
+        for layer in range(w.L):
+            moe.cache_lookup_update_split(dc.desc, layer, ids_dev[s, layer], w.T, w.k, pcie, host,
+                                          dc.expert_slot, dc.fills, dc.n_fills, host_mask)
+            slot_ref, fills, to_host = sim.step_split(layer, ids[s, layer], pcie, host)
+            assert dc.fills_host() == [tuple(f) for f in fills], (s, layer)
+            np.testing.assert_array_equal(dc.expert_slot.cpu().numpy(), slot_ref)
+            want = np.zeros(w.E, dtype=np.uint8)
+            want[to_host] = 1
+            np.testing.assert_array_equal(host_mask.cpu().numpy(), want)
+            fills_total += len(fills)
+            calls += 1
+            if calls % 16 == 0:
+                _compare_tables(dc, sim)
+    _compare_tables(dc, sim)
+    assert int(dc.stats[3].item()) == fills_total * w.entry_bytes
+    assert int(dc.status.item()) == 0
+    if host == 0:
+        assert sim.host_runs == 0
+    if pcie == 0:
+        assert fills_total == 0 and sim.host_runs == sim.misses
+
+
+def test_split_layer_with_host_rows_equals_oracle():
+    """A decode layer under the q* split: lookup_split -> masks -> device fill -> FFN of hits
+    and of filled misses on the GPU; the rows of the experts left to the host are written
+    by the test from the oracle (standing in for host execution, which is not part of the
+    library) -> combine.  Every layer's output equals the oracle's full layer."""
+    w = _small_lru_workload(41)
+    pool = host_pool(w)
+    arena = torch.zeros((w.S, w.entry_elems), dtype=torch.bfloat16, device="cuda")
+    dc = DevCache(w.L, w.E, w.S, w.entry_bytes, arena, pool)
+    lay = MoeLayer(w.T, w.E, w.k, w.d, w.f)
+    hit = torch.empty(w.E, dtype=torch.uint8, device="cuda")
+    miss, host_mask = torch.empty_like(hit), torch.empty_like(hit)
+    tables = [oracle_table(w, range(w.E), layer) for layer in range(w.L)]
+    n_host = 0
+    for step in range(4):
+        for layer in range(w.L):
+            x = configs.gen_x(w, layer, attempt=step)
+            lg = gen.routing_logits(w.seed, gen.TAG_LOGIT + layer * 0x10000 + step * 0x100, w.T,
+                                    w.E, w.k)
+            lay.route(dev(lg))
+            moe.cache_lookup_update_split(dc.desc, layer, lay.ids, w.T, w.k, 20000, 30000,
+                                          dc.expert_slot, dc.fills, dc.n_fills, host_mask)
+            moe.cache_fill_masks(dc.expert_slot, dc.fills, dc.n_fills, w.E, hit, miss, dc.status)
+            moe.cache_fill_device(dc.desc, dc.fills, dc.n_fills, w.E)
+            lay.permute()
+            key = dict(slot_key=dc.key_of, key_base=layer * w.E)
+            lay.ffn(x_device(w, x), arena, w.entry_bytes, dc.expert_slot, mask=hit, **key)
+            lay.ffn(x_device(w, x), arena, w.entry_bytes, dc.expert_slot, mask=miss, **key)
+            torch.cuda.synchronize()
+            ids = lay.ids.cpu().numpy()
+            on_host = set(np.nonzero(host_mask.cpu().numpy())[0].tolist())
+            assign = [a for a in range(w.T * w.k) if int(ids.flat[a]) in on_host]
+            if assign:
+                y = oracle.expert_ffn(x, ids, tables[layer], assign)
+                pos = lay.inv.cpu().numpy()[assign]
+                lay.y_perm[torch.from_numpy(pos).long().cuda()] = torch.from_numpy(y).float().cuda()
+            n_host += len(on_host)
+            lay.combine()
+            torch.cuda.synchronize()
+            _, _, ref = oracle.moe_layer(x, lg, w.k, tables[layer])
+            assert_close(lay.out.cpu().numpy(), ref, bf16_tol(ref), f"step {step} layer {layer}")
+    assert n_host > 0
+    assert int(dc.status.item()) == 0 and int(lay.status.item()) == 0
