@@ -117,6 +117,32 @@ class LruSim:
     def resident_keys(self):
         return set(int(k) for k in self.key_of if k >= 0)
 
+    def resized(self, S_new):
+        """The cache rebuilt with S_new slots at a safe point, keeping the most recent entries.
+
+        FreeToken pages: the GPU expert capacity can be reconfigured at a safe runtime point
+        without restarting the engine or reloading the host-resident pool (benchmark page,
+        "elastic cache" feature card; vram page, on the 2026 paper's elastic memory).  No
+        rule is given for what survives.  Reading: keep the min(S_new, resident) entries
+        used most recently (stamp descending, ties to the lower slot), place them in slots
+        0..n-1 in ascending order of their old slot (so the relative order that breaks
+        stamp ties is kept), keep their stamps; the clock and the counters carry over.
+        """
+        if S_new <= 0:
+            raise ValueError("S_new must be positive")
+        occ = [s for s in range(self.S) if self.key_of[s] >= 0]
+        keep = sorted(occ, key=lambda s: (-int(self.stamp[s]), s))[:S_new]
+        new = LruSim(self.L, self.E, S_new)
+        for j, s in enumerate(sorted(keep)):
+            key = int(self.key_of[s])
+            new.key_of[j] = key
+            new.slot_of[key] = j
+            new.stamp[j] = self.stamp[s]
+        new.clock = self.clock
+        new.accesses, new.hits, new.misses = self.accesses, self.hits, self.misses
+        new.host_runs = self.host_runs
+        return new
+
 
 class CapacityError(Exception):
     def __init__(self, need, have):

@@ -209,3 +209,61 @@ def test_split_step_invariants_on_markov_trace():
     assert saw_host
     assert split.host_runs == n_host
     assert (plain.accesses, plain.hits, plain.misses) == (same.accesses, same.hits, same.misses)
+
+
+def _markov_trace(L, E, S, steps, seed_shift=0):
+    w = configs.with_(configs.LRU_DECODE, L=L, E=E, S=S, steps=steps)
+    ids, _ = gen.markov_routing(w.seed + seed_shift, steps, L, w.T, E, w.k, w.p_stay, w.zipf_s)
+    return w, ids
+
+
+def test_resize_to_same_size_is_invisible_to_hits_and_residency():
+    """Rebuilding at the same S only renumbers slots: the hit/miss sequence and the resident
+    key sets of the rest of the trace equal those of the cache that was never rebuilt."""
+    w, ids = _markov_trace(4, 64, 40, 60)
+    a, b = LruSim(w.L, w.E, w.S), LruSim(w.L, w.E, w.S)
+    for s in range(w.steps):
+        if s == 25:
+            b = b.resized(w.S)
+            assert b.resident_keys() == a.resident_keys()
+        for layer in range(w.L):
+            _, fa = a.step(layer, ids[s, layer])
+            _, fb = b.step(layer, ids[s, layer])
+            assert [e for _, _, e, _ in fa] == [e for _, _, e, _ in fb]
+            assert a.resident_keys() == b.resident_keys()
+    assert (a.accesses, a.hits, a.misses, a.clock) == (b.accesses, b.hits, b.misses, b.clock)
+
+
+def test_resize_keeps_the_most_recent_entries():
+    """Shrinking keeps exactly S_new entries, none used less recently than any dropped one
+    (recency tracked independently of the simulator); growing keeps everything and the next
+    misses take the new empty slots first; later calls keep every LRU invariant."""
+    w, ids = _markov_trace(4, 64, 48, 50, seed_shift=1)
+    sim = LruSim(w.L, w.E, w.S)
+    last = {}
+    call = 0
+    for s in range(30):
+        for layer in range(w.L):
+            sim.step(layer, ids[s, layer])
+            call += 1
+            for e in set(int(v) for v in ids[s, layer].ravel()):
+                last[layer * w.E + e] = call
+    before = sim.resident_keys()
+    small = sim.resized(20)
+    kept = small.resident_keys()
+    assert len(kept) == 20 and kept <= before
+    dropped = before - kept
+    assert min(last[k] for k in kept) >= max(last[k] for k in dropped)
+    assert small.clock == sim.clock and small.misses == sim.misses
+    big = small.resized(64)
+    assert big.resident_keys() == kept
+    assert all(big.key_of[j] == -1 and big.stamp[j] == 0 for j in range(20, 64))
+    for s in range(30, w.steps):
+        for layer in range(w.L):
+            before_stamp, before_key = big.stamp.copy(), big.key_of.copy()
+            U = sorted(set(int(e) for e in ids[s, layer].ravel()))
+            _, fills = big.step(layer, ids[s, layer])
+            _check_invariants(big, big.clock, [layer * w.E + e for e in U], fills, before_stamp,
+                              before_key)
+            if s == 30 and layer == 0 and fills:
+                assert fills[0][0] == 20 and fills[0][3] == -1  # first empty slot, no eviction
