@@ -360,13 +360,41 @@ def bench_lru(args, torch, moe):
             raise RuntimeError("lru graph path disagrees with the host-driven path")
         del g
     wall_g = walls[False]
+
+    # elastic resize at a safe point: 1024 -> 512 slots (keeps the 512 most recent entries,
+    # copied arena to arena), then 512 -> 1536
+    def make_cache(S2):
+        t = dict(slot_of=torch.empty(w.L * w.E, **i32), key_of=torch.empty(S2, **i32),
+                 stamp=torch.empty(S2, **i64), clock=torch.empty(1, **i64),
+                 stats=torch.empty(4, **i64), status=torch.zeros(1, **i32),
+                 arena=torch.empty((S2, w.entry_elems), dtype=torch.bfloat16, device="cuda"))
+        d = moe.moe_cache_t(w.L, w.E, S2, 0, w.entry_bytes, *(t[n].data_ptr() for n in (
+            "slot_of", "key_of", "stamp", "clock", "stats", "status", "arena")), pool.data_ptr())
+        return d, t
+    resize = {}
+    cur = desc
+    for S2 in (w.S // 2, w.S * 3 // 2):
+        d2, t2 = make_cache(S2)
+        e0, e1 = _events(torch, 2)
+        with torch.cuda.stream(comp):
+            torch.cuda.synchronize()
+            e0.record(comp)
+            moe.cache_resize(cur, d2, comp)
+            e1.record(comp)
+            torch.cuda.synchronize()
+        kept = int((t2["key_of"] >= 0).sum().item())
+        ms = e0.elapsed_time(e1)
+        resize[f"{cur.S}_to_{S2}"] = dict(ms=ms, kept=kept,
+                                          copy_gbs=2 * kept * w.entry_bytes / (ms * 1e-3) / 1e9)
+        cur, keep_alive = d2, t2
+    del keep_alive
     pool.close()
     del arena
     torch.cuda.empty_cache()
     return dict(workload=w.name, steps=steps, tok_s=steps * w.T / wall, wall_s=wall,
                 graph_device_fill_tok_s=steps * w.T / wall_g, graph_wall_s=wall_g,
                 graph_overlap_tok_s=steps * w.T / walls[True], graph_overlap_wall_s=walls[True],
-                graph_overlap_fill_gbs=float(st[3]) / walls[True] / 1e9,
+                graph_overlap_fill_gbs=float(st[3]) / walls[True] / 1e9, resize=resize,
                 miss_rate=float(st[2] / st[0]), hits=int(st[1]), misses=int(st[2]),
                 fill_gb=float(st[3] / 1e9), fill_gb_per_step=float(st[3] / 1e9 / steps))
 

@@ -34,7 +34,7 @@ EXPORTS = [
     "moe_permute_workspace_bytes", "moe_permute", "moe_expert_ffn_workspace_bytes",
     "moe_expert_ffn", "moe_combine", "cache_init", "cache_lookup_update",
     "cache_lookup_update_split", "cache_fill",
-    "cache_fill_device", "cache_fill_masks", "layer_stream_prefetch", "moe_hbm_read_probe", "moe_copy_probe",
+    "cache_fill_device", "cache_fill_masks", "cache_resize", "layer_stream_prefetch", "moe_hbm_read_probe", "moe_copy_probe",
 ]
 
 
@@ -90,6 +90,7 @@ def lib():
             "cache_fill": ([ctypes.POINTER(moe_cache_t), vp, i32, vp], i32),
             "cache_fill_device": ([ctypes.POINTER(moe_cache_t), vp, vp, i32, vp], i32),
             "cache_fill_masks": ([vp, vp, vp, i32, vp, vp, vp, vp], i32),
+            "cache_resize": ([ctypes.POINTER(moe_cache_t), ctypes.POINTER(moe_cache_t), vp], i32),
             "layer_stream_prefetch": ([vp, vp, sz, i32, vp, vp, vp], i32),
             "moe_hbm_read_probe": ([vp, sz, vp, vp], i32),
             "moe_copy_probe": ([vp, vp, sz, vp], i32),
@@ -210,6 +211,11 @@ def cache_fill_masks(expert_slot, fills, n_fills, E, hit_mask, miss_mask, status
     _check("cache_fill_masks", lib().cache_fill_masks(
         _p(expert_slot), _p(fills), _p(n_fills), E, _p(hit_mask), _p(miss_mask), _p(status),
         _s(stream)))
+
+
+def cache_resize(old_cache, new_cache, stream=None):
+    _check("cache_resize", lib().cache_resize(ctypes.byref(old_cache), ctypes.byref(new_cache),
+                                              _s(stream)))
 
 
 def layer_stream_prefetch(host_src, dst, nbytes, n_chunks, copy_stream=None, wait_before=None,

@@ -48,6 +48,28 @@ __global__ __launch_bounds__(256) void cache_init_kernel(moe_cache_t c) {
   }
 }
 
+// Ascending bitonic sort of keys[0 .. npow) in LDS by the whole workgroup (npow a power of
+// two); ends with a barrier.
+__device__ void bitonic_sort_lds(unsigned long long* keys, int npow) {
+  const int tid = threadIdx.x;
+  for (int size = 2; size <= npow; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      __syncthreads();
+      for (int i = tid; i < (npow >> 1); i += blockDim.x) {
+        const int lo = 2 * stride * (i / stride) + (i % stride);
+        const int hi = lo + stride;
+        const bool asc = (lo & size) == 0;
+        const unsigned long long x = keys[lo], y = keys[hi];
+        if ((x > y) == asc) {
+          keys[lo] = y;
+          keys[hi] = x;
+        }
+      }
+    }
+  }
+  __syncthreads();
+}
+
 // SPLIT: only the first q* misses (ascending id) are filled, q* minimising
 // max(q * host_mbps, (m - q) * pcie_mbps) over q = 0..m with ties to the larger q (the two
 // paths' times for m misses of equal size, in integers); the others are left to the host
@@ -130,23 +152,7 @@ __global__ __launch_bounds__(kCacheThreads) void lru_lookup_update(moe_cache_t c
     q = s_q;
   }
   const bool to_host = miss && my_rank >= q;
-  // bitonic sort, ascending
-  for (int size = 2; size <= npow; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      __syncthreads();
-      for (int i = tid; i < (npow >> 1); i += kCacheThreads) {
-        const int lo = 2 * stride * (i / stride) + (i % stride);
-        const int hi = lo + stride;
-        const bool asc = (lo & size) == 0;
-        const unsigned long long x = keys[lo], y = keys[hi];
-        if ((x > y) == asc) {
-          keys[lo] = y;
-          keys[hi] = x;
-        }
-      }
-    }
-  }
-  __syncthreads();
+  bitonic_sort_lds(keys, npow);
   if (tid < q) {
     const int s = (int)(keys[tid] & ((1u << kSlotBits) - 1));
     const int e = miss_list[tid];
@@ -257,6 +263,103 @@ __global__ __launch_bounds__(kMaxE) void fill_masks_kernel(const int32_t* __rest
   }
 }
 
+// Elastic resize.  Tables: the survivors are the min(S_new, resident) entries with the
+// largest stamps (ties to the lower old slot), found by sorting (2^50 - 1 - stamp, slot)
+// keys; they go to new slots 0..n-1 in ascending old-slot order (block scan of survivor
+// flags) with their stamps; clock and counters carry over.  The new tables were cleared by
+// cache_init_kernel just before.  One workgroup; old S <= 4096.
+constexpr long long kStampLimit = 1ll << 50;  // clock values stay far below this
+
+__global__ __launch_bounds__(kCacheThreads) void resize_tables(moe_cache_t o, moe_cache_t n) {
+  __shared__ unsigned long long keys[kMaxSlots];
+  __shared__ int keep[kMaxSlots];
+  __shared__ int s_wave[kCacheThreads / 64];
+  __shared__ int s_nres;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int S = o.S;
+  int npow = 64;
+  while (npow < S) npow <<= 1;
+  if (tid == 0) s_nres = 0;
+  for (int s = tid; s < npow; s += kCacheThreads) {
+    const bool used = s < S && o.key_of[s] >= 0;
+    keys[s] = used ? ((unsigned long long)(kStampLimit - 1 - o.stamp[s]) << kSlotBits) | (unsigned)s
+                   : ~0ull;
+    if (s < S) keep[s] = 0;
+  }
+  bitonic_sort_lds(keys, npow);
+  // resident count = position of the first empty key (all occupied keys sort before it)
+  for (int i = tid; i < npow; i += kCacheThreads)
+    if (keys[i] != ~0ull && (i + 1 == npow || keys[i + 1] == ~0ull)) s_nres = i + 1;
+  __syncthreads();
+  const int nkeep = min(s_nres, n.S);
+  for (int i = tid; i < nkeep; i += kCacheThreads) keep[(int)(keys[i] & ((1u << kSlotBits) - 1))] = 1;
+  __syncthreads();
+  // new index of each kept slot = number of kept slots before it (4 slots per thread)
+  int c = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int s = tid * 4 + q;
+    c += s < S ? keep[s] : 0;
+  }
+  int x = c;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) s_wave[wave] = x;
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < wave; ++w) base += s_wave[w];
+  int j = base + x - c;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int s = tid * 4 + q;
+    if (s < S && keep[s]) {
+      const int key = o.key_of[s];
+      n.key_of[j] = key;
+      n.stamp[j] = o.stamp[s];
+      n.slot_of[key] = j;
+      ++j;
+    }
+  }
+  if (tid == 0) {
+    *n.clock = *o.clock;
+    for (int i = 0; i < 4; ++i) n.stats[i] = o.stats[i];
+  }
+}
+
+// Copies the arena entry of every occupied new slot from its old slot.
+__global__ __launch_bounds__(kFillThreads) void resize_copy(moe_cache_t o, moe_cache_t n) {
+  const size_t n16 = n.entry_bytes / 16;
+  constexpr size_t per_iter = (size_t)kFillThreads * kFillUnroll;
+  const size_t iters = (n16 + per_iter - 1) / per_iter;
+  const size_t total = (size_t)n.S * iters;
+  const u32x4* src_arena = (const u32x4*)o.arena;
+  u32x4* dst_arena = (u32x4*)n.arena;
+  for (size_t w = blockIdx.x; w < total; w += gridDim.x) {
+    const int j = (int)(w / iters);
+    const size_t it = w - (size_t)j * iters;
+    const int key = n.key_of[j];
+    if (key < 0) continue;
+    const int s = o.slot_of[key];
+    const u32x4* src = src_arena + (size_t)s * n16;
+    u32x4* dst = dst_arena + (size_t)j * n16;
+    const size_t b = it * per_iter + threadIdx.x;
+    u32x4 v[kFillUnroll];
+#pragma unroll
+    for (int q = 0; q < kFillUnroll; ++q) {
+      const size_t i = b + (size_t)q * kFillThreads;
+      if (i < n16) v[q] = src[i];
+    }
+#pragma unroll
+    for (int q = 0; q < kFillUnroll; ++q) {
+      const size_t i = b + (size_t)q * kFillThreads;
+      if (i < n16) dst[i] = v[q];
+    }
+  }
+}
+
 bool cache_ok(const moe_cache_t* c) {
   return c && c->L > 0 && c->E > 0 && c->E <= kMaxE && c->S > 0 && c->S <= kMaxSlots &&
          (long long)c->L * c->E < (1ll << 31) && c->entry_bytes > 0 && c->slot_of && c->key_of &&
@@ -360,6 +463,34 @@ extern "C" int cache_fill_masks(const int32_t* expert_slot, const moe_fill_t* fi
   if (!expert_slot || !fills || !n_fills || !hit_mask || !miss_mask) return MOE_EINVAL;
   hipLaunchKernelGGL(fill_masks_kernel, dim3(1), dim3(kMaxE), 0, stream, expert_slot, fills,
                      n_fills, E, hit_mask, miss_mask, status);
+  MOE_LAUNCH_CHECK();
+  return MOE_OK;
+}
+
+extern "C" int cache_resize(const moe_cache_t* old_cache, const moe_cache_t* new_cache,
+                            hipStream_t stream) {
+  if (!cache_ok(old_cache) || !cache_ok(new_cache)) return MOE_EINVAL;
+  const moe_cache_t& o = *old_cache;
+  const moe_cache_t& n = *new_cache;
+  if (o.L != n.L || o.E != n.E || o.entry_bytes != n.entry_bytes) return MOE_EINVAL;
+  if (!o.arena || !n.arena || o.entry_bytes % 16 != 0 || !moe_aligned16(o.arena) ||
+      !moe_aligned16(n.arena))
+    return MOE_EINVAL;
+  const uintptr_t oa = (uintptr_t)o.arena, na = (uintptr_t)n.arena;
+  if (oa < na + (uintptr_t)n.S * n.entry_bytes && na < oa + (uintptr_t)o.S * o.entry_bytes)
+    return MOE_EINVAL;  // arenas overlap
+  if (o.slot_of == n.slot_of || o.key_of == n.key_of || o.stamp == n.stamp) return MOE_EINVAL;
+  const long long nt = std::max<long long>((long long)n.L * n.E, n.S);
+  const int blocks = (int)std::min<long long>((nt + 255) / 256, 4096);
+  hipLaunchKernelGGL(cache_init_kernel, dim3(blocks), dim3(256), 0, stream, n);
+  MOE_LAUNCH_CHECK();
+  hipLaunchKernelGGL(resize_tables, dim3(1), dim3(kCacheThreads), 0, stream, o, n);
+  MOE_LAUNCH_CHECK();
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 256;
+  hipLaunchKernelGGL(resize_copy, dim3(4 * cus), dim3(kFillThreads), 0, stream, o, n);
   MOE_LAUNCH_CHECK();
   return MOE_OK;
 }

@@ -185,7 +185,8 @@ typedef struct {
 } moe_fill_t;
 
 /* Empty cache: slot_of = key_of = -1, stamp = clock = stats = 0, status = 0.
- * Runs a fill kernel (no memset nodes), so it may be captured.  S <= 8192. */
+ * Runs a fill kernel (no memset nodes), so it may be captured.  1 <= S <= 4096
+ * (the lookup sorts one key per slot in LDS). */
 int cache_init(const moe_cache_t* cache, hipStream_t stream);
 
 /* One lookup/update of the global LRU for `layer` with the T*k requested ids
@@ -274,6 +275,20 @@ int cache_fill_device(const moe_cache_t* cache, const moe_fill_t* fills, const i
 int cache_fill_masks(const int32_t* expert_slot, const moe_fill_t* fills, const int32_t* n_fills,
                      int E, uint8_t* hit_mask, uint8_t* miss_mask, int32_t* status,
                      hipStream_t stream);
+
+/* Elastic resize of the expert cache at a safe point (benchmark page, "elastic
+ * cache" feature card: GPU expert capacity can be reconfigured at a safe runtime
+ * point without reloading the host-resident pool).  new_cache has its own S'
+ * slots, tables and arena (same L, E, entry_bytes; arenas must not overlap;
+ * 1 <= S' <= 4096); host_pool is not touched.  The new tables are rebuilt from
+ * the old ones: the min(S', resident) entries used most recently (stamp
+ * descending, ties to the lower old slot) are kept, placed in new slots 0..n-1
+ * in ascending order of their old slot, with their stamps; their arena entries
+ * are copied device to device; the other new slots are empty; clock and stats
+ * carry over; new status = 0.  The old cache is only read (its memory may be
+ * released once the stream has passed this call).  Nothing else may use either
+ * cache until the call completes on `stream`.  Capture-safe. */
+int cache_resize(const moe_cache_t* old_cache, const moe_cache_t* new_cache, hipStream_t stream);
 
 /* Full-layer streaming for prefill (llama page, "Official project overview";
  * benchmark page, "How FreeToken serves large MoE models"): waits on

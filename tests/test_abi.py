@@ -99,6 +99,21 @@ def test_cache_host_validation():
     assert ls(*nomask) == moe.MOE_EINVAL
     badlayer = list(args); badlayer[1] = 2
     assert ls(*badlayer) == moe.MOE_ERANGE
+    rs = moe.lib().cache_resize
+    a = moe.moe_cache_t(2, 4, 8, 0, 64, 4096, 8192, 12288, 16, 32, 48, 1 << 20, 0)
+    b = moe.moe_cache_t(2, 4, 4, 0, 64, 20480, 24576, 28672, 64, 80, 96, 1 << 21, 0)
+    ovl = moe.moe_cache_t.from_buffer_copy(b)
+    ovl.arena = (1 << 20) + 64  # inside a's arena
+    assert rs(ctypes.byref(a), ctypes.byref(ovl), None) == moe.MOE_EINVAL
+    otherE = moe.moe_cache_t.from_buffer_copy(b)
+    otherE.E = 5
+    assert rs(ctypes.byref(a), ctypes.byref(otherE), None) == moe.MOE_EINVAL
+    shared = moe.moe_cache_t.from_buffer_copy(b)
+    shared.slot_of = a.slot_of
+    assert rs(ctypes.byref(a), ctypes.byref(shared), None) == moe.MOE_EINVAL
+    noarena = moe.moe_cache_t.from_buffer_copy(b)
+    noarena.arena = 0
+    assert rs(ctypes.byref(a), ctypes.byref(noarena), None) == moe.MOE_EINVAL
     fm = moe.lib().cache_fill_masks
     assert fm(4096, 4096, 4096, 0, 4096, 4096, None, None) == moe.MOE_EINVAL     # E = 0
     assert fm(4096, 4096, 4096, 1025, 4096, 4096, None, None) == moe.MOE_EINVAL  # E > 1024

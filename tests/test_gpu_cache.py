@@ -415,3 +415,48 @@ def test_split_layer_with_host_rows_equals_oracle():
             assert_close(lay.out.cpu().numpy(), ref, bf16_tol(ref), f"step {step} layer {layer}")
     assert n_host > 0
     assert int(dc.status.item()) == 0 and int(lay.status.item()) == 0
+
+
+def _arena_holds_pool(dc, arena, pool, w):
+    """Every occupied slot of the device cache holds its pool entry."""
+    keys = dc.key_of.cpu().numpy()
+    for j in np.nonzero(keys >= 0)[0]:
+        layer, e = divmod(int(keys[j]), w.E)
+        got = arena[j].view(torch.int16).cpu().numpy().view(np.uint16)
+        np.testing.assert_array_equal(got, _pool_entry(pool, w, layer, e), f"slot {j}")
+
+
+def test_resize_shrink_grow_mid_trace_matches_oracle():
+    """A trace with device fills, resized to fewer slots and then to more at safe points:
+    after each resize and every later call the tables equal LruSim.resized's, the arena's
+    occupied slots hold their pool entries, and lookups keep matching the simulator."""
+    w = configs.Workload("lru_resize", seed=43, T=4, d=128, E=16, k=3, f=128, dtype=gen.BF16,
+                         L=3, S=24, alpha=0.5)
+    pool = host_pool(w)
+    steps = 18
+    ids, _ = gen.markov_routing(w.seed, steps, w.L, w.T, w.E, w.k, 0.6, 1.1)
+    ids_dev = dev(ids)
+    sizes = {6: 13, 12: 30}  # step -> new slot count (shrink below residency, then grow)
+    arena = torch.zeros((w.S, w.entry_elems), dtype=torch.bfloat16, device="cuda")
+    dc = DevCache(w.L, w.E, w.S, w.entry_bytes, arena, pool)
+    sim = LruSim(w.L, w.E, w.S)
+    for s in range(steps):
+        if s in sizes:
+            S2 = sizes[s]
+            arena2 = torch.zeros((S2, w.entry_elems), dtype=torch.bfloat16, device="cuda")
+            dc2 = DevCache(w.L, w.E, S2, w.entry_bytes, arena2, pool)
+            moe.cache_resize(dc.desc, dc2.desc)
+            torch.cuda.synchronize()
+            sim = sim.resized(S2)
+            dc, arena = dc2, arena2
+            _compare_tables(dc, sim)
+            _arena_holds_pool(dc, arena, pool, w)
+        for layer in range(w.L):
+            dc.lookup(layer, ids_dev[s, layer], w.T, w.k)
+            moe.cache_fill_device(dc.desc, dc.fills, dc.n_fills, w.E)
+            slot_ref, fills = sim.step(layer, ids[s, layer])
+            assert dc.fills_host() == [tuple(f) for f in fills], (s, layer)
+            np.testing.assert_array_equal(dc.expert_slot.cpu().numpy(), slot_ref)
+        _compare_tables(dc, sim)
+        _arena_holds_pool(dc, arena, pool, w)
+    assert int(dc.status.item()) == 0
