@@ -57,7 +57,7 @@ def _ffn_flops(w):
 
 
 CSRC = os.path.join(ROOT, "expert_ffn_cache_amd", "csrc")
-GEMV_SOURCES = [os.path.join(CSRC, n) for n in ("common.h", "ffn_args.h", "ffn_gemv.hip")]
+GEMV_SOURCES = [os.path.join(CSRC, n) for n in ("common.h", "ffn_args.h", "ffn.hip", "ffn_dot.hip")]
 
 
 def sources_sha256(paths):

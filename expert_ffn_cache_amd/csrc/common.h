@@ -34,6 +34,10 @@ typedef const __attribute__((address_space(1))) u32x4* gptr16;
 // 16-byte global load (global_load_dwordx4, not a flat load).
 __device__ __forceinline__ u32x4 ldg16(const void* p) { return *(gptr16)p; }
 
+// 16-byte non-temporal global load (nt): for data streamed once in whole cache lines, such
+// as expert weight rows in the decode path.
+__device__ __forceinline__ u32x4 ldg16_nt(const void* p) { return __builtin_nontemporal_load((gptr16)p); }
+
 // Compiler-only fence: memory operations are not moved across it.  Placed after
 // prefetch loads so they are issued where written instead of being sunk to their use.
 __device__ __forceinline__ void issue_fence() { asm volatile("" ::: "memory"); }

@@ -8,15 +8,22 @@
 // Three paths:
 //  * fp32 (MOE_F32 weights): plain fp32 FMA loops in this file; small shapes only.
 //  * GEMV (bf16, decode-shaped counts, a few tokens per expert): weight streaming from
-//    HBM into registers, ffn_gemv.hip.
+//    HBM into registers; up to 8 tokens per call with packed bf16 dot products and whole
+//    1 KB row loads (ffn_dot.hip), above that with MFMA (ffn_gemv.hip).
 //  * GEMM (bf16, prefill-shaped counts): LDS-tiled grouped GEMM with direct global->LDS
 //    loads and persistent XCD-aware workgroups, ffn_gemm.hip.
 // Both bf16 paths fuse SiLU(g)*u into the gate/up epilogue and write h once as bf16.
+#include <algorithm>
+
 #include "ffn_args.h"
 
 using namespace moe;
 
 namespace {
+
+constexpr int kDotMaxT = 8;     // up to this many tokens per call every expert takes the dot path
+constexpr int kSplitMaxT = 64;  // up to this many, experts are split by rows between the paths
+constexpr int kDotMaxRows = 4;  // rows per expert the dot path takes when splitting
 
 // ------------------------------------------------------------------ fp32 path
 __global__ __launch_bounds__(64) void f32_gateup(FfnArgs p) {
@@ -101,5 +108,22 @@ extern "C" int moe_expert_ffn(const void* x, int act_dtype, const int32_t* perm,
     return MOE_OK;
   }
   if (path == MOE_PATH_AUTO) path = (long long)T * k <= 8ll * E ? MOE_PATH_GEMV : MOE_PATH_GEMM;
-  return path == MOE_PATH_GEMV ? launch_ffn_gemv(p, T, y_dtype, stream) : launch_ffn_gemm(p, y_dtype, stream);
+  if (path == MOE_PATH_GEMM) return launch_ffn_gemm(p, y_dtype, stream);
+  const int A = T * k, experts = std::min(E, A);
+  if (T > kSplitMaxT || !ffn_dot_supported(d, f))
+    return launch_ffn_gemv(p, T, y_dtype, stream, experts, 3);
+  if (T <= kDotMaxT) return launch_ffn_dot(p, y_dtype, stream, experts, 3);
+  // More tokens: split the experts by rows (counted on the device).  Up to kDotMaxRows rows
+  // the dot-product kernels stream an expert's weights once at full rate; above that the
+  // MFMA kernels take the expert (their cost per row is far lower).  At most
+  // A / (kDotMaxRows + 1) experts have more rows, which bounds the second grid.
+  FfnArgs few = p, many = p;
+  few.nmax = kDotMaxRows;
+  many.nmin = kDotMaxRows + 1;
+  const int many_max = std::min(E, A / (kDotMaxRows + 1));
+  int rc = launch_ffn_dot(few, y_dtype, stream, experts, 1);
+  if (rc == MOE_OK) rc = launch_ffn_gemv(many, T, y_dtype, stream, many_max, 1);
+  if (rc == MOE_OK) rc = launch_ffn_dot(few, y_dtype, stream, experts, 2);
+  if (rc == MOE_OK) rc = launch_ffn_gemv(many, T, y_dtype, stream, many_max, 2);
+  return rc;
 }

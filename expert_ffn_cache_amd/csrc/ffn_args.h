@@ -24,6 +24,7 @@ struct FfnArgs {
   void* h;
   void* y;
   int32_t* status;
+  int nmin = 1, nmax = 0x7fffffff;  // only experts with nmin <= rows <= nmax are processed
 };
 
 // Weights of expert e, or nullptr (and MOE_ERANGE) for a missing or stale slot.
@@ -37,7 +38,8 @@ __device__ __forceinline__ const char* entry_of(const FfnArgs& p, int e) {
 }
 
 __device__ __forceinline__ bool active(const FfnArgs& p, int e) {
-  return p.offsets[e + 1] > p.offsets[e] && (!p.mask || p.mask[e]);
+  const int n = p.offsets[e + 1] - p.offsets[e];
+  return n > 0 && n >= p.nmin && n <= p.nmax && (!p.mask || p.mask[e]);
 }
 
 // The a-th active expert in ascending id order, or -1; called by one full wave.
@@ -60,7 +62,12 @@ __device__ __forceinline__ int nth_active_expert(const FfnArgs& p, int a) {
 
 
 // Launchers (argument checks are done by moe_expert_ffn).  Each returns MOE_OK or MOE_EHIP.
-int launch_ffn_gemv(const FfnArgs& p, int T, int y_dtype, hipStream_t stream);
+// `experts`: grid size in experts (an upper bound on the experts the row filter admits);
+// `parts`: 1 = gate/up kernel, 2 = down kernel, 3 = both.
+int launch_ffn_gemv(const FfnArgs& p, int T, int y_dtype, hipStream_t stream, int experts,
+                    int parts);
+int launch_ffn_dot(const FfnArgs& p, int y_dtype, hipStream_t stream, int experts, int parts);
+bool ffn_dot_supported(int d, int f);  // row lengths the dot-product path handles
 int launch_ffn_gemm(const FfnArgs& p, int y_dtype, hipStream_t stream);
 
 }  // namespace moe

@@ -209,27 +209,30 @@ __global__ __launch_bounds__(256) void gemv_down(FfnArgs p) {
 
 }  // namespace
 
-int launch_ffn_gemv(const FfnArgs& p, int T, int y_dtype, hipStream_t stream) {
-  const int amax = std::min(p.E, T * p.k);
-  const dim3 gu(amax * (p.f / 64)), dn(amax * (p.d / 64)), blk(256);
+int launch_ffn_gemv(const FfnArgs& p, int T, int y_dtype, hipStream_t stream, int experts,
+                    int parts) {
+  if (experts <= 0) return MOE_OK;
+  const dim3 gu(experts * (p.f / 64)), dn(experts * (p.d / 64)), blk(256);
   const bool yf = y_dtype == MOE_F32;
-  if (T <= 16) {
-    hipLaunchKernelGGL(gemv_gateup<1>, gu, blk, 0, stream, p);
+  if (parts & 1) {
+    if (T <= 16) hipLaunchKernelGGL(gemv_gateup<1>, gu, blk, 0, stream, p);
+    else if (T <= 32) hipLaunchKernelGGL(gemv_gateup<2>, gu, blk, 0, stream, p);
+    else hipLaunchKernelGGL(gemv_gateup<4>, gu, blk, 0, stream, p);
     MOE_LAUNCH_CHECK();
-    if (yf) hipLaunchKernelGGL((gemv_down<1, MOE_F32>), dn, blk, 0, stream, p);
-    else hipLaunchKernelGGL((gemv_down<1, MOE_BF16>), dn, blk, 0, stream, p);
-  } else if (T <= 32) {
-    hipLaunchKernelGGL(gemv_gateup<2>, gu, blk, 0, stream, p);
-    MOE_LAUNCH_CHECK();
-    if (yf) hipLaunchKernelGGL((gemv_down<2, MOE_F32>), dn, blk, 0, stream, p);
-    else hipLaunchKernelGGL((gemv_down<2, MOE_BF16>), dn, blk, 0, stream, p);
-  } else {
-    hipLaunchKernelGGL(gemv_gateup<4>, gu, blk, 0, stream, p);
-    MOE_LAUNCH_CHECK();
-    if (yf) hipLaunchKernelGGL((gemv_down<4, MOE_F32>), dn, blk, 0, stream, p);
-    else hipLaunchKernelGGL((gemv_down<4, MOE_BF16>), dn, blk, 0, stream, p);
   }
-  MOE_LAUNCH_CHECK();
+  if (parts & 2) {
+    if (T <= 16) {
+      if (yf) hipLaunchKernelGGL((gemv_down<1, MOE_F32>), dn, blk, 0, stream, p);
+      else hipLaunchKernelGGL((gemv_down<1, MOE_BF16>), dn, blk, 0, stream, p);
+    } else if (T <= 32) {
+      if (yf) hipLaunchKernelGGL((gemv_down<2, MOE_F32>), dn, blk, 0, stream, p);
+      else hipLaunchKernelGGL((gemv_down<2, MOE_BF16>), dn, blk, 0, stream, p);
+    } else {
+      if (yf) hipLaunchKernelGGL((gemv_down<4, MOE_F32>), dn, blk, 0, stream, p);
+      else hipLaunchKernelGGL((gemv_down<4, MOE_BF16>), dn, blk, 0, stream, p);
+    }
+    MOE_LAUNCH_CHECK();
+  }
   return MOE_OK;
 }
 
