@@ -57,7 +57,9 @@ def _ffn_flops(w):
 
 
 CSRC = os.path.join(ROOT, "expert_ffn_cache_amd", "csrc")
-GEMV_SOURCES = [os.path.join(CSRC, n) for n in ("common.h", "ffn_args.h", "ffn.hip", "ffn_dot.hip")]
+# sources of the decode expert-FFN call (dispatch + dot-product kernels), which the committed
+# counter summary was taken on
+DECODE_FFN_SOURCES = [os.path.join(CSRC, n) for n in ("common.h", "ffn_args.h", "ffn.hip", "ffn_dot.hip")]
 
 
 def sources_sha256(paths):
@@ -158,7 +160,7 @@ def bench_decode(args, torch, moe, T, alpha, arena):
     achieved = float(np.sum(byts) / (np.sum(ffn_ms) * 1e-3) / 1e9)
     traffic = None
     if T == 8 and alpha == 0.2:  # the configuration the committed counter summary covers
-        traffic = _counter_traffic(GEMV_SOURCES, "ffn_gemv_decode_e256_k6_d4096_f2048_T8_counters.txt")
+        traffic = _counter_traffic(DECODE_FFN_SOURCES, "ffn_dot_decode_e256_k6_d4096_f2048_T8_counters.txt")
     del graphs
     torch.cuda.empty_cache()
     return dict(
@@ -480,28 +482,32 @@ def bench_probe(args, torch, moe):
     """Achievable HBM read bandwidth (read probe) and a plain copy of known size (the
     reference for scaling hardware byte counters: 1 GiB read + 1 GiB written per copy)."""
     n = 1 << 30
-    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    nr = 4 << 30  # read probe: 4 GiB, far beyond the 256 MB last-level cache
+    big = torch.empty(nr, dtype=torch.uint8, device="cuda")
+    big.fill_(1)
+    src = big[:n]
     dst = torch.empty(n, dtype=torch.uint8, device="cuda")
-    src.fill_(1)
     sink = torch.empty(4096, dtype=torch.int32, device="cuda")
     s = torch.cuda.Stream()
     reps = 10
     with torch.cuda.stream(s):
-        moe.moe_hbm_read_probe(src, n, sink, s)
+        moe.moe_hbm_read_probe(big, nr, sink, s)
         moe.moe_copy_probe(src, dst, n, s)
         a, b, c = _events(torch, 3)
         torch.cuda.synchronize()
         a.record(s)
         for _ in range(reps):
-            moe.moe_hbm_read_probe(src, n, sink, s)
+            moe.moe_hbm_read_probe(big, nr, sink, s)
         b.record(s)
         for _ in range(reps):
             moe.moe_copy_probe(src, dst, n, s)
         c.record(s)
         torch.cuda.synchronize()
-    read_gbs = reps * n / (a.elapsed_time(b) * 1e-3) / 1e9
+    read_gbs = reps * nr / (a.elapsed_time(b) * 1e-3) / 1e9
     copy_gbs = reps * 2 * n / (b.elapsed_time(c) * 1e-3) / 1e9
-    return dict(bytes=n, read_gbs=read_gbs, copy_gbs=copy_gbs, read_frac=read_gbs / HBM_PEAK_GBS)
+    del big
+    return dict(read_bytes=nr, copy_bytes=n, read_gbs=read_gbs, copy_gbs=copy_gbs,
+                read_frac=read_gbs / HBM_PEAK_GBS)
 
 
 # ------------------------------------------------------------------------ CPU baseline
