@@ -30,6 +30,7 @@ TAG_MISC = 13
 
 F32 = 0
 BF16 = 1
+MXFP4 = 2  # weights only: OCP MX FP4 (E2M1 codes, one E8M0 scale per 32 elements)
 
 _lib = None
 
@@ -53,6 +54,10 @@ def lib():
         L.gen_fill_normal.restype = None
         L.gen_fill_normal_segments.argtypes = [u64, u64, i64, vp, i64, fl, i32, vp, vp]
         L.gen_fill_normal_segments.restype = None
+        L.gen_mxfp4_block.argtypes = [vp, vp, vp]
+        L.gen_mxfp4_block.restype = None
+        L.gen_fill_mxfp4_rows.argtypes = [u64, u64, i64, vp, i64, fl, vp, vp, vp, vp]
+        L.gen_fill_mxfp4_rows.restype = None
         L.gen_rank_perm.argtypes = [u64, u64, i32, vp]
         L.gen_rank_perm.restype = None
         L.gen_zipf_bias.argtypes = [u64, u64, i32, db, db, vp]
@@ -127,3 +132,34 @@ def markov_routing(seed, steps, L, B, E, k, p_stay=0.7, zipf_s=1.1):
                              TAG_MRANK, TAG_MSTAY, TAG_MZIPF, TAG_MCHOSEN, TAG_MNOISE,
                              _ptr(ids), _ptr(logits))
     return ids, logits
+
+
+def mxfp4_block(values):
+    """Quantise 32 fp32 values to MXFP4: (16 code bytes, scale byte) (see gen/gen.c)."""
+    v = np.ascontiguousarray(values, dtype=np.float32)
+    assert v.shape == (32,)
+    codes = np.zeros(16, dtype=np.uint8)
+    scale = np.zeros(1, dtype=np.uint8)
+    lib().gen_mxfp4_block(v.ctypes.data, codes.ctypes.data, scale.ctypes.data)
+    return codes, int(scale[0])
+
+
+def fill_mxfp4_rows_ptr(seed, tag, row_i0, K, sd, codes_ptr, code_off, scales_ptr, scale_off):
+    """Rows of K normals quantised to MXFP4 into raw buffers (byte offsets per row)."""
+    row_i0 = np.ascontiguousarray(row_i0, dtype=np.uint64)
+    code_off = np.ascontiguousarray(code_off, dtype=np.int64)
+    scale_off = np.ascontiguousarray(scale_off, dtype=np.int64)
+    lib().gen_fill_mxfp4_rows(seed, tag, len(row_i0), row_i0.ctypes.data, K, sd, codes_ptr,
+                              code_off.ctypes.data, scales_ptr, scale_off.ctypes.data)
+
+
+def mxfp4_rows(seed, tag, i0, R, K, sd):
+    """R consecutive rows of K normals starting at logical index i0, quantised to MXFP4:
+    (codes [R, K/2] uint8, scales [R, K/32] uint8)."""
+    codes = np.zeros((R, K // 2), dtype=np.uint8)
+    scales = np.zeros((R, K // 32), dtype=np.uint8)
+    rows = np.arange(R, dtype=np.uint64) * np.uint64(K) + np.uint64(i0)
+    fill_mxfp4_rows_ptr(seed, tag, rows, K, sd, codes.ctypes.data,
+                        np.arange(R, dtype=np.int64) * (K // 2), scales.ctypes.data,
+                        np.arange(R, dtype=np.int64) * (K // 32))
+    return codes, scales

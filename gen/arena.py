@@ -2,21 +2,43 @@
 
 The entry layout is the library's documented one (include/moe_cache.h):
 [W_gate f x d][W_up f x d][W_down d x f], each row-major, one entry per
-(layer, expert).  This module only places generated values; it computes
-nothing of the layer.
+(layer, expert); for MXFP4 weights, [codes of W_gate][codes of W_up][codes of
+W_down][scales of W_gate][scales of W_up][scales of W_down], each row-major with
+K/2 code bytes and K/32 scale bytes per row of K.  This module only places
+generated values; it computes nothing of the layer.
 """
 import ctypes
 
 import numpy as np
 
-from . import TAG_WG, TAG_WU, TAG_WD, fill_segments_ptr
+from . import TAG_WG, TAG_WU, TAG_WD, MXFP4, fill_segments_ptr, fill_mxfp4_rows_ptr
 from .configs import wg_index, wd_index
+
+
+def _fill_mxfp4_entries(w, pairs, dst_ptr, stride_bytes):
+    d, f = w.d, w.f
+    fd = f * d
+    code_base = {"g": 0, "u": fd // 2, "d": fd}
+    scale_base = {"g": 3 * fd // 2, "u": 3 * fd // 2 + fd // 32, "d": 3 * fd // 2 + 2 * fd // 32}
+    for tag, key, rows, K, index in ((TAG_WG, "g", f, d, wg_index), (TAG_WU, "u", f, d, wg_index),
+                                     (TAG_WD, "d", d, f, wd_index)):
+        row_i0, coff, soff = [], [], []
+        for q, (l, e) in enumerate(pairs):
+            i0 = index(w, l, e)
+            row_i0.append(i0 + np.arange(rows, dtype=np.uint64) * np.uint64(K))
+            coff.append(q * stride_bytes + code_base[key] + np.arange(rows, dtype=np.int64) * (K // 2))
+            soff.append(q * stride_bytes + scale_base[key] + np.arange(rows, dtype=np.int64) * (K // 32))
+        fill_mxfp4_rows_ptr(w.seed, tag, np.concatenate(row_i0), K, w.w_sd, dst_ptr,
+                            np.concatenate(coff), dst_ptr, np.concatenate(soff))
 
 
 def fill_entries_ptr(w, pairs, dst_ptr, entry_stride_elems):
     """Entry q of dst (host address) <- weights of pairs[q] = (layer, expert)."""
     pairs = list(pairs)
     if not pairs:
+        return
+    if w.dtype == MXFP4:
+        _fill_mxfp4_entries(w, pairs, dst_ptr, entry_stride_elems * w.elem)
         return
     fd = w.f * w.d
     base = np.arange(len(pairs), dtype=np.int64) * entry_stride_elems
@@ -29,7 +51,7 @@ def fill_entries_ptr(w, pairs, dst_ptr, entry_stride_elems):
 
 def torch_dtype(w):
     import torch
-    return torch.float32 if w.elem == 4 else torch.bfloat16
+    return torch.float32 if w.elem == 4 else torch.uint8 if w.dtype == MXFP4 else torch.bfloat16
 
 
 def fill_device_entries(w, pairs, arena, slots, chunk=16, staging=None):

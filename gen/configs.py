@@ -10,7 +10,7 @@ import math
 
 import numpy as np
 
-from . import (F32, BF16, TAG_X, TAG_WG, TAG_WU, TAG_WD, TAG_WR, TAG_LOGIT, TAG_RANK,
+from . import (F32, BF16, MXFP4, mxfp4_rows, TAG_X, TAG_WG, TAG_WU, TAG_WD, TAG_WR, TAG_LOGIT, TAG_RANK,
                normal, zipf_bias, routing_logits)
 
 
@@ -23,7 +23,7 @@ class Workload:
     E: int
     k: int
     f: int
-    dtype: int            # F32 or BF16, for x and all weights
+    dtype: int            # F32 or BF16 for x and all weights; MXFP4: bf16 x, MXFP4 weights
     L: int = 1            # layers
     S: int = 0            # cache slots (0 = all experts resident, identity slots)
     alpha: float = 0.2    # Zipf(1.1) bias strength on router logits
@@ -36,11 +36,20 @@ class Workload:
         return 1.0 / math.sqrt(self.d)
 
     @property
+    def act_dtype(self):
+        """Data type of the activations x (MXFP4 applies to the expert weights only)."""
+        return BF16 if self.dtype == MXFP4 else self.dtype
+
+    @property
     def elem(self):
-        return 4 if self.dtype == F32 else 2
+        """Bytes per storage unit of an entry (MXFP4 entries are counted in bytes)."""
+        return 4 if self.dtype == F32 else 1 if self.dtype == MXFP4 else 2
 
     @property
     def entry_elems(self):
+        """Storage units per (layer, expert) entry: 3*d*f weights, or the MXFP4 bytes."""
+        if self.dtype == MXFP4:
+            return 3 * self.d * self.f // 2 + 3 * self.d * self.f // 32
         return 3 * self.d * self.f
 
     @property
@@ -84,12 +93,17 @@ def x_index(w, layer, attempt=0):
 
 
 def gen_x(w, layer=0, attempt=0):
-    return normal(w.seed, TAG_X, x_index(w, layer, attempt), (w.T, w.d), 1.0, w.dtype)
+    return normal(w.seed, TAG_X, x_index(w, layer, attempt), (w.T, w.d), 1.0, w.act_dtype)
 
 
 def gen_expert(w, layer, e, dtype=None):
-    """(W_gate [f,d], W_up [f,d], W_down [d,f]) of one (layer, expert) entry."""
+    """(W_gate [f,d], W_up [f,d], W_down [d,f]) of one (layer, expert) entry.  For MXFP4
+    workloads each matrix is (codes [rows, K/2] uint8, scales [rows, K/32] uint8)."""
     dt = w.dtype if dtype is None else dtype
+    if dt == MXFP4:
+        return (mxfp4_rows(w.seed, TAG_WG, wg_index(w, layer, e), w.f, w.d, w.w_sd),
+                mxfp4_rows(w.seed, TAG_WU, wg_index(w, layer, e), w.f, w.d, w.w_sd),
+                mxfp4_rows(w.seed, TAG_WD, wd_index(w, layer, e), w.d, w.f, w.w_sd))
     wg = normal(w.seed, TAG_WG, wg_index(w, layer, e), (w.f, w.d), w.w_sd, dt)
     wu = normal(w.seed, TAG_WU, wg_index(w, layer, e), (w.f, w.d), w.w_sd, dt)
     wd = normal(w.seed, TAG_WD, wd_index(w, layer, e), (w.d, w.f), w.w_sd, dt)

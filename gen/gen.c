@@ -108,6 +108,75 @@ void gen_fill_normal_segments(uint64_t seed, uint64_t tag, int64_t nseg, const u
   }
 }
 
+/* ---- MXFP4 weights (OCP Microscaling Formats (MX) specification v1.0) ----------------
+ * A block of 32 consecutive elements of a row shares one E8M0 scale X = 2^e (stored as
+ * e + 127); each element is an FP4 E2M1 code (sign bit 3, exponent bits 2:1 with bias 1,
+ * mantissa bit 0), whose magnitudes are 0, 0.5, 1, 1.5, 2, 3, 4, 6.  Conversion of a block
+ * V (the MX spec's rule): e = floor(log2(max |V_i|)) - 2 (2 = the largest E2M1 exponent),
+ * clamped to [-127, 127] (e = -127 for an all-zero block); each element is V_i / X rounded
+ * to nearest on the E2M1 grid, ties to the even code (mantissa bit 0), magnitudes beyond
+ * 6 saturating to 6.  V_i / X is exact (X is a power of two), so every decision is exact.
+ * Storage used by the library: per row of K elements, K/2 code bytes (element 2j in the
+ * low nibble of byte j, element 2j+1 in the high nibble) and K/32 scale bytes.  This is
+ * input preparation (the weights are given in MXFP4); nothing of the layer is computed. */
+static inline uint8_t e2m1_code(float q) {  /* q = V_i / X, |q| < 8 */
+  const float a = fabsf(q);
+  uint8_t c;
+  if (a <= 0.25f) c = 0;
+  else if (a < 0.75f) c = 1;
+  else if (a <= 1.25f) c = 2;
+  else if (a < 1.75f) c = 3;
+  else if (a <= 2.5f) c = 4;
+  else if (a < 3.5f) c = 5;
+  else if (a <= 5.0f) c = 6;
+  else c = 7;
+  return (uint8_t)(c | (q < 0.0f ? 8 : 0));
+}
+
+/* floor(log2(a)) for a finite a > 0 (exact, from the bits). */
+static inline int floor_log2f(float a) {
+  uint32_t u;
+  memcpy(&u, &a, 4);
+  const int ex = (int)((u >> 23) & 0xFF);
+  if (ex != 0) return ex - 127;
+  int k = -127; /* subnormal: 2^-126 * (mantissa / 2^23) */
+  uint32_t m = u & 0x7FFFFF;
+  while (m < 0x400000u) { m <<= 1; --k; }
+  return k;
+}
+
+/* Quantise one block of 32 values: 16 code bytes and one scale byte. */
+void gen_mxfp4_block(const float* v, uint8_t* codes, uint8_t* scale) {
+  float amax = 0.0f;
+  for (int i = 0; i < 32; ++i) amax = fabsf(v[i]) > amax ? fabsf(v[i]) : amax;
+  int e = amax > 0.0f ? floor_log2f(amax) - 2 : -127;
+  if (e < -127) e = -127;
+  if (e > 127) e = 127;
+  *scale = (uint8_t)(e + 127);
+  const float inv = ldexpf(1.0f, -e);
+  for (int j = 0; j < 16; ++j) {
+    const uint8_t lo = e2m1_code(v[2 * j] * inv), hi = e2m1_code(v[2 * j + 1] * inv);
+    codes[j] = (uint8_t)(lo | (hi << 4));
+  }
+}
+
+/* nrows rows of K normals (row r = logical indices [row_i0[r], row_i0[r] + K), sd), each
+ * quantised to MXFP4: codes of row r at codes + code_off[r] (K/2 bytes), scales at
+ * scales + scale_off[r] (K/32 bytes).  K is a multiple of 32. */
+void gen_fill_mxfp4_rows(uint64_t seed, uint64_t tag, int64_t nrows, const uint64_t* row_i0,
+                         int64_t K, float sd, uint8_t* codes, const int64_t* code_off,
+                         uint8_t* scales, const int64_t* scale_off) {
+  const uint64_t key = stream_key(seed, tag);
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < nrows; ++r) {
+    float v[32];
+    for (int64_t b = 0; b < K / 32; ++b) {
+      for (int i = 0; i < 32; ++i) v[i] = normal_from_key(key, row_i0[r] + (uint64_t)(b * 32 + i)) * sd;
+      gen_mxfp4_block(v, codes + code_off[r] + b * 16, scales + scale_off[r] + b);
+    }
+  }
+}
+
 typedef struct {
   uint64_t key;
   int32_t e;

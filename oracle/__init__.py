@@ -85,6 +85,32 @@ def permute(ids, E):
     return counts, offsets, perm, inv
 
 
+# FP4 E2M1 magnitudes by the low three code bits (OCP Microscaling Formats (MX) v1.0, the
+# FP4 element table): exponent bits 2:1 with bias 1, mantissa bit 0, no infinities or NaN.
+_E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def mxfp4_dequant(codes, scales):
+    """Exact values of MXFP4 rows (float64 [R, K]) from codes [R, K/2] and scales [R, K/32].
+
+    OCP MX v1.0: a block of 32 elements shares the scale 2^(s - 127) (E8M0, s = 255 is NaN
+    and not used here); element = (-1)^(code bit 3) * E2M1 magnitude * scale.  Element 2j
+    of a row is the low nibble of code byte j, element 2j + 1 the high nibble (the layout
+    the library documents for MXFP4 entries)."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    scales = np.asarray(scales, dtype=np.uint8)
+    R, half = codes.shape
+    q = np.empty((R, 2 * half), dtype=np.uint8)
+    q[:, 0::2] = codes & 0x0F
+    q[:, 1::2] = codes >> 4
+    if np.any(scales == 255):
+        raise ValueError("E8M0 NaN scale")
+    mag = _E2M1[q & 7]
+    sign = np.where(q & 8, -1.0, 1.0)
+    block = np.ldexp(1.0, scales.astype(np.int64) - 127)
+    return sign * mag * np.repeat(block, 32, axis=1)
+
+
 class ExpertTable:
     """Per-expert weight pointers (keeps the arrays alive).  experts: {e: (wg, wu, wd)}."""
 
