@@ -89,26 +89,29 @@ def _counter_traffic(kernel_srcs, name):
 
 
 # ------------------------------------------------------------------------ decode layer
-def decode_arena(torch):
-    """All 256 experts of the decode layer, resident (shared by every decode measurement)."""
+def decode_arena(torch, dtype=None):
+    """All 256 experts of the decode layer, resident (shared by every decode measurement of
+    one weight format)."""
     from gen import configs
     from gen.arena import device_arena_all_experts
+    w = configs.DECODE if dtype is None else configs.with_(configs.DECODE, dtype=dtype)
     t0 = time.time()
-    arena = device_arena_all_experts(configs.DECODE)
-    log(f"[decode] arena {configs.DECODE.E} x {configs.DECODE.entry_bytes / 1e6:.1f} MB generated "
-        f"in {time.time() - t0:.1f}s")
+    arena = device_arena_all_experts(w)
+    log(f"[decode] arena {w.E} x {w.entry_bytes / 1e6:.1f} MB generated in {time.time() - t0:.1f}s")
     return arena
 
 
-def bench_decode(args, torch, moe, T, alpha, arena):
+def bench_decode(args, torch, moe, T, alpha, arena, dtype=None):
     from gen import configs
     from expert_ffn_cache_amd.layer import MoeLayer
 
     w = configs.with_(configs.DECODE, T=T, alpha=alpha)
+    if dtype is not None:
+        w = configs.with_(w, dtype=dtype)
     R = 16
     x = torch.from_numpy(configs.gen_x(w).view(np.int16)).view(torch.bfloat16).cuda()
     logits = [torch.from_numpy(configs.gen_logits(w, rotation=r)).cuda() for r in range(R)]
-    layers = [MoeLayer(w.T, w.E, w.k, w.d, w.f) for _ in range(R)]
+    layers = [MoeLayer(w.T, w.E, w.k, w.d, w.f, w_dtype=w.dtype) for _ in range(R)]
     s = torch.cuda.Stream()
     graphs = []
     with torch.cuda.stream(s):
@@ -159,7 +162,7 @@ def bench_decode(args, torch, moe, T, alpha, arena):
     ffn_avg_ms = float(np.mean(ffn_ms))
     achieved = float(np.sum(byts) / (np.sum(ffn_ms) * 1e-3) / 1e9)
     traffic = None
-    if T == 8 and alpha == 0.2:  # the configuration the committed counter summary covers
+    if T == 8 and alpha == 0.2 and dtype is None:  # what the committed counter summary covers
         traffic = _counter_traffic(DECODE_FFN_SOURCES, "ffn_dot_decode_e256_k6_d4096_f2048_T8_counters.txt")
     del graphs
     torch.cuda.empty_cache()
@@ -550,6 +553,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true", help="decode at the primary T and alpha only")
+    ap.add_argument("--weights", choices=["bf16", "mxfp4"], default="bf16",
+                    help="expert weight format of the primary decode line (--workload decode)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build has no "
@@ -566,11 +571,13 @@ def main():
     extra = {}
     dec = None
     if wl in ("all", "decode"):
-        arena = decode_arena(torch)
-        dec = bench_decode(args, torch, moe, args.decode_T, args.alpha, arena)
+        import gen
+        wfmt = gen.MXFP4 if args.weights == "mxfp4" else None
+        arena = decode_arena(torch, wfmt)
+        dec = bench_decode(args, torch, moe, args.decode_T, args.alpha, arena, wfmt)
         log(f"[decode] {dec['tok_s']:.0f} tok/s, {dec['ms_per_step'] * 1e3:.1f} us/layer, "
             f"ffn {dec['ffn_ms'] * 1e3:.1f} us, {dec['roofline']['achieved']:.0f} GB/s")
-        if not args.no_sweep:
+        if not args.no_sweep and wfmt is None:
             sweep = {}
             for T, alpha in ((1, 0.2), (64, 0.2), (8, 1.0), (64, 1.0)):
                 r = bench_decode(args, torch, moe, T, alpha, arena)
@@ -582,6 +589,20 @@ def main():
             extra["decode_sweep"] = sweep
         del arena
         torch.cuda.empty_cache()
+        if not args.no_sweep and wfmt is None:
+            # MXFP4 routed experts (the pages' DeepSeek-V4-Flash deployment format)
+            arena = decode_arena(torch, gen.MXFP4)
+            mx = {}
+            for T, alpha in ((8, 0.2), (1, 0.2), (64, 0.2), (8, 1.0)):
+                r = bench_decode(args, torch, moe, T, alpha, arena, gen.MXFP4)
+                mx[f"T{T}_alpha{alpha}"] = dict(
+                    tok_s=r["tok_s"], us_per_layer=r["ms_per_step"] * 1e3, ffn_us=r["ffn_ms"] * 1e3,
+                    unique_experts=r["U_mean"], ffn_gbs=r["roofline"]["achieved"],
+                    hbm_frac=r["roofline"]["frac"])
+                log(f"[decode mxfp4 T={T} alpha={alpha}] {json.dumps(mx[f'T{T}_alpha{alpha}'])}")
+            extra["decode_mxfp4"] = mx
+            del arena
+            torch.cuda.empty_cache()
     if wl in ("all", "prefill"):
         extra["prefill"] = bench_prefill(args, torch, moe)
         log(f"[prefill] {json.dumps(extra['prefill'])}")

@@ -24,6 +24,7 @@ MOE_ERANGE = -5
 
 MOE_F32 = 0
 MOE_BF16 = 1
+MOE_MXFP4 = 2
 
 MOE_PATH_AUTO = 0
 MOE_PATH_GEMV = 1
@@ -31,7 +32,8 @@ MOE_PATH_GEMM = 2
 
 EXPORTS = [
     "moe_strerror", "moe_abi_version", "moe_router_logits", "moe_route",
-    "moe_permute_workspace_bytes", "moe_permute", "moe_expert_ffn_workspace_bytes",
+    "moe_permute_workspace_bytes", "moe_permute", "moe_entry_bytes",
+    "moe_expert_ffn_workspace_bytes",
     "moe_expert_ffn", "moe_combine", "cache_init", "cache_lookup_update",
     "cache_lookup_update_split", "cache_fill",
     "cache_fill_device", "cache_fill_masks", "cache_resize", "layer_stream_prefetch", "moe_hbm_read_probe", "moe_copy_probe",
@@ -78,6 +80,7 @@ def lib():
             "moe_route": ([vp, i32, i32, i32, vp, vp, vp], i32),
             "moe_permute_workspace_bytes": ([i32, i32, i32], sz),
             "moe_permute": ([vp, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp, vp], i32),
+            "moe_entry_bytes": ([i32, i32, i32], sz),
             "moe_expert_ffn_workspace_bytes": ([i32, i32, i32, i32], sz),
             "moe_expert_ffn": ([vp, i32, vp, vp, i32, i32, i32, i32, i32, vp, vp, sz, i32, vp, vp,
                                 i32, vp, sz, vp, i32, i32, vp, vp], i32),
@@ -159,6 +162,10 @@ def moe_permute(topk_ids, T, k, E, counts, offsets, perm, inv, ws, ws_bytes, sta
     _check("moe_permute", lib().moe_permute(_p(topk_ids), T, k, E, _p(counts), _p(offsets),
                                             _p(perm), _p(inv), _p(ws), ws_bytes, _p(status),
                                             _s(stream)))
+
+
+def moe_entry_bytes(d, f, w_dtype):
+    return lib().moe_entry_bytes(d, f, w_dtype)
 
 
 def moe_expert_ffn_workspace_bytes(T, k, f, act_dtype):

@@ -13,6 +13,7 @@ constexpr int kWave = 64;
 constexpr int kMaxE = 1024;
 constexpr int kMaxK = 16;
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -37,6 +38,11 @@ __device__ __forceinline__ u32x4 ldg16(const void* p) { return *(gptr16)p; }
 // 16-byte non-temporal global load (nt): for data streamed once in whole cache lines, such
 // as expert weight rows in the decode path.
 __device__ __forceinline__ u32x4 ldg16_nt(const void* p) { return __builtin_nontemporal_load((gptr16)p); }
+// One byte through the global (not flat) path: a flat load would also count against the
+// LDS counter, so every later LDS wait would wait for it too.
+__device__ __forceinline__ uint32_t ldg_u8(const void* p) {
+  return *(const __attribute__((address_space(1))) uint8_t*)p;
+}
 
 // Compiler-only fence: memory operations are not moved across it.  Placed after
 // prefetch loads so they are issued where written instead of being sunk to their use.

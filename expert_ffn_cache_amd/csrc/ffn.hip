@@ -12,6 +12,8 @@
 //    1 KB row loads (ffn_dot.hip), above that with MFMA (ffn_gemv.hip).
 //  * GEMM (bf16, prefill-shaped counts): LDS-tiled grouped GEMM with direct global->LDS
 //    loads and persistent XCD-aware workgroups, ffn_gemm.hip.
+//  * MXFP4 weights (bf16 activations): codes expanded to bf16 in registers and multiplied
+//    on the matrix cores against staged token rows (ffn_mx.hip).
 // Both bf16 paths fuse SiLU(g)*u into the gate/up epilogue and write h once as bf16.
 #include <algorithm>
 
@@ -66,6 +68,17 @@ __global__ __launch_bounds__(64) void f32_down(FfnArgs p) {
 
 }  // namespace
 
+extern "C" size_t moe_entry_bytes(int d, int f, int w_dtype) {
+  if (d <= 0 || f <= 0) return 0;
+  const size_t fd = (size_t)d * f;
+  switch (w_dtype) {
+    case MOE_F32: return 3 * fd * 4;
+    case MOE_BF16: return 3 * fd * 2;
+    case MOE_MXFP4: return 3 * fd / 2 + 3 * (fd / 32);
+    default: return 0;
+  }
+}
+
 extern "C" size_t moe_expert_ffn_workspace_bytes(int T, int k, int f, int act_dtype) {
   if (T <= 0 || k <= 0 || f <= 0) return 256;
   const size_t el = act_dtype == MOE_F32 ? 4 : 2;
@@ -82,16 +95,17 @@ extern "C" int moe_expert_ffn(const void* x, int act_dtype, const int32_t* perm,
   if (d <= 0 || f <= 0 || d % 64 != 0 || f % 64 != 0) return MOE_EINVAL;
   if ((long long)T * k >= (1ll << 31)) return MOE_EINVAL;
   if (path < MOE_PATH_AUTO || path > MOE_PATH_GEMM) return MOE_EINVAL;
-  const bool f32 = w_dtype == MOE_F32;
+  const bool f32 = w_dtype == MOE_F32, mx = w_dtype == MOE_MXFP4;
   if (f32) {
     if (act_dtype != MOE_F32 || y_dtype != MOE_F32) return MOE_EUNSUPPORTED;
-  } else if (w_dtype == MOE_BF16) {
+  } else if (w_dtype == MOE_BF16 || mx) {
     if (act_dtype != MOE_BF16 || (y_dtype != MOE_F32 && y_dtype != MOE_BF16)) return MOE_EUNSUPPORTED;
   } else {
     return MOE_EUNSUPPORTED;
   }
-  const size_t el = f32 ? 4 : 2;
-  if (entry_stride < 3 * (size_t)d * f * el || entry_stride % 16 != 0) return MOE_EINVAL;
+  if (mx && (path == MOE_PATH_GEMM || !ffn_mx_supported(d, f))) return MOE_EUNSUPPORTED;
+  const size_t need = mx ? moe_entry_bytes(d, f, w_dtype) : 3 * (size_t)d * f * (f32 ? 4 : 2);
+  if (entry_stride < need || entry_stride % 16 != 0) return MOE_EINVAL;
   if (T == 0) return MOE_OK;
   if (!x || !perm || !offsets || !arena || !ws || !y_perm) return MOE_EINVAL;
   if (!moe_aligned16(x) || !moe_aligned16(arena) || !moe_aligned16(ws) || !moe_aligned16(y_perm))
@@ -107,6 +121,7 @@ extern "C" int moe_expert_ffn(const void* x, int act_dtype, const int32_t* perm,
     MOE_LAUNCH_CHECK();
     return MOE_OK;
   }
+  if (mx) return launch_ffn_mx(p, y_dtype, stream, std::min(E, T * k));
   if (path == MOE_PATH_AUTO) path = (long long)T * k <= 8ll * E ? MOE_PATH_GEMV : MOE_PATH_GEMM;
   if (path == MOE_PATH_GEMM) return launch_ffn_gemm(p, y_dtype, stream);
   const int A = T * k, experts = std::min(E, A);

@@ -60,7 +60,6 @@ __device__ __forceinline__ int nth_active_expert(const FfnArgs& p, int a) {
   return -1;
 }
 
-
 // Launchers (argument checks are done by moe_expert_ffn).  Each returns MOE_OK or MOE_EHIP.
 // `experts`: grid size in experts (an upper bound on the experts the row filter admits);
 // `parts`: 1 = gate/up kernel, 2 = down kernel, 3 = both.
@@ -68,6 +67,9 @@ int launch_ffn_gemv(const FfnArgs& p, int T, int y_dtype, hipStream_t stream, in
                     int parts);
 int launch_ffn_dot(const FfnArgs& p, int y_dtype, hipStream_t stream, int experts, int parts);
 bool ffn_dot_supported(int d, int f);  // row lengths the dot-product path handles
+// MXFP4 weights (codes expanded in registers, products on the matrix cores)
+int launch_ffn_mx(const FfnArgs& p, int y_dtype, hipStream_t stream, int experts);
+bool ffn_mx_supported(int d, int f);
 int launch_ffn_gemm(const FfnArgs& p, int y_dtype, hipStream_t stream);
 
 }  // namespace moe

@@ -24,8 +24,6 @@ constexpr int kDotNTL = 2;  // token rows staged in LDS at a time
 constexpr int kDotUPW = 2;  // weight rows (units / output channels) per wave
 constexpr int kDotUPB = 4 * kDotUPW;
 
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
 // acc + a . b over 8 bf16 pairs.  The pairs are taken with shufflevector: built instead by
 // bit-casting the 32-bit words of a u32x4, the chained builtin was compiled with the first
 // word's registers for every step on this toolchain.

@@ -16,9 +16,12 @@ def _tdtype(code):
 
 
 class MoeLayer:
-    def __init__(self, T, E, k, d, f, dtype=MOE_BF16, y_dtype=MOE_F32, device="cuda"):
+    def __init__(self, T, E, k, d, f, dtype=MOE_BF16, y_dtype=MOE_F32, device="cuda",
+                 w_dtype=None):
+        """dtype: activations (and weights unless w_dtype is given, e.g. MOE_MXFP4)."""
         self.T, self.E, self.k, self.d, self.f = T, E, k, d, f
         self.dtype, self.y_dtype = dtype, y_dtype
+        self.w_dtype = dtype if w_dtype is None else w_dtype
         A = T * k
         dev = torch.device(device)
         i32 = dict(dtype=torch.int32, device=dev)
@@ -46,7 +49,7 @@ class MoeLayer:
     def ffn(self, x, arena, entry_stride, expert_slot=None, mask=None, slot_key=None, key_base=0,
             path=MOE_PATH_AUTO, stream=None):
         moe_expert_ffn(x, self.dtype, self.perm, self.offsets, self.T, self.k, self.E, self.d,
-                       self.f, expert_slot, arena, entry_stride, self.dtype, mask, slot_key,
+                       self.f, expert_slot, arena, entry_stride, self.w_dtype, mask, slot_key,
                        key_base, self.ffn_ws, self.ffn_ws_bytes, self.y_perm, self.y_dtype, path,
                        self.status, stream)
 

@@ -58,6 +58,8 @@ def lib():
         L.gen_mxfp4_block.restype = None
         L.gen_fill_mxfp4_rows.argtypes = [u64, u64, i64, vp, i64, fl, vp, vp, vp, vp]
         L.gen_fill_mxfp4_rows.restype = None
+        L.gen_fill_mxfp4_tiled.argtypes = [u64, u64, i64, vp, i64, i64, fl, vp, vp, vp, vp]
+        L.gen_fill_mxfp4_tiled.restype = None
         L.gen_rank_perm.argtypes = [u64, u64, i32, vp]
         L.gen_rank_perm.restype = None
         L.gen_zipf_bias.argtypes = [u64, u64, i32, db, db, vp]
@@ -151,6 +153,17 @@ def fill_mxfp4_rows_ptr(seed, tag, row_i0, K, sd, codes_ptr, code_off, scales_pt
     scale_off = np.ascontiguousarray(scale_off, dtype=np.int64)
     lib().gen_fill_mxfp4_rows(seed, tag, len(row_i0), row_i0.ctypes.data, K, sd, codes_ptr,
                               code_off.ctypes.data, scales_ptr, scale_off.ctypes.data)
+
+
+def fill_mxfp4_tiled_ptr(seed, tag, i0, R, K, sd, codes_ptr, code_base, scales_ptr, scale_base):
+    """Matrices q of R x K normals (logical start i0[q]) quantised to MXFP4 in the library's
+    tiled entry layout (see gen/gen.c), at byte offsets code_base[q] / scale_base[q]."""
+    i0 = np.ascontiguousarray(i0, dtype=np.uint64)
+    code_base = np.ascontiguousarray(code_base, dtype=np.int64)
+    scale_base = np.ascontiguousarray(scale_base, dtype=np.int64)
+    assert R % 16 == 0 and K % 32 == 0
+    lib().gen_fill_mxfp4_tiled(seed, tag, len(i0), i0.ctypes.data, R, K, sd, codes_ptr,
+                               code_base.ctypes.data, scales_ptr, scale_base.ctypes.data)
 
 
 def mxfp4_rows(seed, tag, i0, R, K, sd):

@@ -3,15 +3,15 @@
 The entry layout is the library's documented one (include/moe_cache.h):
 [W_gate f x d][W_up f x d][W_down d x f], each row-major, one entry per
 (layer, expert); for MXFP4 weights, [codes of W_gate][codes of W_up][codes of
-W_down][scales of W_gate][scales of W_up][scales of W_down], each row-major with
-K/2 code bytes and K/32 scale bytes per row of K.  This module only places
-generated values; it computes nothing of the layer.
+W_down][scales of W_gate][scales of W_up][scales of W_down], each matrix in tiles
+of 16 rows x 128 elements (gen/gen.c gives the byte offsets).  This module only
+places generated values; it computes nothing of the layer.
 """
 import ctypes
 
 import numpy as np
 
-from . import TAG_WG, TAG_WU, TAG_WD, MXFP4, fill_segments_ptr, fill_mxfp4_rows_ptr
+from . import TAG_WG, TAG_WU, TAG_WD, MXFP4, fill_segments_ptr, fill_mxfp4_tiled_ptr
 from .configs import wg_index, wd_index
 
 
@@ -20,16 +20,12 @@ def _fill_mxfp4_entries(w, pairs, dst_ptr, stride_bytes):
     fd = f * d
     code_base = {"g": 0, "u": fd // 2, "d": fd}
     scale_base = {"g": 3 * fd // 2, "u": 3 * fd // 2 + fd // 32, "d": 3 * fd // 2 + 2 * fd // 32}
+    base = np.arange(len(pairs), dtype=np.int64) * stride_bytes
     for tag, key, rows, K, index in ((TAG_WG, "g", f, d, wg_index), (TAG_WU, "u", f, d, wg_index),
                                      (TAG_WD, "d", d, f, wd_index)):
-        row_i0, coff, soff = [], [], []
-        for q, (l, e) in enumerate(pairs):
-            i0 = index(w, l, e)
-            row_i0.append(i0 + np.arange(rows, dtype=np.uint64) * np.uint64(K))
-            coff.append(q * stride_bytes + code_base[key] + np.arange(rows, dtype=np.int64) * (K // 2))
-            soff.append(q * stride_bytes + scale_base[key] + np.arange(rows, dtype=np.int64) * (K // 32))
-        fill_mxfp4_rows_ptr(w.seed, tag, np.concatenate(row_i0), K, w.w_sd, dst_ptr,
-                            np.concatenate(coff), dst_ptr, np.concatenate(soff))
+        i0 = np.array([index(w, l, e) for l, e in pairs], dtype=np.uint64)
+        fill_mxfp4_tiled_ptr(w.seed, tag, i0, rows, K, w.w_sd, dst_ptr, base + code_base[key],
+                             dst_ptr, base + scale_base[key])
 
 
 def fill_entries_ptr(w, pairs, dst_ptr, entry_stride_elems):

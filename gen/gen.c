@@ -116,9 +116,9 @@ void gen_fill_normal_segments(uint64_t seed, uint64_t tag, int64_t nseg, const u
  * clamped to [-127, 127] (e = -127 for an all-zero block); each element is V_i / X rounded
  * to nearest on the E2M1 grid, ties to the even code (mantissa bit 0), magnitudes beyond
  * 6 saturating to 6.  V_i / X is exact (X is a power of two), so every decision is exact.
- * Storage used by the library: per row of K elements, K/2 code bytes (element 2j in the
- * low nibble of byte j, element 2j+1 in the high nibble) and K/32 scale bytes.  This is
- * input preparation (the weights are given in MXFP4); nothing of the layer is computed. */
+ * A block's 16 code bytes hold element 2j in the low nibble of byte j and element 2j+1 in
+ * the high nibble.  This is input preparation (the weights are given in MXFP4); nothing of
+ * the layer is computed. */
 static inline uint8_t e2m1_code(float q) {  /* q = V_i / X, |q| < 8 */
   const float a = fabsf(q);
   uint8_t c;
@@ -173,6 +173,39 @@ void gen_fill_mxfp4_rows(uint64_t seed, uint64_t tag, int64_t nrows, const uint6
     for (int64_t b = 0; b < K / 32; ++b) {
       for (int i = 0; i < 32; ++i) v[i] = normal_from_key(key, row_i0[r] + (uint64_t)(b * 32 + i)) * sd;
       gen_mxfp4_block(v, codes + code_off[r] + b * 16, scales + scale_off[r] + b);
+    }
+  }
+}
+
+/* Byte offsets of block b (elements 32b .. 32b+31) of row r of an R x K MXFP4 matrix in the
+ * library's tiled entry layout: tiles of 16 rows x 128 elements, row strips one after the
+ * other and, inside a strip, tiles in k order (the last tile of a strip holds what is left
+ * of K); inside a tile, the 16 code bytes of (row i, block q of the tile) sit at slot
+ * 16 q + i, and its scale byte at the same slot of the strip's scale tile. */
+static inline int64_t mx_code_off(int64_t r, int64_t b, int64_t K) {
+  return (r / 16) * 8 * K + (b / 4) * 1024 + (16 * (b % 4) + r % 16) * 16;
+}
+static inline int64_t mx_scale_off(int64_t r, int64_t b, int64_t K) {
+  return (r / 16) * (K / 2) + (b / 4) * 64 + 16 * (b % 4) + r % 16;
+}
+
+/* nmat matrices of R x K normals (matrix q: element (r, c) = logical index i0[q] + r K + c,
+ * sd) quantised to MXFP4 into the tiled layout: codes at codes + code_base[q], scales at
+ * scales + scale_base[q].  R is a multiple of 16 and K of 32. */
+void gen_fill_mxfp4_tiled(uint64_t seed, uint64_t tag, int64_t nmat, const uint64_t* i0,
+                          int64_t R, int64_t K, float sd, uint8_t* codes,
+                          const int64_t* code_base, uint8_t* scales, const int64_t* scale_base) {
+  const uint64_t key = stream_key(seed, tag);
+#pragma omp parallel for schedule(static)
+  for (int64_t qr = 0; qr < nmat * R; ++qr) {
+    const int64_t q = qr / R, r = qr % R;
+    float v[32];
+    uint8_t blk[16];
+    for (int64_t b = 0; b < K / 32; ++b) {
+      for (int i = 0; i < 32; ++i)
+        v[i] = normal_from_key(key, i0[q] + (uint64_t)(r * K + b * 32 + i)) * sd;
+      gen_mxfp4_block(v, blk, scales + scale_base[q] + mx_scale_off(r, b, K));
+      memcpy(codes + code_base[q] + mx_code_off(r, b, K), blk, 16);
     }
   }
 }

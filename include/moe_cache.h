@@ -60,8 +60,9 @@ extern "C" {
 #define MOE_ECAPACITY (-4)    /* more unique experts requested than cache slots */
 #define MOE_ERANGE (-5)       /* id, layer or slot out of range; stale cache slot */
 
-#define MOE_F32 0  /* IEEE binary32 */
-#define MOE_BF16 1 /* bfloat16 (upper half of binary32) */
+#define MOE_F32 0   /* IEEE binary32 */
+#define MOE_BF16 1  /* bfloat16 (upper half of binary32) */
+#define MOE_MXFP4 2 /* expert weights only: OCP MX FP4, see moe_entry_bytes */
 
 /* Static text for a status code. */
 const char* moe_strerror(int status);
@@ -115,6 +116,27 @@ int moe_permute(const int32_t* topk_ids, int T, int k, int E, int32_t* counts, i
  * 16).  The same layout is used by the host pool, the device cache arena and
  * the streaming buffers, so a fill is one contiguous copy. */
 
+/* Bytes of one (layer, expert) entry with weights in w_dtype (0 for an unknown type).
+ * MOE_F32 / MOE_BF16: 3*d*f elements, [W_gate f x d][W_up f x d][W_down d x f].
+ * MOE_MXFP4 (the pages deploy DeepSeek-V4-Flash routed experts in MXFP4:
+ * benchmark page, "FreeToken benchmark results", model table; format: OCP
+ * Microscaling Formats (MX) v1.0): every row of K contraction elements is K/32
+ * blocks of 32 FP4 E2M1 codes sharing one E8M0 scale 2^(s - 127); a block's 16
+ * code bytes hold element 2j in the low nibble of byte j, element 2j+1 in the
+ * high nibble.  Entry bytes:
+ *   [codes W_gate][codes W_up][codes W_down][scales W_gate][scales W_up][scales W_down]
+ * with f*d/2 code bytes and f*d/32 scale bytes per matrix, = 3*d*f*17/32 in all
+ * (13.4 MB at d=4096, f=2048, vs 50.3 MB in bf16).  Each R x K matrix is stored
+ * in tiles of 16 rows x 128 elements, so that one 1 KB read is one tile: rows
+ * 16*rt .. 16*rt+15 start at byte 8*K*rt of the matrix's codes (K/2*rt of its
+ * scales); tile kt of that strip at +1024*kt (+64*kt), the strip's last tile
+ * holding the K mod 128 elements left when K is not a multiple of 128; inside a
+ * tile, slot l = 16*q + i (16 code bytes at 16*l, the scale byte at l) is row i
+ * of the strip, elements 32*q .. 32*q+31 of the tile.  So block b of row r has
+ * its codes at 8*K*(r/16) + 1024*(b/4) + 16*(16*(b%4) + r%16) and its scale at
+ * K/2*(r/16) + 64*(b/4) + 16*(b%4) + r%16. */
+size_t moe_entry_bytes(int d, int f, int w_dtype);
+
 /* Workspace bytes moe_expert_ffn needs (the SwiGLU intermediate, [T*k][f]). */
 size_t moe_expert_ffn_workspace_bytes(int T, int k, int f, int act_dtype);
 
@@ -133,7 +155,11 @@ size_t moe_expert_ffn_workspace_bytes(int T, int k, int f, int act_dtype);
  *  (expert_slot NULL = identity slots); y_perm [T*k][d] in y_dtype.
  *  MOE_F32 weights need MOE_F32 activations and y (fp32 arithmetic end to
  *  end); MOE_BF16 weights need MOE_BF16 activations, y fp32 or bf16, and
- *  round h to bf16 before the down projection.
+ *  round h to bf16 before the down projection.  MOE_MXFP4 weights (entry
+ *  layout under moe_entry_bytes) need MOE_BF16 activations; each weight is its
+ *  exact value (E2M1 value x block scale), the rest as for MOE_BF16.  MXFP4 runs
+ *  on the weight-streaming path only (MOE_PATH_GEMM returns MOE_EUNSUPPORTED);
+ *  d, f <= 8128.
  *  slot_key (nullable, device, [S]): when given, a slot whose key is not
  *  key_base + e, or a negative slot, sets *status = MOE_ERANGE and that
  *  expert's rows are not written (stale-cache detection).

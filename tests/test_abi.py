@@ -35,6 +35,13 @@ def test_strerror_and_version():
     assert moe.abi_version() == 1
 
 
+def test_entry_bytes():
+    assert moe.moe_entry_bytes(4096, 2048, moe.MOE_MXFP4) == 3 * 4096 * 2048 * 17 // 32
+    assert moe.moe_entry_bytes(4096, 2048, moe.MOE_BF16) == 3 * 4096 * 2048 * 2
+    assert moe.moe_entry_bytes(256, 512, moe.MOE_F32) == 3 * 256 * 512 * 4
+    assert moe.moe_entry_bytes(64, 64, 9) == 0
+
+
 def test_workspace_sizes():
     assert moe.moe_permute_workspace_bytes(8192, 6, 256) >= 48 * 256 * 4
     assert moe.moe_permute_workspace_bytes(8192, 6, 256) % 256 == 0

@@ -126,14 +126,15 @@ def _ffn_case(w, path, ydt=moe.MOE_F32):
     counts, offsets, perm, inv = oracle.permute(ids, w.E)
     arena = device_arena_all_experts(w)
     A = w.T * w.k
-    nws = moe.moe_expert_ffn_workspace_bytes(w.T, w.k, w.f, w.dtype)
+    nws = moe.moe_expert_ffn_workspace_bytes(w.T, w.k, w.f, w.act_dtype)
     ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
     ytd = torch.float32 if ydt == moe.MOE_F32 else torch.bfloat16
     y = torch.full((A, w.d), float("nan"), dtype=ytd, device="cuda")
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
-    moe.moe_expert_ffn(x_device(w, x), w.dtype, dev(perm), dev(offsets), w.T, w.k, w.E, w.d, w.f,
-                       None, arena, w.entry_bytes, w.dtype, None, None, 0, ws, nws, y, ydt, path,
-                       status)
+    assert w.entry_bytes == moe.moe_entry_bytes(w.d, w.f, w.dtype)
+    moe.moe_expert_ffn(x_device(w, x), w.act_dtype, dev(perm), dev(offsets), w.T, w.k, w.E, w.d,
+                       w.f, None, arena, w.entry_bytes, w.dtype, None, None, 0, ws, nws, y, ydt,
+                       path, status)
     torch.cuda.synchronize()
     assert int(status.item()) == 0
     table = oracle_table(w, sorted(set(ids.ravel().tolist())))
@@ -179,6 +180,29 @@ def test_ffn_decode_dot_and_mfma_split(T, E, k, d, f, ydt):
     w = configs.Workload("dot_split", seed=23, T=T, d=d, E=E, k=k, f=f, dtype=gen.BF16, alpha=0.5)
     y, ref = _ffn_case(w, moe.MOE_PATH_GEMV, ydt)
     assert_close(y, ref, bf16_tol(ref), f"y_perm T={T} E={E} d={d} f={f}")
+
+
+@pytest.mark.parametrize("T,E,k,d,f", [(8, 16, 6, 512, 256), (1, 8, 4, 4096, 2048), (8, 4, 2, 320, 192),
+                                       (40, 6, 3, 1088, 448), (5, 64, 6, 2048, 4096),
+                                       (32, 128, 8, 1088, 576)])
+@pytest.mark.parametrize("ydt", [moe.MOE_F32, moe.MOE_BF16])
+def test_ffn_mxfp4_parity(T, E, k, d, f, ydt):
+    """MXFP4 expert weights (OCP MX: E2M1 codes, E8M0 scale per 32) against the oracle on the
+    exactly dequantised weights: decode shapes, row lengths that leave a short last tile,
+    experts with many rows (several staging passes), the full decode row lengths; strips
+    streamed by one wave (many experts) and split over 2 or 4 waves (few experts)."""
+    w = configs.Workload("mx", seed=25, T=T, d=d, E=E, k=k, f=f, dtype=gen.MXFP4, alpha=0.5)
+    y, ref = _ffn_case(w, moe.MOE_PATH_AUTO, ydt)
+    assert_close(y, ref, bf16_tol(ref), f"y_perm mxfp4 T={T} d={d} f={f}")
+
+
+def test_ffn_mxfp4_rejects_gemm_path_and_short_entries():
+    w = configs.Workload("mx_bad", seed=26, T=4, d=256, E=4, k=2, f=128, dtype=gen.MXFP4)
+    with pytest.raises(moe.MoeError) as ei:
+        _ffn_case(w, moe.MOE_PATH_GEMM)
+    assert ei.value.status == moe.MOE_EUNSUPPORTED
+    assert moe.moe_entry_bytes(4096, 2048, moe.MOE_MXFP4) == 3 * 4096 * 2048 * 17 // 32
+    assert moe.moe_entry_bytes(4096, 2048, moe.MOE_BF16) == 3 * 4096 * 2048 * 2
 
 
 def test_ffn_gemm_wide_n_tiles():

@@ -77,3 +77,30 @@ def test_random_blocks_round_to_a_nearest_grid_value():
 def test_all_zero_block():
     codes, s = gen.mxfp4_block(np.zeros(32, dtype=np.float32))
     assert s == 0 and np.all(codes == 0)
+
+
+def test_tiled_entry_layout():
+    """An MXFP4 entry written for the library holds every block of every matrix where the
+    documented tiled layout puts it (16-row x 128-element tiles; strips whose last tile is
+    short when K is not a multiple of 128), and nothing else: each byte is written once."""
+    from gen import configs
+    from gen.arena import fill_entries_ptr
+    for d, f in ((320, 192), (256, 128)):
+        w = configs.Workload("mx_layout", seed=31, T=1, d=d, E=2, k=1, f=f, dtype=gen.MXFP4)
+        nbytes = w.entry_elems
+        buf = np.full(nbytes, 0xA5, dtype=np.uint8)
+        fill_entries_ptr(w, [(0, 1)], buf.ctypes.data, nbytes)
+        fd = f * d
+        seen = np.zeros(nbytes, dtype=np.int64)
+        mats = configs.gen_expert(w, 0, 1)
+        for mi, ((codes, scales), (R, K)) in enumerate(zip(mats, ((f, d), (f, d), (d, f)))):
+            cbase, sbase = mi * fd // 2, 3 * fd // 2 + mi * fd // 32
+            for r in range(R):
+                for b in range(K // 32):
+                    co = cbase + 8 * K * (r // 16) + 1024 * (b // 4) + 16 * (16 * (b % 4) + r % 16)
+                    so = sbase + K // 2 * (r // 16) + 64 * (b // 4) + 16 * (b % 4) + r % 16
+                    assert np.array_equal(buf[co:co + 16], codes[r, 16 * b:16 * b + 16]), (mi, r, b)
+                    assert buf[so] == scales[r, b], (mi, r, b)
+                    seen[co:co + 16] += 1
+                    seen[so] += 1
+        assert np.all(seen == 1)
