@@ -60,6 +60,8 @@ CSRC = os.path.join(ROOT, "expert_ffn_cache_amd", "csrc")
 # sources of the decode expert-FFN call (dispatch + dot-product kernels), which the committed
 # counter summary was taken on
 DECODE_FFN_SOURCES = [os.path.join(CSRC, n) for n in ("common.h", "ffn_args.h", "ffn.hip", "ffn_dot.hip")]
+# the same for MXFP4 weights (dispatch + FP4-expanding MFMA kernels)
+MXFP4_FFN_SOURCES = [os.path.join(CSRC, n) for n in ("common.h", "ffn_args.h", "ffn.hip", "ffn_mx.hip")]
 
 
 def sources_sha256(paths):
@@ -102,6 +104,7 @@ def decode_arena(torch, dtype=None):
 
 
 def bench_decode(args, torch, moe, T, alpha, arena, dtype=None):
+    import gen
     from gen import configs
     from expert_ffn_cache_amd.layer import MoeLayer
 
@@ -162,8 +165,11 @@ def bench_decode(args, torch, moe, T, alpha, arena, dtype=None):
     ffn_avg_ms = float(np.mean(ffn_ms))
     achieved = float(np.sum(byts) / (np.sum(ffn_ms) * 1e-3) / 1e9)
     traffic = None
-    if T == 8 and alpha == 0.2 and dtype is None:  # what the committed counter summary covers
-        traffic = _counter_traffic(DECODE_FFN_SOURCES, "ffn_dot_decode_e256_k6_d4096_f2048_T8_counters.txt")
+    if T == 8 and alpha == 0.2:  # what the committed counter summaries cover
+        if dtype is None:
+            traffic = _counter_traffic(DECODE_FFN_SOURCES, "ffn_dot_decode_e256_k6_d4096_f2048_T8_counters.txt")
+        elif dtype == gen.MXFP4:
+            traffic = _counter_traffic(MXFP4_FFN_SOURCES, "ffn_mx_decode_e256_k6_d4096_f2048_T8_counters.txt")
     del graphs
     torch.cuda.empty_cache()
     return dict(
