@@ -182,14 +182,14 @@ def bench_decode(args, torch, moe, T, alpha, arena, dtype=None):
 
 
 # ------------------------------------------------------------------------ prefill layer
-def bench_prefill(args, torch, moe):
+def bench_prefill(args, torch, moe, dtype=None):
     from gen import configs
     from gen.arena import device_arena_all_experts
     from expert_ffn_cache_amd.layer import MoeLayer
 
     out = {}
     t0 = time.time()
-    base = configs.PREFILL
+    base = configs.PREFILL if dtype is None else configs.with_(configs.PREFILL, dtype=dtype)
     arena = device_arena_all_experts(base)
     log(f"[prefill] arena generated in {time.time() - t0:.1f}s")
     x = torch.from_numpy(configs.gen_x(base).view(np.int16)).view(torch.bfloat16).cuda()
@@ -197,7 +197,8 @@ def bench_prefill(args, torch, moe):
         w = configs.with_(base, alpha=alpha)
         R = 2
         logits = [torch.from_numpy(configs.gen_logits(w, rotation=r)).cuda() for r in range(R)]
-        layers = [MoeLayer(w.T, w.E, w.k, w.d, w.f, y_dtype=moe.MOE_BF16) for _ in range(R)]
+        layers = [MoeLayer(w.T, w.E, w.k, w.d, w.f, y_dtype=moe.MOE_BF16, w_dtype=w.dtype)
+                  for _ in range(R)]
         s = torch.cuda.Stream()
         steps = max(4, args.steps // 5)
         with torch.cuda.stream(s):
@@ -612,6 +613,10 @@ def main():
     if wl in ("all", "prefill"):
         extra["prefill"] = bench_prefill(args, torch, moe)
         log(f"[prefill] {json.dumps(extra['prefill'])}")
+        if not args.no_sweep or args.weights == "mxfp4":
+            import gen
+            extra["prefill_mxfp4"] = bench_prefill(args, torch, moe, gen.MXFP4)
+            log(f"[prefill mxfp4] {json.dumps(extra['prefill_mxfp4'])}")
     if wl in ("all", "stream"):
         extra["stream_prefill"] = bench_stream(args, torch, moe)
         log(f"[stream] {json.dumps(extra['stream_prefill'])}")

@@ -13,7 +13,8 @@
 //  * GEMM (bf16, prefill-shaped counts): LDS-tiled grouped GEMM with direct global->LDS
 //    loads and persistent XCD-aware workgroups, ffn_gemm.hip.
 //  * MXFP4 weights (bf16 activations): codes expanded to bf16 in registers and multiplied
-//    on the matrix cores against staged token rows (ffn_mx.hip).
+//    on the matrix cores against staged token rows: weight streaming for decode-shaped
+//    counts (ffn_mx.hip), a grouped GEMM for prefill-shaped ones (ffn_mx_gemm.hip).
 // Both bf16 paths fuse SiLU(g)*u into the gate/up epilogue and write h once as bf16.
 #include <algorithm>
 
@@ -103,7 +104,6 @@ extern "C" int moe_expert_ffn(const void* x, int act_dtype, const int32_t* perm,
   } else {
     return MOE_EUNSUPPORTED;
   }
-  if (mx && (path == MOE_PATH_GEMM || !ffn_mx_supported(d, f))) return MOE_EUNSUPPORTED;
   const size_t need = mx ? moe_entry_bytes(d, f, w_dtype) : 3 * (size_t)d * f * (f32 ? 4 : 2);
   if (entry_stride < need || entry_stride % 16 != 0) return MOE_EINVAL;
   if (T == 0) return MOE_OK;
@@ -121,7 +121,11 @@ extern "C" int moe_expert_ffn(const void* x, int act_dtype, const int32_t* perm,
     MOE_LAUNCH_CHECK();
     return MOE_OK;
   }
-  if (mx) return launch_ffn_mx(p, y_dtype, stream, std::min(E, T * k));
+  if (mx) {
+    const bool gemm = path == MOE_PATH_GEMM || (path == MOE_PATH_AUTO && (long long)T * k > 8ll * E) ||
+                      !ffn_mx_supported(d, f);
+    return gemm ? launch_ffn_mx_gemm(p, T, y_dtype, stream) : launch_ffn_mx(p, y_dtype, stream, std::min(E, T * k));
+  }
   if (path == MOE_PATH_AUTO) path = (long long)T * k <= 8ll * E ? MOE_PATH_GEMV : MOE_PATH_GEMM;
   if (path == MOE_PATH_GEMM) return launch_ffn_gemm(p, y_dtype, stream);
   const int A = T * k, experts = std::min(E, A);

@@ -69,7 +69,8 @@ int launch_ffn_dot(const FfnArgs& p, int y_dtype, hipStream_t stream, int expert
 bool ffn_dot_supported(int d, int f);  // row lengths the dot-product path handles
 // MXFP4 weights (codes expanded in registers, products on the matrix cores)
 int launch_ffn_mx(const FfnArgs& p, int y_dtype, hipStream_t stream, int experts);
-bool ffn_mx_supported(int d, int f);
+bool ffn_mx_supported(int d, int f);  // shapes the weight-streaming MXFP4 kernels handle
+int launch_ffn_mx_gemm(const FfnArgs& p, int T, int y_dtype, hipStream_t stream);
 int launch_ffn_gemm(const FfnArgs& p, int y_dtype, hipStream_t stream);
 
 }  // namespace moe

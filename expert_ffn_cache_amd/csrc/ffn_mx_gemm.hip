@@ -1,0 +1,315 @@
+// Prefill-shaped expert FFN with MXFP4 expert weights: a grouped GEMM over the experts' token
+// rows.  The activations stay bf16, so the products run on v_mfma_f32_16x16x32_bf16 with
+// the FP4 codes expanded to bf16 in registers (v_cvt_scalef32_pk_bf16_fp4, exact for E8M0
+// scales): the same arithmetic as the decode kernels, with the weights of an expert reused
+// across 64 token rows per workgroup instead of streamed once per token group.
+//
+// Tile: a workgroup computes 64 token rows of one expert x 128 weight rows (4 waves, each 2
+// strips of 16 rows), stepping over K one 128-element tile column at a time.  The entry's
+// tiled layout (16 rows x 128 elements per tile, slot l = 16 q + i = row i, block q) means
+// a wave's 16-byte loads of one tile column are contiguous and each lane then holds its
+// MFMA B operands for four k-groups (as in the decode kernels).  The token rows of the
+// current tile column sit in LDS (double-buffered, rows padded by 16 bytes so a 16-row
+// operand read hits 16 distinct bank groups); the next column's rows and weight codes are
+// loaded into registers while the current one is multiplied.  Rows past an expert's count
+// read row 0 of the block and their outputs are dropped; elements past K stage as zero.
+//
+// Work list: workgroup -> (expert, 64-row block) in expert order, found on the device from
+// the offsets (one wave scans the experts' block counts), x 128-row weight block; blocks
+// are dealt XCD-major so the workgroups sharing an expert's token rows share an L2.
+#include <algorithm>
+
+#include "ffn_args.h"
+
+namespace moe {
+namespace {
+
+constexpr int kMgM = 64;             // token rows per workgroup
+constexpr int kMgS = 2;              // 16-row strips per wave
+constexpr int kMgN = 4 * 16 * kMgS;  // weight rows per workgroup
+constexpr int kMgLd = 128 + 8;       // LDS row stride (bf16) of a staged tile column
+
+__device__ __forceinline__ float mg_e8m0(uint32_t s) {
+  return s ? __uint_as_float(s << 23) : __uint_as_float(0x00400000u);  // 2^(s - 127)
+}
+
+__device__ __forceinline__ bf16x8 mg_expand8(uint32_t w, float sc) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3);
+  return __builtin_shufflevector(__builtin_shufflevector(a, b, 0, 1, 2, 3),
+                                 __builtin_shufflevector(c, d, 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+struct MgItem {
+  int e;       // expert, or -1 past the end of the work list
+  int m0;      // first row of the block within the expert's rows
+  int n0, n;   // the expert's grouped rows [n0, n0 + n)
+  const uint8_t* w;
+};
+
+// The mb-th (expert, 64-row block) pair over the active experts in ascending id.
+__device__ __forceinline__ MgItem mg_item(const FfnArgs& p, int mb) {
+  __shared__ int s_e, s_m0;
+  __shared__ const char* s_w;
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    int seen = 0, ef = -1, m0 = 0;
+    for (int e0 = 0; e0 < p.E; e0 += 64) {
+      const int e = e0 + lane;
+      const int nb = e < p.E && active(p, e) ? (p.offsets[e + 1] - p.offsets[e] + kMgM - 1) / kMgM : 0;
+      int incl = nb;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int v = __shfl_up(incl, off);
+        if (lane >= off) incl += v;
+      }
+      const int total = __shfl(incl, 63);
+      if (mb < seen + total) {
+        const bool mine = mb >= seen + incl - nb && mb < seen + incl;
+        const int src = __ffsll((long long)__ballot(mine)) - 1;
+        ef = e0 + src;
+        m0 = (mb - seen - __shfl(incl - nb, src)) * kMgM;
+        break;
+      }
+      seen += total;
+    }
+    if (lane == 0) {
+      s_e = ef;
+      s_m0 = m0;
+      s_w = ef >= 0 ? entry_of(p, ef) : nullptr;
+    }
+  }
+  __syncthreads();
+  MgItem it{s_e, s_m0, 0, 0, (const uint8_t*)s_w};
+  if (it.e >= 0) {
+    it.n0 = p.offsets[it.e];
+    it.n = p.offsets[it.e + 1] - it.n0;
+  }
+  return it;
+}
+
+// This thread's share of one staged tile column: 64 rows x 16 chunks of 8 elements, four
+// chunks per thread; src_row(t) gives the source row of block row t (rows past the expert
+// repeat block row 0).
+struct MgStage {
+  u32x4 v[4];
+};
+
+template <typename RowOf>
+__device__ __forceinline__ void mg_load_a(MgStage& st, const uint16_t* src, int K, int kt,
+                                          int rows, RowOf src_row) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = threadIdx.x + 256 * i, t = c >> 4, ch = c & 15;
+    const int k = kt * 128 + ch * 8;
+    st.v[i] = k < K ? ldg16(src + (size_t)src_row(t < rows ? t : 0) * K + k) : u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+__device__ __forceinline__ void mg_store_a(const MgStage& st, uint16_t* lds) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = threadIdx.x + 256 * i, t = c >> 4, ch = c & 15;
+    *(u32x4*)&lds[t * kMgLd + ch * 8] = st.v[i];
+  }
+}
+
+template <int NMAT>
+struct MgB {
+  u32x4 c[kMgS][NMAT];
+  uint32_t s[kMgS][NMAT];
+};
+
+// Tile column kt of the wave's strips (cb/sb: strip 0's codes/scales of each matrix, the
+// next strip 8 K / K/2 bytes further); nstr strips exist (the last workgroup of a matrix
+// may own fewer); lanes whose block is past K load zeros.
+template <int NMAT>
+__device__ __forceinline__ void mg_load_b(MgB<NMAT>& b, const uint8_t* const (&cb)[NMAT],
+                                          const uint8_t* const (&sb)[NMAT], int K, int kt,
+                                          int nstr, int lane) {
+  const bool ok = kt * 128 + 32 * (lane >> 4) < K;
+#pragma unroll
+  for (int s = 0; s < kMgS; ++s)
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m) {
+      if (ok && s < nstr) {
+        b.c[s][m] = ldg16(cb[m] + (size_t)s * 8 * K + (size_t)kt * 1024 + lane * 16);
+        b.s[s][m] = ldg_u8(sb[m] + (size_t)s * (K / 2) + (size_t)kt * 64 + lane);
+      } else {
+        b.c[s][m] = u32x4{0u, 0u, 0u, 0u};
+        b.s[s][m] = 0u;
+      }
+    }
+  issue_fence();
+}
+
+// acc[s][m][mt] += A(mt) x B(s, m)^T over one tile column.
+template <int NMAT>
+__device__ __forceinline__ void mg_mma(const MgB<NMAT>& b, const uint16_t* lds, int lane,
+                                       f32x4 (&acc)[kMgS][NMAT][4]) {
+  bf16x8 w[kMgS][NMAT][4];
+#pragma unroll
+  for (int s = 0; s < kMgS; ++s)
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m) {
+      const float sc = mg_e8m0(b.s[s][m]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) w[s][m][j] = mg_expand8(b.c[s][m][j], sc);
+    }
+  const uint16_t* ar = lds + (lane & 15) * kMgLd + 32 * (lane >> 4);
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    bf16x8 a[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) a[j] = as_bf16x8(*(const u32x4*)(ar + mt * 16 * kMgLd + 8 * j));
+#pragma unroll
+    for (int s = 0; s < kMgS; ++s)
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[s][m][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], w[s][m][j], acc[s][m][mt], 0, 0, 0);
+  }
+}
+
+// Workgroup id -> logical block, XCD-major: workgroups are dealt round-robin over the 8 XCDs,
+// so consecutive logical blocks (the weight blocks of one token block) land on one XCD.
+__device__ __forceinline__ int mg_logical_block() {
+  const int g = gridDim.x;  // a multiple of 8
+  return (blockIdx.x & 7) * (g >> 3) + (blockIdx.x >> 3);
+}
+
+// The K loop shared by both kernels: stages token rows, streams the weight tiles.
+template <int NMAT, typename RowOf>
+__device__ __forceinline__ void mg_run(const uint16_t* src, int K, int rows, RowOf src_row,
+                                       const uint8_t* const (&cb)[NMAT],
+                                       const uint8_t* const (&sb)[NMAT], int nstr, int lane,
+                                       uint16_t* lds, f32x4 (&acc)[kMgS][NMAT][4]) {
+  const int nk = (K + 127) >> 7;
+  MgStage st;
+  MgB<NMAT> b;
+  mg_load_b<NMAT>(b, cb, sb, K, 0, nstr, lane);
+  mg_load_a(st, src, K, 0, rows, src_row);
+  mg_store_a(st, lds);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const MgB<NMAT> cur = b;
+    uint16_t* cur_lds = lds + (kt & 1) * kMgM * kMgLd;
+    if (kt + 1 < nk) {
+      mg_load_b<NMAT>(b, cb, sb, K, kt + 1, nstr, lane);
+      mg_load_a(st, src, K, kt + 1, rows, src_row);
+    }
+    mg_mma<NMAT>(cur, cur_lds, lane, acc);
+    if (kt + 1 < nk) mg_store_a(st, lds + ((kt + 1) & 1) * kMgM * kMgLd);
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(256) void mg_gateup(FfnArgs p) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * kMgM * kMgLd];
+  const int nnb = (p.f + kMgN - 1) / kMgN;
+  const int L = mg_logical_block();
+  const MgItem it = mg_item(p, L / nnb);
+  if (it.e < 0 || !it.w) return;
+  const int nb = L - (L / nnb) * nnb;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rt0 = nb * (kMgN / 16) + wave * kMgS;  // first strip of this wave
+  const int nstr = min(kMgS, p.f / 16 - rt0);
+  const int rows = min(kMgM, it.n - it.m0);
+  const int K = p.d;
+  const size_t fd = (size_t)p.f * K;
+  const uint8_t* W = it.w;
+  const size_t so = (size_t)rt0 * 8 * K, ss = (size_t)rt0 * (K / 2);
+  const uint8_t* const cb[2] = {W + so, W + fd / 2 + so};
+  const uint8_t* const sb[2] = {W + 3 * fd / 2 + ss, W + 3 * fd / 2 + fd / 32 + ss};
+  f32x4 acc[kMgS][2][4];
+#pragma unroll
+  for (int s = 0; s < kMgS; ++s)
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) acc[s][m][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int base = it.n0 + it.m0;
+  mg_run<2>((const uint16_t*)p.x, K, rows, [&](int t) { return p.perm[base + t] / p.k; }, cb, sb,
+            nstr, lane, lds, acc);
+  uint16_t* H = (uint16_t*)p.h;
+  const int col = lane & 15, kg = lane >> 4;
+#pragma unroll
+  for (int s = 0; s < kMgS; ++s) {
+    if (s >= nstr) continue;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = mt * 16 + kg * 4 + i;  // lane holds C[4 kg + i][col] of the 16x16 tile
+        if (t < rows)
+          H[(size_t)(base + t) * p.f + 16 * (rt0 + s) + col] = f32_to_bf16(silu(acc[s][0][mt][i]) * acc[s][1][mt][i]);
+      }
+  }
+}
+
+template <int YDT>
+__global__ __launch_bounds__(256) void mg_down(FfnArgs p) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * kMgM * kMgLd];
+  const int nnb = (p.d + kMgN - 1) / kMgN;
+  const int L = mg_logical_block();
+  const MgItem it = mg_item(p, L / nnb);
+  if (it.e < 0 || !it.w) return;
+  const int nb = L - (L / nnb) * nnb;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rt0 = nb * (kMgN / 16) + wave * kMgS;
+  const int nstr = min(kMgS, p.d / 16 - rt0);
+  const int rows = min(kMgM, it.n - it.m0);
+  const int K = p.f;
+  const size_t fd = (size_t)K * p.d;
+  const uint8_t* W = it.w;
+  const size_t so = (size_t)rt0 * 8 * K, ss = (size_t)rt0 * (K / 2);
+  const uint8_t* const cb[1] = {W + fd + so};
+  const uint8_t* const sb[1] = {W + 3 * fd / 2 + 2 * (fd / 32) + ss};
+  f32x4 acc[kMgS][1][4];
+#pragma unroll
+  for (int s = 0; s < kMgS; ++s)
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) acc[s][0][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int base = it.n0 + it.m0;
+  mg_run<1>((const uint16_t*)p.h, K, rows, [&](int t) { return base + t; }, cb, sb, nstr, lane,
+            lds, acc);
+  const int col = lane & 15, kg = lane >> 4;
+#pragma unroll
+  for (int s = 0; s < kMgS; ++s) {
+    if (s >= nstr) continue;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = mt * 16 + kg * 4 + i;
+        if (t < rows) {
+          const size_t o = (size_t)(base + t) * p.d + 16 * (rt0 + s) + col;
+          if (YDT == MOE_F32) ((float*)p.y)[o] = acc[s][0][mt][i];
+          else ((uint16_t*)p.y)[o] = f32_to_bf16(acc[s][0][mt][i]);
+        }
+      }
+  }
+}
+
+}  // namespace
+
+int launch_ffn_mx_gemm(const FfnArgs& p, int T, int y_dtype, hipStream_t stream) {
+  // (expert, 64-row block) pairs: at most T*k/64 + (number of experts with rows)
+  const long A = (long)T * p.k;
+  const long mbs = A / kMgM + std::min<long>(p.E, A);
+  auto grid = [&](int R) {
+    const long g = mbs * ((R + kMgN - 1) / kMgN);
+    return dim3((unsigned)((g + 7) / 8 * 8));
+  };
+  hipLaunchKernelGGL(mg_gateup, grid(p.f), dim3(256), 0, stream, p);
+  MOE_LAUNCH_CHECK();
+  if (y_dtype == MOE_F32) hipLaunchKernelGGL(mg_down<MOE_F32>, grid(p.d), dim3(256), 0, stream, p);
+  else hipLaunchKernelGGL(mg_down<MOE_BF16>, grid(p.d), dim3(256), 0, stream, p);
+  MOE_LAUNCH_CHECK();
+  return MOE_OK;
+}
+
+}  // namespace moe

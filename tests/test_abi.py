@@ -73,6 +73,15 @@ def test_host_validation_codes():
     short = list(args); short[11] = 100
     assert L.moe_expert_ffn(*short) == moe.MOE_EINVAL
     assert L.moe_expert_ffn(*args) == moe.MOE_EINVAL  # null buffers
+    # MXFP4 weights: bf16 activations only; entries at least moe_entry_bytes; both paths
+    mx = list(args); mx[12] = moe.MOE_MXFP4; mx[11] = moe.moe_entry_bytes(4096, 2048, moe.MOE_MXFP4)
+    mx_short = list(mx); mx_short[11] -= 16
+    assert L.moe_expert_ffn(*mx_short) == moe.MOE_EINVAL
+    mx_f32 = list(mx); mx_f32[1] = moe.MOE_F32
+    assert L.moe_expert_ffn(*mx_f32) == moe.MOE_EUNSUPPORTED
+    for path in (moe.MOE_PATH_AUTO, moe.MOE_PATH_GEMV, moe.MOE_PATH_GEMM):
+        mx_p = list(mx); mx_p[20] = path
+        assert L.moe_expert_ffn(*mx_p) == moe.MOE_EINVAL  # accepted up to the null buffers
 
 
 def test_cache_host_validation():

@@ -196,13 +196,19 @@ def test_ffn_mxfp4_parity(T, E, k, d, f, ydt):
     assert_close(y, ref, bf16_tol(ref), f"y_perm mxfp4 T={T} d={d} f={f}")
 
 
-def test_ffn_mxfp4_rejects_gemm_path_and_short_entries():
-    w = configs.Workload("mx_bad", seed=26, T=4, d=256, E=4, k=2, f=128, dtype=gen.MXFP4)
-    with pytest.raises(moe.MoeError) as ei:
-        _ffn_case(w, moe.MOE_PATH_GEMM)
-    assert ei.value.status == moe.MOE_EUNSUPPORTED
-    assert moe.moe_entry_bytes(4096, 2048, moe.MOE_MXFP4) == 3 * 4096 * 2048 * 17 // 32
-    assert moe.moe_entry_bytes(4096, 2048, moe.MOE_BF16) == 3 * 4096 * 2048 * 2
+@pytest.mark.parametrize("T,E,k,d,f,alpha,path", [
+    (300, 8, 2, 512, 256, 0.5, moe.MOE_PATH_AUTO),     # several 64-row blocks per expert
+    (200, 6, 3, 320, 192, 0.5, moe.MOE_PATH_AUTO),     # short last tiles, partial weight blocks
+    (512, 16, 4, 256, 384, 1.0, moe.MOE_PATH_AUTO),    # skewed: empty and crowded experts
+    (64, 4, 2, 4096, 2048, 0.5, moe.MOE_PATH_GEMM),    # full row lengths, partial row blocks
+    (1, 4, 2, 256, 128, 0.5, moe.MOE_PATH_GEMM)])      # a single token
+@pytest.mark.parametrize("ydt", [moe.MOE_F32, moe.MOE_BF16])
+def test_ffn_mxfp4_gemm_parity(T, E, k, d, f, alpha, path, ydt):
+    """MXFP4 weights on the grouped-GEMM path (prefill-shaped counts) against the oracle on
+    the exactly dequantised weights."""
+    w = configs.Workload("mxg", seed=27, T=T, d=d, E=E, k=k, f=f, dtype=gen.MXFP4, alpha=alpha)
+    y, ref = _ffn_case(w, path, ydt)
+    assert_close(y, ref, bf16_tol(ref), f"y_perm mxfp4 gemm T={T} d={d} f={f}")
 
 
 def test_ffn_gemm_wide_n_tiles():
