@@ -249,14 +249,14 @@ def bench_prefill(args, torch, moe, dtype=None):
 
 
 # ------------------------------------------------------------------------ multi-layer LRU decode
-def bench_lru(args, torch, moe):
+def bench_lru(args, torch, moe, dtype=None, with_resize=True):
     import ctypes
     from gen import configs
     import gen
-    from gen.arena import host_pool
+    from gen.arena import host_pool, torch_dtype
     from expert_ffn_cache_amd.layer import MoeLayer
 
-    w = configs.LRU_DECODE
+    w = configs.LRU_DECODE if dtype is None else configs.with_(configs.LRU_DECODE, dtype=dtype)
     steps = args.lru_steps
     t0 = time.time()
     pool = host_pool(w)
@@ -265,7 +265,7 @@ def bench_lru(args, torch, moe):
     logits = torch.from_numpy(lg).cuda()
     xs = [torch.from_numpy(configs.gen_x(w, l).view(np.int16)).view(torch.bfloat16).cuda()
           for l in range(w.L)]
-    arena = torch.empty((w.S, w.entry_elems), dtype=torch.bfloat16, device="cuda")
+    arena = torch.empty((w.S, w.entry_elems), dtype=torch_dtype(w), device="cuda")
     i32 = dict(dtype=torch.int32, device="cuda")
     i64 = dict(dtype=torch.int64, device="cuda")
     slot_of, key_of = torch.empty(w.L * w.E, **i32), torch.empty(w.S, **i32)
@@ -280,7 +280,7 @@ def bench_lru(args, torch, moe):
     mirror = torch.empty((w.E + 1) * 4, dtype=torch.int32, pin_memory=True)
     masks = torch.zeros((2, 2, w.E), dtype=torch.uint8, pin_memory=True)
     masks_dev = torch.zeros((w.L, 2, w.E), dtype=torch.uint8, device="cuda")
-    lay = MoeLayer(w.T, w.E, w.k, w.d, w.f)
+    lay = MoeLayer(w.T, w.E, w.k, w.d, w.f, w_dtype=w.dtype)
     comp, copy = torch.cuda.Stream(), torch.cuda.Stream()
     last_ffn = _mk_event(torch, comp)
     fill_done = _mk_event(torch, copy)
@@ -379,13 +379,13 @@ def bench_lru(args, torch, moe):
         t = dict(slot_of=torch.empty(w.L * w.E, **i32), key_of=torch.empty(S2, **i32),
                  stamp=torch.empty(S2, **i64), clock=torch.empty(1, **i64),
                  stats=torch.empty(4, **i64), status=torch.zeros(1, **i32),
-                 arena=torch.empty((S2, w.entry_elems), dtype=torch.bfloat16, device="cuda"))
+                 arena=torch.empty((S2, w.entry_elems), dtype=torch_dtype(w), device="cuda"))
         d = moe.moe_cache_t(w.L, w.E, S2, 0, w.entry_bytes, *(t[n].data_ptr() for n in (
             "slot_of", "key_of", "stamp", "clock", "stats", "status", "arena")), pool.data_ptr())
         return d, t
     resize = {}
-    cur = desc
-    for S2 in (w.S // 2, w.S * 3 // 2):
+    cur, keep_alive = desc, None
+    for S2 in ((w.S // 2, w.S * 3 // 2) if with_resize else ()):
         d2, t2 = make_cache(S2)
         e0, e1 = _events(torch, 2)
         with torch.cuda.stream(comp):
@@ -399,11 +399,12 @@ def bench_lru(args, torch, moe):
         resize[f"{cur.S}_to_{S2}"] = dict(ms=ms, kept=kept,
                                           copy_gbs=2 * kept * w.entry_bytes / (ms * 1e-3) / 1e9)
         cur, keep_alive = d2, t2
-    del keep_alive
+    keep_alive = None
     pool.close()
     del arena
     torch.cuda.empty_cache()
-    return dict(workload=w.name, steps=steps, tok_s=steps * w.T / wall, wall_s=wall,
+    return dict(workload=w.name, weights="mxfp4" if w.dtype == gen.MXFP4 else "bf16",
+                entry_bytes=w.entry_bytes, steps=steps, tok_s=steps * w.T / wall, wall_s=wall,
                 graph_device_fill_tok_s=steps * w.T / wall_g, graph_wall_s=wall_g,
                 graph_overlap_tok_s=steps * w.T / walls[True], graph_overlap_wall_s=walls[True],
                 graph_overlap_fill_gbs=float(st[3]) / walls[True] / 1e9, resize=resize,
@@ -412,21 +413,23 @@ def bench_lru(args, torch, moe):
 
 
 # ------------------------------------------------------------------------ streamed prefill
-def bench_stream(args, torch, moe):
+def bench_stream(args, torch, moe, dtype=None):
+    import gen
     from gen import configs
-    from gen.arena import host_pool
+    from gen.arena import host_pool, torch_dtype
     from expert_ffn_cache_amd.layer import MoeLayer
 
-    w = configs.STREAM_PREFILL
+    w = configs.STREAM_PREFILL if dtype is None else configs.with_(configs.STREAM_PREFILL, dtype=dtype)
     t0 = time.time()
     pool = host_pool(w)
     log(f"[stream] pinned pool {pool.nbytes / 1e9:.2f} GB in {time.time() - t0:.1f}s")
     layer_bytes = w.E * w.entry_bytes
-    bufs = [torch.empty((w.E, w.entry_elems), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    bufs = [torch.empty((w.E, w.entry_elems), dtype=torch_dtype(w), device="cuda") for _ in range(2)]
     xs = [torch.from_numpy(configs.gen_x(w, l).view(np.int16)).view(torch.bfloat16).cuda()
           for l in range(w.L)]
     lgs = [torch.from_numpy(configs.gen_logits(w, layer=l)).cuda() for l in range(w.L)]
-    layers = [MoeLayer(w.T, w.E, w.k, w.d, w.f, y_dtype=moe.MOE_BF16) for _ in range(w.L)]
+    layers = [MoeLayer(w.T, w.E, w.k, w.d, w.f, y_dtype=moe.MOE_BF16, w_dtype=w.dtype)
+              for _ in range(w.L)]
     comp, copy = torch.cuda.Stream(), torch.cuda.Stream()
     # measured pinned H2D bandwidth (one layer block through the same copy entry point)
     with torch.cuda.stream(copy):
@@ -481,7 +484,8 @@ def bench_stream(args, torch, moe):
     pool.close()
     del bufs
     torch.cuda.empty_cache()
-    return dict(workload=w.name, tok_s=w.T / (wall_ms * 1e-3), wall_ms=wall_ms,
+    return dict(workload=w.name, weights="mxfp4" if w.dtype == gen.MXFP4 else "bf16",
+                layer_bytes=layer_bytes, tok_s=w.T / (wall_ms * 1e-3), wall_ms=wall_ms,
                 h2d_gbs=h2d_gbs, ideal_ms=ideal_ms, efficiency=ideal_ms / wall_ms,
                 overlap=overlap, copy_ms_per_layer=float(np.mean([b - a for a, b in copies])),
                 compute_ms_per_layer=float(np.mean([b - a for a, b in comps])))
@@ -559,7 +563,8 @@ def main():
     ap.add_argument("--lru-steps", type=int, default=512)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-sweep", action="store_true", help="decode at the primary T and alpha only")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="primary lines only: no decode T/alpha sweep and no MXFP4 extras")
     ap.add_argument("--weights", choices=["bf16", "mxfp4"], default="bf16",
                     help="expert weight format of the primary decode line (--workload decode)")
     args = ap.parse_args()
@@ -620,12 +625,20 @@ def main():
     if wl in ("all", "stream"):
         extra["stream_prefill"] = bench_stream(args, torch, moe)
         log(f"[stream] {json.dumps(extra['stream_prefill'])}")
+        if not args.no_sweep:
+            import gen
+            extra["stream_prefill_mxfp4"] = bench_stream(args, torch, moe, gen.MXFP4)
+            log(f"[stream mxfp4] {json.dumps(extra['stream_prefill_mxfp4'])}")
     if wl in ("all", "probe"):
         extra["hbm_probe"] = bench_probe(args, torch, moe)
         log(f"[probe] {json.dumps(extra['hbm_probe'])}")
     if wl in ("all", "lru"):
         extra["lru_decode"] = bench_lru(args, torch, moe)
         log(f"[lru] {json.dumps(extra['lru_decode'])}")
+        if not args.no_sweep:
+            import gen
+            extra["lru_decode_mxfp4"] = bench_lru(args, torch, moe, gen.MXFP4, with_resize=False)
+            log(f"[lru mxfp4] {json.dumps(extra['lru_decode_mxfp4'])}")
     cpu = None
     if dec and not args.no_cpu_baseline:
         cpu = cpu_baseline(args)
