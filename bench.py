@@ -52,6 +52,21 @@ def _ffn_bytes(w, U):
     return U * w.entry_bytes + A * w.d * 2 + 2 * A * w.f * 2 + A * w.d * 4
 
 
+_STREAMS = {}
+
+
+def _stream(torch, role):
+    """The stream of a role ("comp", "copy", "side"), created once per process.  HIP maps
+    streams onto a few hardware queues (GPU_MAX_HW_QUEUES, 4 here); streams that share a
+    queue run in queue order, so a fresh pair of streams per measurement can serialise a
+    copy with unrelated compute.  One stream per role, created together at start-up, keeps
+    the roles on distinct queues for every measurement."""
+    if not _STREAMS:
+        for r in ("comp", "copy", "side"):
+            _STREAMS[r] = torch.cuda.Stream()
+    return _STREAMS[role]
+
+
 def _ffn_flops(w):
     return 2.0 * w.T * w.k * 3 * w.d * w.f
 
@@ -115,7 +130,7 @@ def bench_decode(args, torch, moe, T, alpha, arena, dtype=None):
     x = torch.from_numpy(configs.gen_x(w).view(np.int16)).view(torch.bfloat16).cuda()
     logits = [torch.from_numpy(configs.gen_logits(w, rotation=r)).cuda() for r in range(R)]
     layers = [MoeLayer(w.T, w.E, w.k, w.d, w.f, w_dtype=w.dtype) for _ in range(R)]
-    s = torch.cuda.Stream()
+    s = _stream(torch, "comp")
     graphs = []
     with torch.cuda.stream(s):
         for r in range(R):
@@ -199,7 +214,7 @@ def bench_prefill(args, torch, moe, dtype=None):
         logits = [torch.from_numpy(configs.gen_logits(w, rotation=r)).cuda() for r in range(R)]
         layers = [MoeLayer(w.T, w.E, w.k, w.d, w.f, y_dtype=moe.MOE_BF16, w_dtype=w.dtype)
                   for _ in range(R)]
-        s = torch.cuda.Stream()
+        s = _stream(torch, "comp")
         steps = max(4, args.steps // 5)
         with torch.cuda.stream(s):
             for r in range(R):
@@ -281,7 +296,7 @@ def bench_lru(args, torch, moe, dtype=None, with_resize=True):
     masks = torch.zeros((2, 2, w.E), dtype=torch.uint8, pin_memory=True)
     masks_dev = torch.zeros((w.L, 2, w.E), dtype=torch.uint8, device="cuda")
     lay = MoeLayer(w.T, w.E, w.k, w.d, w.f, w_dtype=w.dtype)
-    comp, copy = torch.cuda.Stream(), torch.cuda.Stream()
+    comp, copy = _stream(torch, "comp"), _stream(torch, "copy")
     last_ffn = _mk_event(torch, comp)
     fill_done = _mk_event(torch, copy)
     got = torch.cuda.Event()
@@ -330,7 +345,7 @@ def bench_lru(args, torch, moe, dtype=None, with_resize=True):
     # forks after each lookup: the fill kernel runs on a side branch while the FFN of the
     # hits runs, and the FFN of the misses follows the join.
     lg_static = torch.empty((w.L, w.T, w.E), dtype=torch.float32, device="cuda")
-    side = torch.cuda.Stream()
+    side = _stream(torch, "side")
     walls = {}
     for overlap in (False, True):
         with torch.cuda.stream(comp):
@@ -430,7 +445,7 @@ def bench_stream(args, torch, moe, dtype=None):
     lgs = [torch.from_numpy(configs.gen_logits(w, layer=l)).cuda() for l in range(w.L)]
     layers = [MoeLayer(w.T, w.E, w.k, w.d, w.f, y_dtype=moe.MOE_BF16, w_dtype=w.dtype)
               for _ in range(w.L)]
-    comp, copy = torch.cuda.Stream(), torch.cuda.Stream()
+    comp, copy = _stream(torch, "comp"), _stream(torch, "copy")
     # measured pinned H2D bandwidth (one layer block through the same copy entry point)
     with torch.cuda.stream(copy):
         a, b = _events(torch, 2)
@@ -502,7 +517,7 @@ def bench_probe(args, torch, moe):
     src = big[:n]
     dst = torch.empty(n, dtype=torch.uint8, device="cuda")
     sink = torch.empty(4096, dtype=torch.int32, device="cuda")
-    s = torch.cuda.Stream()
+    s = _stream(torch, "comp")
     reps = 10
     with torch.cuda.stream(s):
         moe.moe_hbm_read_probe(big, nr, sink, s)
