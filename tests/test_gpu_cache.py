@@ -8,7 +8,7 @@ import torch
 
 import gen
 from gen import configs
-from gen.arena import host_pool
+from gen.arena import host_pool, torch_dtype
 import oracle
 from oracle import LruSim
 import expert_ffn_cache_amd as moe
@@ -174,9 +174,9 @@ def test_cache_fill_rejects_out_of_range_records():
     assert ei.value.status == moe.MOE_ERANGE
 
 
-def _small_lru_workload(seed):
+def _small_lru_workload(seed, dtype=gen.BF16):
     # S >= T*k; 3 layers x ~11 unique ids per layer evict every step
-    return configs.Workload("lru_small", seed=seed, T=4, d=256, E=16, k=3, f=192, dtype=gen.BF16,
+    return configs.Workload("lru_small", seed=seed, T=4, d=256, E=16, k=3, f=192, dtype=dtype,
                             L=3, S=14, alpha=0.5)
 
 
@@ -221,20 +221,20 @@ def test_device_fill_matches_host_fill_and_pool():
     assert int(dc.status.item()) == 0
 
 
-@pytest.mark.parametrize("overlap", [False, True])
-def test_decode_step_with_device_fills_replays_as_one_graph(overlap):
+@pytest.mark.parametrize("overlap,dtype", [(False, gen.BF16), (True, gen.BF16), (True, gen.MXFP4)])
+def test_decode_step_with_device_fills_replays_as_one_graph(overlap, dtype):
     """route -> lookup -> device fill -> permute -> FFN through slots (key-checked) -> combine
     for every layer, captured once and replayed over several steps with new routing written
     into the captured input between replays: every layer's output equals the oracle and the
     cache tables equal the sequential simulator's.  With overlap, the graph forks after the
     lookup: the fill runs on a side branch while the FFN of the hits runs, and the FFN of
-    the misses follows the join."""
-    w = _small_lru_workload(35)
+    the misses follows the join.  MXFP4 entries take the same path (fills are byte copies)."""
+    w = _small_lru_workload(35, dtype)
     pool = host_pool(w)
-    arena = torch.zeros((w.S, w.entry_elems), dtype=torch.bfloat16, device="cuda")
+    arena = torch.zeros((w.S, w.entry_elems), dtype=torch_dtype(w), device="cuda")
     dc = DevCache(w.L, w.E, w.S, w.entry_bytes, arena, pool)
     sim = LruSim(w.L, w.E, w.S)
-    layers = [MoeLayer(w.T, w.E, w.k, w.d, w.f) for _ in range(w.L)]
+    layers = [MoeLayer(w.T, w.E, w.k, w.d, w.f, w_dtype=w.dtype) for _ in range(w.L)]
     xs = [configs.gen_x(w, layer) for layer in range(w.L)]
     xs_dev = [x_device(w, x) for x in xs]
     tables = [oracle_table(w, range(w.E), layer) for layer in range(w.L)]
