@@ -138,11 +138,42 @@ struct MxItem {
   const uint8_t* w;
 };
 
+// The a-th active expert in ascending id (called by one full wave), the offsets of 256
+// experts read in one round trip: a workgroup here streams little, so its start-up latency
+// shows.
+__device__ __forceinline__ int mx_nth_active(const FfnArgs& p, int a) {
+  const int lane = threadIdx.x & 63;
+  int seen = 0;
+  for (int e0 = 0; e0 < p.E; e0 += 256) {
+    int n[4];
+    bool ok[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = min(e0 + 64 * j + lane, p.E - 1);
+      n[j] = p.offsets[e + 1] - p.offsets[e];
+      ok[j] = !p.mask || p.mask[e];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = e0 + 64 * j + lane;
+      const bool act = e < p.E && n[j] > 0 && n[j] >= p.nmin && n[j] <= p.nmax && ok[j];
+      const unsigned long long m = __ballot(act);
+      const int c = __popcll(m);
+      if (a < seen + c) {
+        const bool mine = act && __popcll(m & lanemask_lt(lane)) == a - seen;
+        return e0 + 64 * j + __ffsll((long long)__ballot(mine)) - 1;
+      }
+      seen += c;
+    }
+  }
+  return -1;
+}
+
 __device__ __forceinline__ MxItem mx_item(const FfnArgs& p, int a) {
   __shared__ int s_e;
   __shared__ const char* s_w;
   if (threadIdx.x < 64) {
-    const int e = nth_active_expert(p, a);
+    const int e = mx_nth_active(p, a);
     if (threadIdx.x == 0) {
       s_e = e;
       s_w = e >= 0 ? entry_of(p, e) : nullptr;

@@ -7,10 +7,13 @@
 // One 64-wide wavefront per token.  Each lane holds ceil(E/64) logits in
 // registers (lane l owns experts l, l+64, ...).  Each of the k rounds is a
 // wave-wide max over a 64-bit key (order-preserving logit bits, then the
-// complemented expert id so that ties go to the lower id) with xor shuffles;
+// complemented expert id so that ties go to the lower id), taken as two 32-bit
+// maxima (the high word, then the low word among the lanes that hold that high
+// word) with DPP moves and scalar read-outs, so a round makes no LDS round trip;
 // the owner lane retires the winner.  The softmax over the k winners is done
 // in registers (lane j holds winner j) and written coalesced.
 #include "common.h"
+#include "wave.h"
 
 using namespace moe;
 
@@ -42,14 +45,12 @@ __global__ __launch_bounds__(256) void route_topk_softmax(const float* __restric
   float sel_v = 0.0f, top = 0.0f;
   int sel_id = 0;
   for (int r = 0; r < k; ++r) {
-    unsigned long long best = key[0];
+    unsigned long long mine = key[0];
 #pragma unroll
-    for (int i = 1; i < NPL; ++i) best = key[i] > best ? key[i] : best;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const unsigned long long o = __shfl_xor(best, off);
-      best = o > best ? o : best;
-    }
+    for (int i = 1; i < NPL; ++i) mine = key[i] > mine ? key[i] : mine;
+    const uint32_t hi = wave_max_u32((uint32_t)(mine >> 32));
+    const uint32_t lo = wave_max_u32((uint32_t)(mine >> 32) == hi ? (uint32_t)mine : 0u);
+    const unsigned long long best = ((unsigned long long)hi << 32) | lo;
     const int id = (int)(~(uint32_t)best);
     const float v = from_order_bits((uint32_t)(best >> 32));
     if (r == 0) top = v;

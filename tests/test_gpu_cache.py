@@ -119,16 +119,17 @@ def test_lru_bad_id_and_layer():
     assert int(dc.clock.item()) == 0
 
 
-def test_fill_then_ffn_through_slots_and_stale_slot_detection():
+@pytest.mark.parametrize("dtype", [gen.BF16, gen.MXFP4])
+def test_fill_then_ffn_through_slots_and_stale_slot_detection(dtype):
     """A small multi-layer cache: lookup -> D2H fill list -> cache_fill from the pinned pool ->
     FFN reading weights through expert_slot with the key check -> combine; every step's
     output equals the oracle.  Then a corrupted key makes the FFN report MOE_ERANGE."""
-    w = configs.Workload("lru_small", seed=31, T=4, d=256, E=16, k=3, f=192, dtype=gen.BF16,
+    w = configs.Workload("lru_small", seed=31, T=4, d=256, E=16, k=3, f=192, dtype=dtype,
                          L=3, S=14, alpha=0.5)  # S >= T*k; 3 layers x ~11 unique ids evict
     pool = host_pool(w)
-    arena = torch.empty((w.S, w.entry_elems), dtype=torch.bfloat16, device="cuda")
+    arena = torch.empty((w.S, w.entry_elems), dtype=torch_dtype(w), device="cuda")
     dc = DevCache(w.L, w.E, w.S, w.entry_bytes, arena, pool)
-    lay = MoeLayer(w.T, w.E, w.k, w.d, w.f)
+    lay = MoeLayer(w.T, w.E, w.k, w.d, w.f, w_dtype=w.dtype)
     copy = torch.cuda.Stream()
     fills_host = (moe.moe_fill_t * w.E)()
     for step in range(6):
