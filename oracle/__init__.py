@@ -105,10 +105,10 @@ def mxfp4_dequant(codes, scales):
     q[:, 1::2] = codes >> 4
     if np.any(scales == 255):
         raise ValueError("E8M0 NaN scale")
-    mag = _E2M1[q & 7]
-    sign = np.where(q & 8, -1.0, 1.0)
+    # value of each of the 16 codes: sign bit 3, E2M1 magnitude from bits 2:0
+    code_value = np.array([(-1.0 if c & 8 else 1.0) * _E2M1[c & 7] for c in range(16)])
     block = np.ldexp(1.0, scales.astype(np.int64) - 127)
-    return sign * mag * np.repeat(block, 32, axis=1)
+    return (code_value[q].reshape(R, -1, 32) * block[:, :, None]).reshape(R, 2 * half)
 
 
 class ExpertTable:

@@ -52,7 +52,7 @@ def _run_layer(w, rotation=0, y_dtype=moe.MOE_F32, arena=None):
     lg = configs.gen_logits(w, rotation=rotation)
     if arena is None:
         arena = device_arena_all_experts(w)
-    L = MoeLayer(w.T, w.E, w.k, w.d, w.f, dtype=w.dtype, y_dtype=y_dtype)
+    L = MoeLayer(w.T, w.E, w.k, w.d, w.f, dtype=w.act_dtype, y_dtype=y_dtype, w_dtype=w.dtype)
     L.forward(x_device(w, x), dev(lg), arena, w.entry_bytes)
     torch.cuda.synchronize()
     return x, lg, L, arena
@@ -99,6 +99,39 @@ def test_prefill_layer_full_size_sampled(alpha, decode_arena):
     _, _, ref = oracle.moe_layer(x, lg, w.k, oracle_table(w, need), tokens=toks)
     out = L.out.cpu().numpy()[toks]
     assert_close(out, ref, bf16_tol(ref), f"prefill alpha={alpha}")
+    assert int(L.status.item()) == 0
+    del arena
+
+
+def test_decode_layer_full_size_mxfp4():
+    """The decode layer with MXFP4 experts (E=256, k=6, d=4096, f=2048, T=8, all experts
+    resident): every output element against the oracle on the exactly dequantised weights."""
+    w = configs.with_(configs.DECODE, dtype=gen.MXFP4)
+    x, lg, L, arena = _run_layer(w)
+    ids, wt, ref = oracle.moe_layer(x, lg, w.k, oracle_table(w, sorted(set(oracle.route(lg, w.k)[0].ravel().tolist()))))
+    np.testing.assert_array_equal(L.ids.cpu().numpy(), ids)
+    assert_close(L.out.cpu().numpy(), ref, bf16_tol(ref), "decode mxfp4 T=8")
+    assert int(L.status.item()) == 0
+    del arena
+
+
+def test_prefill_layer_full_size_sampled_mxfp4():
+    """T=8192 prefill with MXFP4 experts (grouped GEMM): routing and grouping bit-exact,
+    outputs of sampled tokens (first, last, spread, and rows of the most loaded expert)."""
+    w = configs.with_(configs.PREFILL, dtype=gen.MXFP4)
+    x, lg, L, arena = _run_layer(w)
+    ids, wt = oracle.route(lg, w.k)
+    np.testing.assert_array_equal(L.ids.cpu().numpy(), ids)
+    counts, offsets, perm, inv = oracle.permute(ids, w.E)
+    np.testing.assert_array_equal(L.perm.cpu().numpy(), perm)
+    r = np.random.default_rng(7)
+    big = int(np.argmax(counts))
+    toks = set([0, w.T - 1]) | set(r.choice(w.T, 6, replace=False).tolist())
+    toks |= set((perm[offsets[big]:offsets[big + 1]][-3:] // w.k).tolist())
+    toks = np.array(sorted(toks), dtype=np.int32)
+    need = sorted(set(ids[toks].ravel().tolist()))
+    _, _, ref = oracle.moe_layer(x, lg, w.k, oracle_table(w, need), tokens=toks)
+    assert_close(L.out.cpu().numpy()[toks], ref, bf16_tol(ref), "prefill mxfp4")
     assert int(L.status.item()) == 0
     del arena
 
