@@ -297,6 +297,19 @@ def bench_lru(args, torch, moe, dtype=None, with_resize=True):
     masks_dev = torch.zeros((w.L, 2, w.E), dtype=torch.uint8, device="cuda")
     lay = MoeLayer(w.T, w.E, w.k, w.d, w.f, w_dtype=w.dtype)
     comp, copy = _stream(torch, "comp"), _stream(torch, "copy")
+    # pinned H2D bandwidth for these entries: 64 pool entries into the arena (overwritten
+    # by the fills later; the cache starts cold)
+    nb = min(64, w.S) * w.entry_bytes
+    with torch.cuda.stream(copy):
+        moe.layer_stream_prefetch(pool.entry_ptr(0), arena, nb, 1, copy, None, None)
+        ha, hb = _events(torch, 2)
+        torch.cuda.synchronize()
+        ha.record(copy)
+        for _ in range(3):
+            moe.layer_stream_prefetch(pool.entry_ptr(0), arena, nb, 1, copy, None, None)
+        hb.record(copy)
+        torch.cuda.synchronize()
+    h2d_gbs = 3 * nb / (ha.elapsed_time(hb) * 1e-3) / 1e9
     last_ffn = _mk_event(torch, comp)
     fill_done = _mk_event(torch, copy)
     got = torch.cuda.Event()
@@ -424,7 +437,10 @@ def bench_lru(args, torch, moe, dtype=None, with_resize=True):
                 graph_overlap_tok_s=steps * w.T / walls[True], graph_overlap_wall_s=walls[True],
                 graph_overlap_fill_gbs=float(st[3]) / walls[True] / 1e9, resize=resize,
                 miss_rate=float(st[2] / st[0]), hits=int(st[1]), misses=int(st[2]),
-                fill_gb=float(st[3] / 1e9), fill_gb_per_step=float(st[3] / 1e9 / steps))
+                fill_gb=float(st[3] / 1e9), fill_gb_per_step=float(st[3] / 1e9 / steps),
+                h2d_gbs=h2d_gbs, fill_time_s=float(st[3]) / (h2d_gbs * 1e9),
+                fill_time_over_wall=float(st[3]) / (h2d_gbs * 1e9) / wall,
+                fill_time_over_graph_overlap_wall=float(st[3]) / (h2d_gbs * 1e9) / walls[True])
 
 
 # ------------------------------------------------------------------------ streamed prefill
@@ -496,12 +512,19 @@ def bench_stream(args, torch, moe, dtype=None):
     if status != 0:
         raise RuntimeError(f"stream: device status {status}")
     ideal_ms = w.L * layer_bytes / (h2d_gbs * 1e9) * 1e3
+    # closed-form double-buffer timing from the measured per-layer copy (c) and compute (k)
+    # times: the first copy, then each step waits for the longer of the next copy and the
+    # current compute, then the last compute
+    c = [b - a for a, b in copies]
+    k = [b - a for a, b in comps]
+    model_ms = c[0] + sum(max(c[l + 1], k[l]) for l in range(w.L - 1)) + k[-1]
     pool.close()
     del bufs
     torch.cuda.empty_cache()
     return dict(workload=w.name, weights="mxfp4" if w.dtype == gen.MXFP4 else "bf16",
                 layer_bytes=layer_bytes, tok_s=w.T / (wall_ms * 1e-3), wall_ms=wall_ms,
                 h2d_gbs=h2d_gbs, ideal_ms=ideal_ms, efficiency=ideal_ms / wall_ms,
+                model_ms=model_ms, wall_over_model=wall_ms / model_ms,
                 overlap=overlap, copy_ms_per_layer=float(np.mean([b - a for a, b in copies])),
                 compute_ms_per_layer=float(np.mean([b - a for a, b in comps])))
 
