@@ -607,8 +607,9 @@ def main():
                     help="expert weight format of the primary decode line (--workload decode)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build has no "
-              "multi-GPU path; see the sharding notes in DESIGN.md.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the library has no "
+              "multi-GPU path (expert-parallel sharding is a design note, not code).",
+              file=sys.stderr)
         sys.exit(2)
     import torch
     import expert_ffn_cache_amd as moe
