@@ -74,7 +74,7 @@ def _ffn_flops(w):
 CSRC = os.path.join(ROOT, "expert_ffn_cache_amd", "csrc")
 # sources of the decode expert-FFN kernels (dot-product kernels and the headers they
 # include), which the committed counter summary was taken on
-DECODE_FFN_SOURCES = [os.path.join(CSRC, n) for n in ("common.h", "ffn_args.h", "ffn_dot.hip")]
+DECODE_FFN_SOURCES = [os.path.join(CSRC, n) for n in ("common.h", "ffn_args.h", "wave.h", "ffn_dot.hip")]
 # the same for MXFP4 weights (FP4-expanding MFMA kernels)
 MXFP4_FFN_SOURCES = [os.path.join(CSRC, n) for n in ("common.h", "ffn_args.h", "ffn_mx.hip")]
 

@@ -16,6 +16,7 @@
 #include <algorithm>
 
 #include "ffn_args.h"
+#include "wave.h"
 
 namespace moe {
 namespace {
@@ -40,11 +41,9 @@ __device__ __forceinline__ float dot8(u32x4 a, u32x4 b, float acc) {
   return acc;
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-  return v;
-}
+// One cross-lane sum per (weight row, token): DPP adds inside each 16-lane row, then the
+// four row sums as scalars (no LDS round trips).
+__device__ __forceinline__ float wave_sum(float v) { return wave_sum_f32(v); }
 
 __device__ __forceinline__ u32x4 ldw_nt(const uint16_t* p, bool ok) {
   return ok ? ldg16_nt(p) : u32x4{0u, 0u, 0u, 0u};

@@ -26,4 +26,19 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return max(max(a, b), max(c, d));
 }
 
+// Sum of v over the wave, the same in every lane: DPP adds inside each 16-lane row, then
+// the four row sums read out as scalars and added in a fixed order.
+__device__ __forceinline__ float wave_sum_f32(float v) {
+  v += __uint_as_float(dpp_u32<0xB1>(__float_as_uint(v)));   // quad_perm [1,0,3,2]
+  v += __uint_as_float(dpp_u32<0x4E>(__float_as_uint(v)));   // quad_perm [2,3,0,1]
+  v += __uint_as_float(dpp_u32<0x141>(__float_as_uint(v)));  // row_half_mirror
+  v += __uint_as_float(dpp_u32<0x140>(__float_as_uint(v)));  // row_mirror
+  const uint32_t b = __float_as_uint(v);
+  const float a0 = __uint_as_float(__builtin_amdgcn_readlane(b, 0));
+  const float a1 = __uint_as_float(__builtin_amdgcn_readlane(b, 16));
+  const float a2 = __uint_as_float(__builtin_amdgcn_readlane(b, 32));
+  const float a3 = __uint_as_float(__builtin_amdgcn_readlane(b, 48));
+  return (a0 + a1) + (a2 + a3);
+}
+
 }  // namespace moe
