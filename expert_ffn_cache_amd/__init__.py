@@ -32,7 +32,7 @@ MOE_PATH_GEMM = 2
 
 EXPORTS = [
     "moe_strerror", "moe_abi_version", "moe_router_logits", "moe_route",
-    "moe_permute_workspace_bytes", "moe_permute", "moe_entry_bytes",
+    "moe_permute_workspace_bytes", "moe_permute", "moe_route_permute", "moe_entry_bytes",
     "moe_expert_ffn_workspace_bytes",
     "moe_expert_ffn", "moe_combine", "cache_init", "cache_lookup_update",
     "cache_lookup_update_split", "cache_fill",
@@ -80,6 +80,7 @@ def lib():
             "moe_route": ([vp, i32, i32, i32, vp, vp, vp], i32),
             "moe_permute_workspace_bytes": ([i32, i32, i32], sz),
             "moe_permute": ([vp, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp, vp], i32),
+            "moe_route_permute": ([vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp], i32),
             "moe_entry_bytes": ([i32, i32, i32], sz),
             "moe_expert_ffn_workspace_bytes": ([i32, i32, i32, i32], sz),
             "moe_expert_ffn": ([vp, i32, vp, vp, i32, i32, i32, i32, i32, vp, vp, sz, i32, vp, vp,
@@ -162,6 +163,13 @@ def moe_permute(topk_ids, T, k, E, counts, offsets, perm, inv, ws, ws_bytes, sta
     _check("moe_permute", lib().moe_permute(_p(topk_ids), T, k, E, _p(counts), _p(offsets),
                                             _p(perm), _p(inv), _p(ws), ws_bytes, _p(status),
                                             _s(stream)))
+
+
+def moe_route_permute(logits, T, E, k, topk_ids, topk_w, counts, offsets, perm, inv, ws, ws_bytes,
+                      status=None, stream=None):
+    _check("moe_route_permute", lib().moe_route_permute(
+        _p(logits), T, E, k, _p(topk_ids), _p(topk_w), _p(counts), _p(offsets), _p(perm), _p(inv),
+        _p(ws), ws_bytes, _p(status), _s(stream)))
 
 
 def moe_entry_bytes(d, f, w_dtype):

@@ -14,8 +14,10 @@
 //           comes from ballots over the id bits (equal-id lane mask) and a
 //           popcount of the lower lanes; the last lane of each id group
 //           advances the wave's running base.
-// When everything fits one chunk (decode), a single fused launch does it all.
+// When everything fits one chunk (decode), a single fused launch does it all; for a
+// handful of tokens moe_route_permute also folds the routing into that launch.
 #include "common.h"
+#include "route_dev.h"
 
 using namespace moe;
 
@@ -24,6 +26,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kChunk = 1024;           // assignments per workgroup
 constexpr int kPerWave = kChunk / 4;   // 256 per wave, 4 steps of 64
+constexpr int kRoutePermuteMaxT = 16;  // tokens routed inside the fused launch (4 per wave)
 
 __device__ __forceinline__ int id_bits(int E) {
   int b = 0;
@@ -108,13 +111,12 @@ __global__ __launch_bounds__(1024) void permute_scan(int nchunk, int E, int32_t*
 // Per chunk: stable ranks and scatter.  FUSED: single chunk, computes counts
 // and offsets itself (ws unused).
 template <bool FUSED>
-__global__ __launch_bounds__(kThreads) void permute_rank(const int32_t* __restrict__ ids, int A,
-                                                         int E, const int32_t* __restrict__ ws,
-                                                         int32_t* __restrict__ counts,
-                                                         int32_t* __restrict__ offsets,
-                                                         int32_t* __restrict__ perm,
-                                                         int32_t* __restrict__ inv,
-                                                         int32_t* status) {
+__device__ __forceinline__ void permute_block(const int32_t* __restrict__ ids, int A, int E,
+                                              const int32_t* __restrict__ ws,
+                                              int32_t* __restrict__ counts,
+                                              int32_t* __restrict__ offsets,
+                                              int32_t* __restrict__ perm, int32_t* __restrict__ inv,
+                                              int32_t* status) {
   __shared__ int wb[4][kMaxE];
   __shared__ int s_wave[4];
   __shared__ int s_total;
@@ -197,6 +199,31 @@ __global__ __launch_bounds__(kThreads) void permute_rank(const int32_t* __restri
   }
 }
 
+template <bool FUSED>
+__global__ __launch_bounds__(kThreads) void permute_rank(const int32_t* __restrict__ ids, int A,
+                                                         int E, const int32_t* __restrict__ ws,
+                                                         int32_t* __restrict__ counts,
+                                                         int32_t* __restrict__ offsets,
+                                                         int32_t* __restrict__ perm,
+                                                         int32_t* __restrict__ inv,
+                                                         int32_t* status) {
+  permute_block<FUSED>(ids, A, E, ws, counts, offsets, perm, inv, status);
+}
+
+// Routing and grouping of a few tokens in one workgroup: the four waves route the tokens
+// (route_dev.h), then the workgroup groups the T*k assignments as permute_rank<true> does.
+// The ids written by one wave are read by the others after the barrier (same workgroup).
+template <int NPL>
+__global__ __launch_bounds__(kThreads) void route_permute_small(
+    const float* __restrict__ logits, int T, int E, int k, int32_t* __restrict__ ids,
+    float* __restrict__ w, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ perm, int32_t* __restrict__ inv, int32_t* status) {
+  for (int t = threadIdx.x >> 6; t < T; t += kThreads / 64)
+    route_token<NPL>(logits + (size_t)t * E, E, k, ids + (size_t)t * k, w + (size_t)t * k);
+  __syncthreads();
+  permute_block<true>(ids, T * k, E, nullptr, counts, offsets, perm, inv, status);
+}
+
 }  // namespace
 
 extern "C" size_t moe_permute_workspace_bytes(int T, int k, int E) {
@@ -229,6 +256,34 @@ extern "C" int moe_permute(const int32_t* topk_ids, int T, int k, int E, int32_t
   MOE_LAUNCH_CHECK();
   hipLaunchKernelGGL(permute_rank<false>, dim3(nchunk), dim3(kThreads), 0, stream, topk_ids, A, E,
                      (const int32_t*)w, counts, offsets, perm, inv, status);
+  MOE_LAUNCH_CHECK();
+  return MOE_OK;
+}
+
+extern "C" int moe_route_permute(const float* logits, int T, int E, int k, int32_t* topk_ids,
+                                 float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm,
+                                 int32_t* inv, void* ws, size_t ws_bytes, int32_t* status,
+                                 hipStream_t stream) {
+  if (T < 0 || E <= 0 || E > kMaxE || k <= 0 || k > kMaxK || k > E) return MOE_EINVAL;
+  if ((long long)T * E >= (1ll << 31) || (long long)T * k >= (1ll << 31)) return MOE_EINVAL;
+  if (!counts || !offsets) return MOE_EINVAL;
+  if (T > kRoutePermuteMaxT) {
+    int rc = moe_route(logits, T, E, k, topk_ids, topk_w, stream);
+    if (rc == MOE_OK) rc = moe_permute(topk_ids, T, k, E, counts, offsets, perm, inv, ws, ws_bytes, status, stream);
+    return rc;
+  }
+  if (T > 0 && (!logits || !topk_ids || !topk_w || !perm || !inv)) return MOE_EINVAL;
+  const dim3 g(1), b(kThreads);
+  if (E <= 64)
+    hipLaunchKernelGGL(route_permute_small<1>, g, b, 0, stream, logits, T, E, k, topk_ids, topk_w, counts, offsets, perm, inv, status);
+  else if (E <= 128)
+    hipLaunchKernelGGL(route_permute_small<2>, g, b, 0, stream, logits, T, E, k, topk_ids, topk_w, counts, offsets, perm, inv, status);
+  else if (E <= 256)
+    hipLaunchKernelGGL(route_permute_small<4>, g, b, 0, stream, logits, T, E, k, topk_ids, topk_w, counts, offsets, perm, inv, status);
+  else if (E <= 512)
+    hipLaunchKernelGGL(route_permute_small<8>, g, b, 0, stream, logits, T, E, k, topk_ids, topk_w, counts, offsets, perm, inv, status);
+  else
+    hipLaunchKernelGGL(route_permute_small<16>, g, b, 0, stream, logits, T, E, k, topk_ids, topk_w, counts, offsets, perm, inv, status);
   MOE_LAUNCH_CHECK();
   return MOE_OK;
 }

@@ -1,12 +1,13 @@
 """One routed-MoE layer forward as a sequence of library calls on caller-owned buffers.
 
-route -> permute -> expert FFN -> combine (each a libmoecache.so entry point).
+route + permute (one launch for small T) -> expert FFN -> combine, each a libmoecache.so
+entry point.
 Device memory comes from torch; this class only allocates the intermediate
 buffers once and forwards pointers.
 """
 import torch
 
-from . import (MOE_F32, MOE_BF16, MOE_PATH_AUTO, moe_route, moe_permute,
+from . import (MOE_F32, MOE_BF16, MOE_PATH_AUTO, moe_route, moe_permute, moe_route_permute,
                moe_permute_workspace_bytes, moe_expert_ffn, moe_expert_ffn_workspace_bytes,
                moe_combine)
 
@@ -46,6 +47,12 @@ class MoeLayer:
         moe_permute(self.ids, self.T, self.k, self.E, self.counts, self.offsets, self.perm,
                     self.inv, self.perm_ws, self.perm_ws_bytes, self.status, stream)
 
+    def route_permute(self, logits, stream=None):
+        """route() then permute(), in one launch for small T."""
+        moe_route_permute(logits, self.T, self.E, self.k, self.ids, self.w, self.counts,
+                          self.offsets, self.perm, self.inv, self.perm_ws, self.perm_ws_bytes,
+                          self.status, stream)
+
     def ffn(self, x, arena, entry_stride, expert_slot=None, mask=None, slot_key=None, key_base=0,
             path=MOE_PATH_AUTO, stream=None):
         moe_expert_ffn(x, self.dtype, self.perm, self.offsets, self.T, self.k, self.E, self.d,
@@ -59,8 +66,7 @@ class MoeLayer:
 
     def forward(self, x, logits, arena, entry_stride, expert_slot=None, path=MOE_PATH_AUTO,
                 stream=None):
-        self.route(logits, stream)
-        self.permute(stream)
+        self.route_permute(logits, stream)
         self.ffn(x, arena, entry_stride, expert_slot, path=path, stream=stream)
         self.combine(stream)
         return self.out

@@ -107,6 +107,15 @@ int moe_permute(const int32_t* topk_ids, int T, int k, int E, int32_t* counts, i
                 int32_t* perm, int32_t* inv, void* ws, size_t ws_bytes, int32_t* status,
                 hipStream_t stream);
 
+/* moe_route followed by moe_permute, with the same results (both steps as defined
+ * above).  For T <= 16 both run in one launch (one workgroup routes the tokens
+ * and groups the assignments), which saves a kernel boundary on the decode
+ * path; larger T makes the two calls.  ws / ws_bytes as for moe_permute (not
+ * touched by the one-launch form); status as for moe_permute. */
+int moe_route_permute(const float* logits, int T, int E, int k, int32_t* topk_ids, float* topk_w,
+                      int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv, void* ws,
+                      size_t ws_bytes, int32_t* status, hipStream_t stream);
+
 /* Entry layout of one (layer, expert) cache entry, in w_dtype elements:
  *   [ W_gate: f rows x d ][ W_up: f rows x d ][ W_down: d rows x f ]
  * every matrix row-major with the contraction index contiguous (W_gate row i

@@ -62,6 +62,11 @@ def test_host_validation_codes():
     assert L.moe_route(None, 4, 64, 2, None, None, None) == moe.MOE_EINVAL
     assert L.moe_router_logits(None, None, moe.MOE_BF16, 4, 64, 8, None, None) == moe.MOE_EUNSUPPORTED
     assert L.moe_combine(None, 7, None, None, 4, 2, 64, None, None) == moe.MOE_EUNSUPPORTED
+    # route + permute: the checks of both, before any launch
+    rp = [None, 8, 256, 6, None, None, None, None, None, None, None, 0, None, None]
+    assert L.moe_route_permute(*rp) == moe.MOE_EINVAL  # null counts/offsets
+    rp_k = list(rp); rp_k[3] = 300
+    assert L.moe_route_permute(*rp_k) == moe.MOE_EINVAL  # k > E
     assert L.moe_combine(None, moe.MOE_F32, None, None, 4, 2, 100, None, None) == moe.MOE_EINVAL
     # d, f must be multiples of 64; dtype pairs
     args = [None, moe.MOE_BF16, None, None, 8, 6, 256, 4096, 2048, None, None, 3 * 4096 * 2048 * 2,

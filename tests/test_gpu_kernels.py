@@ -96,6 +96,48 @@ def test_permute_out_of_range_id_sets_status():
     assert int(status.item()) == moe.MOE_ERANGE
 
 
+ROUTE_PERMUTE_CASES = [  # (T, E, k, kind): one-launch form up to T = 16, two calls above
+    (1, 256, 6, "zipf"), (8, 256, 6, "zipf"), (5, 8, 2, "normal"), (16, 1024, 16, "normal"),
+    (13, 65, 3, "zeros"), (16, 300, 5, "ties"), (1, 1, 1, "normal"), (17, 256, 6, "zipf"),
+    (64, 128, 8, "zipf"), (0, 256, 6, "zipf")]
+
+
+@pytest.mark.parametrize("T,E,k,kind", ROUTE_PERMUTE_CASES)
+def test_route_permute_equals_route_then_permute(T, E, k, kind):
+    """The combined entry point gives what moe_route and moe_permute give, bit for bit, and
+    the oracle's routing and grouping."""
+    lg = _route_logits(max(T, 1), E, k, kind, seed=T + 3 * E + k)[:T]
+    outs = []
+    for combined in (False, True):
+        ids, w = _i32((max(T, 1), k)), torch.full((max(T, 1), k), -1.0, device="cuda")
+        counts, offsets = _i32(E), _i32(E + 1)
+        perm, inv = _i32(max(T * k, 1)), _i32(max(T * k, 1))
+        status = torch.zeros(1, dtype=torch.int32, device="cuda")
+        nws = moe.moe_permute_workspace_bytes(T, k, E)
+        ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+        lg_d = dev(lg) if T else torch.empty((1, E), device="cuda")
+        if combined:
+            moe.moe_route_permute(lg_d, T, E, k, ids, w, counts, offsets, perm, inv, ws, nws, status)
+        else:
+            moe.moe_route(lg_d, T, E, k, ids, w)
+            moe.moe_permute(ids, T, k, E, counts, offsets, perm, inv, ws, nws, status)
+        torch.cuda.synchronize()
+        assert int(status.item()) == 0
+        outs.append([a.cpu().numpy()[:n] if n is not None else a.cpu().numpy()
+                     for a, n in ((ids.view(-1), T * k), (w.view(-1), T * k), (counts, None),
+                                  (offsets, None), (perm, T * k), (inv, T * k))])
+    for a, b in zip(*outs):
+        np.testing.assert_array_equal(a, b)
+    if T:
+        ref_ids, ref_w = oracle.route(lg, k)
+        np.testing.assert_array_equal(outs[1][0].reshape(T, k), ref_ids)
+        rc, ro, rp, ri = oracle.permute(ref_ids, E)
+        for got, want in zip(outs[1][2:], (rc, ro, rp, ri)):
+            np.testing.assert_array_equal(got, want)
+    else:
+        assert not outs[1][2].any() and not outs[1][3].any()
+
+
 # ---------------------------------------------------------------- combine
 @pytest.mark.parametrize("ydt", [moe.MOE_F32, moe.MOE_BF16])
 @pytest.mark.parametrize("T,k,d", [(16, 2, 256), (8, 6, 4096), (777, 8, 2048), (1, 1, 64)])
