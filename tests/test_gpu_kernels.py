@@ -226,7 +226,9 @@ def test_ffn_decode_dot_and_mfma_split(T, E, k, d, f, ydt):
 
 @pytest.mark.parametrize("T,E,k,d,f", [(8, 16, 6, 512, 256), (1, 8, 4, 4096, 2048), (8, 4, 2, 320, 192),
                                        (40, 6, 3, 1088, 448), (5, 64, 6, 2048, 4096),
-                                       (32, 128, 8, 1088, 576)])
+                                       (32, 128, 8, 1088, 576),
+                                       (4, 4, 2, 8128, 64),     # longest rows the streaming kernels stage
+                                       (4, 4, 2, 64, 8192)])    # beyond it: the GEMM takes decode too
 @pytest.mark.parametrize("ydt", [moe.MOE_F32, moe.MOE_BF16])
 def test_ffn_mxfp4_parity(T, E, k, d, f, ydt):
     """MXFP4 expert weights (OCP MX: E2M1 codes, E8M0 scale per 32) against the oracle on the
