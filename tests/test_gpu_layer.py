@@ -165,3 +165,35 @@ def test_layer_is_deterministic_and_graph_replayable():
             g.replay()
             torch.cuda.synchronize()
             assert torch.equal(L.out, outs[rot]), (rep, rot)
+
+
+def _random_shapes(n, seed):
+    """Seeded layer shapes across the dispatch boundaries: T from 1 to 200 (one-launch
+    routing, weight streaming, row split, grouped GEMM), E up to 300 (not powers of two),
+    k up to 8, d and f multiples of 64 (row lengths that leave short tiles and partial
+    lane chunks), Zipf skews 0.2 to 1."""
+    r = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        E = int(r.choice([5, 16, 37, 64, 130, 300]))
+        k = int(r.integers(1, min(8, E) + 1))
+        T = int(r.choice([1, 3, 8, 13, 16, 17, 40, 64, 65, 200]))
+        d = 64 * int(r.integers(1, 17))
+        f = 64 * int(r.integers(1, 13))
+        out.append((T, E, k, d, f, float(r.choice([0.2, 0.5, 1.0]))))
+    return out
+
+
+@pytest.mark.parametrize("dtype", [gen.BF16, gen.MXFP4])
+@pytest.mark.parametrize("T,E,k,d,f,alpha", _random_shapes(10, 1))
+def test_layer_random_shapes(T, E, k, d, f, alpha, dtype):
+    """Whole layer (routing and grouping, expert FFN on the path the host picks, combine)
+    on seeded random shapes, bf16 and MXFP4 experts, against the oracle."""
+    w = configs.Workload("rand", seed=T * 7 + E + d, T=T, d=d, E=E, k=k, f=f, dtype=dtype,
+                         alpha=alpha)
+    x, lg, L, arena = _run_layer(w)
+    ids, wt, ref = oracle.moe_layer(x, lg, w.k, oracle_table(w, sorted(set(oracle.route(lg, w.k)[0].ravel().tolist()))))
+    np.testing.assert_array_equal(L.ids.cpu().numpy(), ids)
+    assert_close(L.out.cpu().numpy(), ref, bf16_tol(ref), f"layer T={T} E={E} k={k} d={d} f={f}")
+    assert int(L.status.item()) == 0
+    del arena
