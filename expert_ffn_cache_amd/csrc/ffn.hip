@@ -104,6 +104,8 @@ extern "C" int moe_expert_ffn(const void* x, int act_dtype, const int32_t* perm,
   } else {
     return MOE_EUNSUPPORTED;
   }
+  const bool bf16_gemm_fits = ffn_gemm_supported(T, k, d, f);
+  if (w_dtype == MOE_BF16 && path == MOE_PATH_GEMM && !bf16_gemm_fits) return MOE_EUNSUPPORTED;
   const size_t need = mx ? moe_entry_bytes(d, f, w_dtype) : 3 * (size_t)d * f * (f32 ? 4 : 2);
   if (entry_stride < need || entry_stride % 16 != 0) return MOE_EINVAL;
   if (T == 0) return MOE_OK;
@@ -126,7 +128,9 @@ extern "C" int moe_expert_ffn(const void* x, int act_dtype, const int32_t* perm,
                       !ffn_mx_supported(d, f);
     return gemm ? launch_ffn_mx_gemm(p, T, y_dtype, stream) : launch_ffn_mx(p, y_dtype, stream, std::min(E, T * k));
   }
-  if (path == MOE_PATH_AUTO) path = (long long)T * k <= 8ll * E ? MOE_PATH_GEMV : MOE_PATH_GEMM;
+  // Past the GEMM's size limit the weight-streaming kernels (64-bit offsets) take the call.
+  if (path == MOE_PATH_AUTO)
+    path = (long long)T * k <= 8ll * E || !bf16_gemm_fits ? MOE_PATH_GEMV : MOE_PATH_GEMM;
   if (path == MOE_PATH_GEMM) return launch_ffn_gemm(p, y_dtype, stream);
   const int A = T * k, experts = std::min(E, A);
   if (T > kSplitMaxT || !ffn_dot_supported(d, f))

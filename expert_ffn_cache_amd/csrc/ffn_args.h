@@ -71,6 +71,7 @@ bool ffn_dot_supported(int d, int f);  // row lengths the dot-product path handl
 int launch_ffn_mx(const FfnArgs& p, int y_dtype, hipStream_t stream, int experts);
 bool ffn_mx_supported(int d, int f);  // shapes the weight-streaming MXFP4 kernels handle
 int launch_ffn_mx_gemm(const FfnArgs& p, int T, int y_dtype, hipStream_t stream);
+bool ffn_gemm_supported(long long T, int k, int d, int f);
 int launch_ffn_gemm(const FfnArgs& p, int y_dtype, hipStream_t stream);
 
 }  // namespace moe

@@ -147,7 +147,7 @@ void gemm_tile256(FfnArgs p, int n_ntiles) {
         ob[t] = (uint32_t)((rr >> 5) * p.f + (unit < p.f ? unit : 0)) * (uint32_t)p.d + lc * 8;
       } else {
         const int o = nt * QBN + R;
-        ob[t] = (uint32_t)(2 * p.f * p.d) + (uint32_t)(o < p.d ? o : 0) * (uint32_t)p.f + lc * 8;
+        ob[t] = 2u * (uint32_t)p.f * (uint32_t)p.d + (uint32_t)(o < p.d ? o : 0) * (uint32_t)p.f + lc * 8;
       }
     }
     auto stage_ptr = [&](auto tag) -> uint16_t* {
@@ -288,6 +288,12 @@ int num_cus() {
 }
 
 }  // namespace
+
+// The loaders keep element offsets in 32 bits (token rows of x and h, rows of an entry).
+bool ffn_gemm_supported(long long T, int k, int d, int f) {
+  constexpr long long lim = 1ll << 32;
+  return T * d <= lim && T * k * f <= lim && 3ll * d * f <= lim;
+}
 
 int launch_ffn_gemm(const FfnArgs& p, int y_dtype, hipStream_t stream) {
   const dim3 grid((num_cus() + 7) / 8 * 8), blk(512);

@@ -167,7 +167,10 @@ size_t moe_expert_ffn_workspace_bytes(int T, int k, int f, int act_dtype);
  *  round h to bf16 before the down projection.  MOE_MXFP4 weights (entry
  *  layout under moe_entry_bytes) need MOE_BF16 activations; each weight is its
  *  exact value (E2M1 value x block scale), the rest as for MOE_BF16.  MXFP4 runs
- *  on both paths (the weight-streaming one for d, f <= 8128).
+ *  on both paths (the weight-streaming one for d, f <= 8128).  With MOE_BF16
+ *  weights the GEMM path needs T*d, T*k*f and 3*d*f each <= 2^32 (it keeps
+ *  element offsets in 32 bits): MOE_PATH_GEMM past that returns
+ *  MOE_EUNSUPPORTED, MOE_PATH_AUTO takes the weight-streaming kernels.
  *  slot_key (nullable, device, [S]): when given, a slot whose key is not
  *  key_base + e, or a negative slot, sets *status = MOE_ERANGE and that
  *  expert's rows are not written (stale-cache detection).

@@ -87,6 +87,17 @@ def test_host_validation_codes():
     for path in (moe.MOE_PATH_AUTO, moe.MOE_PATH_GEMV, moe.MOE_PATH_GEMM):
         mx_p = list(mx); mx_p[20] = path
         assert L.moe_expert_ffn(*mx_p) == moe.MOE_EINVAL  # accepted up to the null buffers
+    # bf16 GEMM keeps 32-bit element offsets: an explicit GEMM request past 2^32 elements of
+    # h (T*k*f) or of an entry (3*d*f) is refused; AUTO is accepted (weight-streaming path)
+    big_t = list(args); big_t[4] = 400_000; big_t[20] = moe.MOE_PATH_GEMM
+    assert L.moe_expert_ffn(*big_t) == moe.MOE_EUNSUPPORTED
+    big_t[20] = moe.MOE_PATH_AUTO
+    assert L.moe_expert_ffn(*big_t) == moe.MOE_EINVAL  # accepted up to the null buffers
+    fits = list(args); fits[4] = 349_525; fits[20] = moe.MOE_PATH_GEMM  # T*k*f just under 2^32
+    assert L.moe_expert_ffn(*fits) == moe.MOE_EINVAL
+    big_w = list(args); big_w[7] = big_w[8] = 40_000; big_w[11] = 3 * 40_000 * 40_000 * 2
+    big_w[20] = moe.MOE_PATH_GEMM
+    assert L.moe_expert_ffn(*big_w) == moe.MOE_EUNSUPPORTED
 
 
 def test_cache_host_validation():
