@@ -27,6 +27,8 @@ namespace {
 constexpr int kDotMaxT = 8;     // up to this many tokens per call every expert takes the dot path
 constexpr int kSplitMaxT = 64;  // up to this many, experts are split by rows between the paths
 constexpr int kDotMaxRows = 4;  // rows per expert the dot path takes when splitting
+// Rounds of resident workgroups in the row-split dot-product launches (each loops over items).
+constexpr int kDotSplitRounds = 2;
 
 // ------------------------------------------------------------------ fp32 path
 __global__ __launch_bounds__(64) void f32_gateup(FfnArgs p) {
@@ -139,14 +141,17 @@ extern "C" int moe_expert_ffn(const void* x, int act_dtype, const int32_t* perm,
   // More tokens: split the experts by rows (counted on the device).  Up to kDotMaxRows rows
   // the dot-product kernels stream an expert's weights once at full rate; above that the
   // MFMA kernels take the expert (their cost per row is far lower).  At most
-  // A / (kDotMaxRows + 1) experts have more rows, which bounds the second grid.
+  // A / (kDotMaxRows + 1) experts have more rows, which bounds the second grid.  The first
+  // class has no host-side bound below min(E, A) experts, most of them absent when routing
+  // is skewed, so its launches are capped grids of looping workgroups: an absent item costs
+  // one lookup per workgroup instead of one per (expert, row block).
   FfnArgs few = p, many = p;
   few.nmax = kDotMaxRows;
   many.nmin = kDotMaxRows + 1;
   const int many_max = std::min(E, A / (kDotMaxRows + 1));
-  int rc = launch_ffn_dot(few, y_dtype, stream, experts, 1);
+  int rc = launch_ffn_dot(few, y_dtype, stream, experts, 1, kDotSplitRounds);
   if (rc == MOE_OK) rc = launch_ffn_gemv(many, T, y_dtype, stream, many_max, 1);
-  if (rc == MOE_OK) rc = launch_ffn_dot(few, y_dtype, stream, experts, 2);
+  if (rc == MOE_OK) rc = launch_ffn_dot(few, y_dtype, stream, experts, 2, kDotSplitRounds);
   if (rc == MOE_OK) rc = launch_ffn_gemv(many, T, y_dtype, stream, many_max, 2);
   return rc;
 }

@@ -25,6 +25,7 @@ struct FfnArgs {
   void* y;
   int32_t* status;
   int nmin = 1, nmax = 0x7fffffff;  // only experts with nmin <= rows <= nmax are processed
+  int items = 0x7fffffff;           // work items of a grid-stride launch (set by its launcher)
 };
 
 // Weights of expert e, or nullptr (and MOE_ERANGE) for a missing or stale slot.
@@ -60,12 +61,17 @@ __device__ __forceinline__ int nth_active_expert(const FfnArgs& p, int a) {
   return -1;
 }
 
+int num_cus();  // compute units of the current device (256 if it cannot be read)
+
 // Launchers (argument checks are done by moe_expert_ffn).  Each returns MOE_OK or MOE_EHIP.
 // `experts`: grid size in experts (an upper bound on the experts the row filter admits);
 // `parts`: 1 = gate/up kernel, 2 = down kernel, 3 = both.
 int launch_ffn_gemv(const FfnArgs& p, int T, int y_dtype, hipStream_t stream, int experts,
                     int parts);
-int launch_ffn_dot(const FfnArgs& p, int y_dtype, hipStream_t stream, int experts, int parts);
+// `rounds` > 0: at most that many full rounds of resident workgroups, each looping over
+// (expert, row block) items; 0: one workgroup per item.
+int launch_ffn_dot(const FfnArgs& p, int y_dtype, hipStream_t stream, int experts, int parts,
+                   int rounds = 0);
 bool ffn_dot_supported(int d, int f);  // row lengths the dot-product path handles
 // MXFP4 weights (codes expanded in registers, products on the matrix cores)
 int launch_ffn_mx(const FfnArgs& p, int y_dtype, hipStream_t stream, int experts);

@@ -55,9 +55,11 @@ struct DotItem {
   const uint16_t* w;
 };
 
+template <bool LOOP>
 __device__ __forceinline__ DotItem dot_item(const FfnArgs& p, int a) {
   __shared__ int s_e;
   __shared__ const char* s_w;
+  if (LOOP) __syncthreads();  // every wave has read the previous item's s_e / s_w
   if (threadIdx.x < 64) {
     const int e = nth_active_expert(p, a);
     if (threadIdx.x == 0) {
@@ -82,17 +84,20 @@ __device__ __forceinline__ void stage_rows(uint16_t* lds, const uint16_t* src, i
   __syncthreads();
 }
 
-// Gate/up: workgroup (4 waves) = kDotUPB units of one expert; NCH = 16-byte chunks per lane
-// per row (d <= 512 * NCH).  Dynamic LDS: kDotNTL x d bf16.
-template <int NCH>
-__global__ __launch_bounds__(256) void dot_gateup(FfnArgs p) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t xs[];
+// Gate/up item j = (a, unit block): kDotUPB units of the a-th active expert, one workgroup
+// (4 waves); NCH = 16-byte chunks per lane per row (d <= 512 * NCH).  Dynamic LDS:
+// kDotNTL x d bf16.  Returns false once the a-th active expert does not exist.
+template <int NCH, bool LOOP>
+__device__ __forceinline__ bool gateup_item(const FfnArgs& p, uint16_t* xs, int j) {
   const int nub = p.f / kDotUPB;
-  const int a = blockIdx.x / nub, ub = blockIdx.x - a * nub;
-  const DotItem it = dot_item(p, a);
-  if (it.e < 0 || !it.w) return;
+  const int a = (int)((unsigned)j / (unsigned)nub), ub = j - a * nub;
+  const DotItem it = dot_item<LOOP>(p, a);
+  if (it.e < 0) return false;
+  if (!it.w) return true;
   const int n0 = p.offsets[it.e], n = p.offsets[it.e + 1] - n0;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int tid = threadIdx.x;
+  if (LOOP) asm volatile("" : "+v"(tid));  // lane offsets recomputed per item, not held across items
+  const int lane = tid & 63, wave = threadIdx.x >> 6;
   const int d = p.d, nck = d >> 3;
   uint16_t* H = (uint16_t*)p.h;
   const int u0 = ub * kDotUPB + wave * kDotUPW;
@@ -140,17 +145,33 @@ __global__ __launch_bounds__(256) void dot_gateup(FfnArgs p) {
       }
     }
   }
+  return true;
+}
+
+// One item per workgroup, or (LOOP) a capped grid whose workgroups take items j = blockIdx.x,
+// blockIdx.x + gridDim.x, ... < p.items: items are a-major, so once one finds no expert no
+// later one has one.  The looping form is held to the single-item form's occupancy at d=4096.
+template <int NCH, bool LOOP>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LOOP && NCH == 8 ? 3 : 1)))
+void dot_gateup(FfnArgs p) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t xs[];
+  if (!LOOP) {
+    gateup_item<NCH, false>(p, xs, blockIdx.x);
+    return;
+  }
+  for (int j = blockIdx.x; j < p.items; j += gridDim.x)
+    if (!gateup_item<NCH, true>(p, xs, j)) break;
 }
 
 // Down: workgroup = kDotUPB output channels of one expert; NCH chunks per lane per W_down
 // row (f <= 512 * NCH); the expert's rows of h are contiguous.  Dynamic LDS: kDotNTL x f.
-template <int NCH, int YDT>
-__global__ __launch_bounds__(256) void dot_down(FfnArgs p) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t hs[];
+template <int NCH, int YDT, bool LOOP>
+__device__ __forceinline__ bool down_item(const FfnArgs& p, uint16_t* hs, int j) {
   const int nub = p.d / kDotUPB;
-  const int a = blockIdx.x / nub, ub = blockIdx.x - a * nub;
-  const DotItem it = dot_item(p, a);
-  if (it.e < 0 || !it.w) return;
+  const int a = (int)((unsigned)j / (unsigned)nub), ub = j - a * nub;
+  const DotItem it = dot_item<LOOP>(p, a);
+  if (it.e < 0) return false;
+  if (!it.w) return true;
   const int n0 = p.offsets[it.e], n = p.offsets[it.e + 1] - n0;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int f = p.f, nck = f >> 3;
@@ -197,6 +218,18 @@ __global__ __launch_bounds__(256) void dot_down(FfnArgs p) {
       }
     }
   }
+  return true;
+}
+
+template <int NCH, int YDT, bool LOOP>
+__global__ __launch_bounds__(256) void dot_down(FfnArgs p) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t hs[];
+  if (!LOOP) {
+    down_item<NCH, YDT, false>(p, hs, blockIdx.x);
+    return;
+  }
+  for (int j = blockIdx.x; j < p.items; j += gridDim.x)
+    if (!down_item<NCH, YDT, true>(p, hs, j)) break;
 }
 
 int nch_of(int k_elems) {  // 16-byte chunks per lane for a row of k_elems, or 0 if too long
@@ -204,42 +237,73 @@ int nch_of(int k_elems) {  // 16-byte chunks per lane for a row of k_elems, or 0
   return c <= 2 ? 2 : c <= 4 ? 4 : c <= 8 ? 8 : c <= 16 ? 16 : 0;
 }
 
-template <int NCH>
-void launch_gu(const FfnArgs& p, dim3 g, hipStream_t s) {
-  hipLaunchKernelGGL(dot_gateup<NCH>, g, dim3(256), (size_t)kDotNTL * p.d * 2, s, p);
+// Grid of a launch over `items` items: one workgroup per item, or with rounds > 0 and more
+// items than that many full rounds of resident workgroups, exactly those rounds (the kernel's
+// occupancy at this LDS size, queried from the runtime) of looping workgroups.
+template <typename K>
+int dot_grid(K kernel, size_t lds, int items, int rounds, bool& loop) {
+  loop = false;
+  if (rounds <= 0) return items;
+  int occ = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, 256, lds) != hipSuccess || occ <= 0)
+    occ = 1;
+  const long long cap = (long long)rounds * occ * num_cus();
+  if (items <= cap) return items;
+  loop = true;
+  return (int)cap;
 }
 
 template <int NCH>
-void launch_dn(const FfnArgs& p, dim3 g, bool yf, hipStream_t s) {
+void launch_gu(const FfnArgs& p, int rounds, hipStream_t s) {
+  const size_t lds = (size_t)kDotNTL * p.d * 2;
+  bool loop;
+  const int g = dot_grid(dot_gateup<NCH, true>, lds, p.items, rounds, loop);
+  if (loop) hipLaunchKernelGGL((dot_gateup<NCH, true>), dim3(g), dim3(256), lds, s, p);
+  else hipLaunchKernelGGL((dot_gateup<NCH, false>), dim3(g), dim3(256), lds, s, p);
+}
+
+template <int NCH, int YDT>
+void launch_dn_t(const FfnArgs& p, int rounds, hipStream_t s) {
   const size_t lds = (size_t)kDotNTL * p.f * 2;
-  if (yf) hipLaunchKernelGGL((dot_down<NCH, MOE_F32>), g, dim3(256), lds, s, p);
-  else hipLaunchKernelGGL((dot_down<NCH, MOE_BF16>), g, dim3(256), lds, s, p);
+  bool loop;
+  const int g = dot_grid(dot_down<NCH, YDT, true>, lds, p.items, rounds, loop);
+  if (loop) hipLaunchKernelGGL((dot_down<NCH, YDT, true>), dim3(g), dim3(256), lds, s, p);
+  else hipLaunchKernelGGL((dot_down<NCH, YDT, false>), dim3(g), dim3(256), lds, s, p);
+}
+
+template <int NCH>
+void launch_dn(const FfnArgs& p, bool yf, int rounds, hipStream_t s) {
+  if (yf) launch_dn_t<NCH, MOE_F32>(p, rounds, s);
+  else launch_dn_t<NCH, MOE_BF16>(p, rounds, s);
 }
 
 }  // namespace
 
 bool ffn_dot_supported(int d, int f) { return nch_of(d) > 0 && nch_of(f) > 0; }
 
-int launch_ffn_dot(const FfnArgs& p, int y_dtype, hipStream_t stream, int experts, int parts) {
+int launch_ffn_dot(const FfnArgs& p, int y_dtype, hipStream_t stream, int experts, int parts,
+                   int rounds) {
   if (experts <= 0) return MOE_OK;
-  const dim3 gu(experts * (p.f / kDotUPB)), dn(experts * (p.d / kDotUPB));
+  FfnArgs pg = p, pd = p;
+  pg.items = experts * (p.f / kDotUPB);
+  pd.items = experts * (p.d / kDotUPB);
   const bool yf = y_dtype == MOE_F32;
   if (parts & 1) {
     switch (nch_of(p.d)) {
-      case 2: launch_gu<2>(p, gu, stream); break;
-      case 4: launch_gu<4>(p, gu, stream); break;
-      case 8: launch_gu<8>(p, gu, stream); break;
-      case 16: launch_gu<16>(p, gu, stream); break;
+      case 2: launch_gu<2>(pg, rounds, stream); break;
+      case 4: launch_gu<4>(pg, rounds, stream); break;
+      case 8: launch_gu<8>(pg, rounds, stream); break;
+      case 16: launch_gu<16>(pg, rounds, stream); break;
       default: return MOE_EINVAL;
     }
     MOE_LAUNCH_CHECK();
   }
   if (parts & 2) {
     switch (nch_of(p.f)) {
-      case 2: launch_dn<2>(p, dn, yf, stream); break;
-      case 4: launch_dn<4>(p, dn, yf, stream); break;
-      case 8: launch_dn<8>(p, dn, yf, stream); break;
-      case 16: launch_dn<16>(p, dn, yf, stream); break;
+      case 2: launch_dn<2>(pd, yf, rounds, stream); break;
+      case 4: launch_dn<4>(pd, yf, rounds, stream); break;
+      case 8: launch_dn<8>(pd, yf, rounds, stream); break;
+      case 16: launch_dn<16>(pd, yf, rounds, stream); break;
       default: return MOE_EINVAL;
     }
     MOE_LAUNCH_CHECK();

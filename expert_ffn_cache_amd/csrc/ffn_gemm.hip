@@ -274,6 +274,8 @@ void gemm_tile256(FfnArgs p, int n_ntiles) {
   }
 }
 
+}  // namespace
+
 int num_cus() {
   static int cached[64] = {0};
   int dev = 0;
@@ -286,8 +288,6 @@ int num_cus() {
   }
   return cached[dev];
 }
-
-}  // namespace
 
 // The loaders keep element offsets in 32 bits (token rows of x and h, rows of an entry).
 bool ffn_gemm_supported(long long T, int k, int d, int f) {

@@ -211,14 +211,16 @@ def test_ffn_gemv_decode_shapes(T):
 
 @pytest.mark.parametrize("T,E,k,d,f", [(8, 4, 2, 320, 192), (8, 6, 3, 1088, 448), (5, 16, 4, 4160, 64),
                                        (1, 8, 8, 512, 2048), (7, 64, 6, 2048, 960),
-                                       (24, 32, 4, 512, 256), (64, 64, 6, 384, 320)])
+                                       (24, 32, 4, 512, 256), (64, 64, 6, 384, 320),
+                                       (48, 128, 6, 512, 256)])
 @pytest.mark.parametrize("ydt", [moe.MOE_F32, moe.MOE_BF16])
 def test_ffn_decode_dot_and_mfma_split(T, E, k, d, f, ydt):
     """Weight-streaming calls: up to 8 tokens every expert takes the dot-product kernels
     (any number of rows, staged two at a time); up to 64 tokens experts are split on the
     device by rows between the dot-product and the MFMA kernels.  Row lengths that are not
     multiples of 512 elements (partial last chunk per lane), few experts with many rows,
-    many experts with one row each."""
+    many experts with one row each; more (expert, row block) items than the split launch's
+    workgroups, so each workgroup loops over several."""
     w = configs.Workload("dot_split", seed=23, T=T, d=d, E=E, k=k, f=f, dtype=gen.BF16, alpha=0.5)
     y, ref = _ffn_case(w, moe.MOE_PATH_GEMV, ydt)
     assert_close(y, ref, bf16_tol(ref), f"y_perm T={T} E={E} d={d} f={f}")
