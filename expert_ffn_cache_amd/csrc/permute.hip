@@ -210,18 +210,31 @@ __global__ __launch_bounds__(kThreads) void permute_rank(const int32_t* __restri
   permute_block<FUSED>(ids, A, E, ws, counts, offsets, perm, inv, status);
 }
 
-// Routing and grouping of a few tokens in one workgroup: the four waves route the tokens
-// (route_dev.h), then the workgroup groups the T*k assignments as permute_rank<true> does.
-// The ids written by one wave are read by the others after the barrier (same workgroup).
+// Routing and grouping of a few tokens in one workgroup: wave w routes tokens w, w+4, ...
+// (route_dev.h; all of its logit rows are loaded before the first is ranked), keeping the
+// ids in LDS as well, then the workgroup groups the T*k assignments from LDS as
+// permute_rank<true> does from memory.
 template <int NPL>
 __global__ __launch_bounds__(kThreads) void route_permute_small(
     const float* __restrict__ logits, int T, int E, int k, int32_t* __restrict__ ids,
     float* __restrict__ w, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ perm, int32_t* __restrict__ inv, int32_t* status) {
-  for (int t = threadIdx.x >> 6; t < T; t += kThreads / 64)
-    route_token<NPL>(logits + (size_t)t * E, E, k, ids + (size_t)t * k, w + (size_t)t * k);
+  constexpr int kTPW = kRoutePermuteMaxT / (kThreads / 64);  // tokens per wave
+  __shared__ int32_t s_ids[kRoutePermuteMaxT * kMaxK];
+  const int wave = threadIdx.x >> 6;
+  unsigned long long key[kTPW][NPL];
+#pragma unroll
+  for (int i = 0; i < kTPW; ++i) {
+    const int t = wave + 4 * i;
+    if (t < T) route_keys<NPL>(logits + (size_t)t * E, E, key[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < kTPW; ++i) {
+    const int t = wave + 4 * i;
+    if (t < T) route_pick<NPL>(key[i], k, ids + (size_t)t * k, w + (size_t)t * k, s_ids + t * k);
+  }
   __syncthreads();
-  permute_block<true>(ids, T * k, E, nullptr, counts, offsets, perm, inv, status);
+  permute_block<true>(s_ids, T * k, E, nullptr, counts, offsets, perm, inv, status);
 }
 
 }  // namespace

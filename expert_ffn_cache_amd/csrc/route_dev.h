@@ -28,17 +28,24 @@ __device__ __forceinline__ float from_order_bits(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
-// ids[j], w[j] (j < k) of the token whose E logits are at row; called by a full wave.
+// Keys of one token's E logits at row (lane l: experts l, l+64, ...); called by a full wave.
 template <int NPL>
-__device__ __forceinline__ void route_token(const float* __restrict__ row, int E, int k,
-                                            int32_t* __restrict__ ids, float* __restrict__ w) {
+__device__ __forceinline__ void route_keys(const float* __restrict__ row, int E,
+                                           unsigned long long (&key)[NPL]) {
   const int lane = threadIdx.x & 63;
-  unsigned long long key[NPL];
 #pragma unroll
   for (int i = 0; i < NPL; ++i) {
     const int e = lane + 64 * i;
     key[i] = e < E ? ((unsigned long long)order_bits(row[e]) << 32) | (uint32_t)(~(uint32_t)e) : 0ull;
   }
+}
+
+// ids[j], w[j] (j < k) from a token's keys (consumed); also ids into ids2 when not null.
+template <int NPL>
+__device__ __forceinline__ void route_pick(unsigned long long (&key)[NPL], int k,
+                                           int32_t* __restrict__ ids, float* __restrict__ w,
+                                           int32_t* ids2) {
+  const int lane = threadIdx.x & 63;
   float sel_v = 0.0f, top = 0.0f;
   int sel_id = 0;
   for (int r = 0; r < k; ++r) {
@@ -68,7 +75,17 @@ __device__ __forceinline__ void route_token(const float* __restrict__ row, int E
   if (lane < k) {
     ids[lane] = sel_id;
     w[lane] = ex / sum;
+    if (ids2) ids2[lane] = sel_id;
   }
+}
+
+// ids[j], w[j] (j < k) of the token whose E logits are at row; called by a full wave.
+template <int NPL>
+__device__ __forceinline__ void route_token(const float* __restrict__ row, int E, int k,
+                                            int32_t* __restrict__ ids, float* __restrict__ w) {
+  unsigned long long key[NPL];
+  route_keys<NPL>(row, E, key);
+  route_pick<NPL>(key, k, ids, w, nullptr);
 }
 
 }  // namespace moe
