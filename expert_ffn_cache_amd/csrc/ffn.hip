@@ -5,11 +5,12 @@
 // (the GPU runs the experts it holds on the tokens routed to them: FreeToken
 // RTX-4090 page, component table; SwiGLU form and no biases are a reading).
 //
-// Three paths:
+// Paths by weight type:
 //  * fp32 (MOE_F32 weights): plain fp32 FMA loops in this file; small shapes only.
 //  * GEMV (bf16, decode-shaped counts, a few tokens per expert): weight streaming from
 //    HBM into registers; up to 8 tokens per call with packed bf16 dot products and whole
-//    1 KB row loads (ffn_dot.hip), above that with MFMA (ffn_gemv.hip).
+//    1 KB row loads (ffn_dot.hip), up to 64 tokens split by rows per expert between those
+//    and MFMA (ffn_gemv.hip), above that MFMA alone.
 //  * GEMM (bf16, prefill-shaped counts): LDS-tiled grouped GEMM with direct global->LDS
 //    loads and persistent XCD-aware workgroups, ffn_gemm.hip.
 //  * MXFP4 weights (bf16 activations): codes expanded to bf16 in registers and multiplied

@@ -67,14 +67,16 @@ def decode_arena():
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("T", [1, 8, 64])
-def test_decode_layer_full_size(T, decode_arena):
-    """E=256, k=6, d=4096, f=2048, bf16, all experts resident: every output element."""
-    w = configs.with_(configs.DECODE, T=T)
+@pytest.mark.parametrize("T,alpha", [(1, 0.2), (8, 0.2), (64, 0.2), (16, 1.0), (64, 1.0)])
+def test_decode_layer_full_size(T, alpha, decode_arena):
+    """E=256, k=6, d=4096, f=2048, bf16, all experts resident: every output element.  Above
+    8 tokens the experts are split by rows and the few-row launches loop over their items;
+    alpha=1 (skewed routing) leaves most of those items without an expert."""
+    w = configs.with_(configs.DECODE, T=T, alpha=alpha)
     x, lg, L, _ = _run_layer(w, arena=decode_arena)
     ids, wt, ref = oracle.moe_layer(x, lg, w.k, oracle_table(w, sorted(set(oracle.route(lg, w.k)[0].ravel().tolist()))))
     np.testing.assert_array_equal(L.ids.cpu().numpy(), ids)
-    assert_close(L.out.cpu().numpy(), ref, bf16_tol(ref), f"decode T={T}")
+    assert_close(L.out.cpu().numpy(), ref, bf16_tol(ref), f"decode T={T} alpha={alpha}")
     assert int(L.status.item()) == 0
 
 
