@@ -160,6 +160,27 @@ def bench_decode(args, torch, moe, T, alpha, arena, dtype=None):
         e1.record(s)
         torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
+    # the same R layer forwards captured back to back in one graph (as a serving step runs
+    # its layers): per-layer time without the launch gap between single-layer replays
+    ms_multi = None
+    if not args.no_graph:
+        with torch.cuda.stream(s):
+            gm = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gm, stream=s):
+                for r in range(R):
+                    layers[r].forward(x, logits[r], arena, w.entry_bytes, stream=s)
+            gm.replay()
+            s.synchronize()
+            reps = max(1, args.steps // R)
+            e2, e3 = _events(torch, 2)
+            torch.cuda.synchronize()
+            e2.record(s)
+            for _ in range(reps):
+                gm.replay()
+            e3.record(s)
+            torch.cuda.synchronize()
+            ms_multi = e2.elapsed_time(e3) / (reps * R)
+            del gm
     # the dominant entry point (expert FFN: gate/up + down weight-streaming kernels), timed
     # per call with events on its stream
     ffn_ms = []
@@ -190,6 +211,8 @@ def bench_decode(args, torch, moe, T, alpha, arena, dtype=None):
     return dict(
         workload=w.name, T=w.T, ms_per_step=ms, tok_s=w.T / (ms * 1e-3), U_mean=float(np.mean(U)),
         ffn_ms=ffn_avg_ms,
+        ms_per_layer_in_16_layer_graph=ms_multi,
+        tok_s_16_layer_graph=None if ms_multi is None else w.T / (ms_multi * 1e-3),
         roofline=dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
                       frac=achieved / HBM_PEAK_GBS,
                       traffic=None if traffic is None else traffic),
@@ -628,6 +651,9 @@ def main():
         dec = bench_decode(args, torch, moe, args.decode_T, args.alpha, arena, wfmt)
         log(f"[decode] {dec['tok_s']:.0f} tok/s, {dec['ms_per_step'] * 1e3:.1f} us/layer, "
             f"ffn {dec['ffn_ms'] * 1e3:.1f} us, {dec['roofline']['achieved']:.0f} GB/s")
+        if dec["ms_per_layer_in_16_layer_graph"] is not None:
+            log(f"[decode] 16 layers per graph: {dec['tok_s_16_layer_graph']:.0f} tok/s, "
+                f"{dec['ms_per_layer_in_16_layer_graph'] * 1e3:.1f} us/layer")
         if not args.no_sweep and wfmt is None:
             sweep = {}
             for T, alpha in ((1, 0.2), (64, 0.2), (8, 1.0), (64, 1.0)):
@@ -696,7 +722,8 @@ def main():
         "roofline": dec["roofline"],
         "cpu_baseline": cpu,
         "extra": dict(decode_ffn_ms=dec["ffn_ms"], decode_unique_experts=dec["U_mean"],
-                      decode_algorithmic_bytes_per_ffn=dec["algorithmic_bytes_per_call"], **extra),
+                      decode_algorithmic_bytes_per_ffn=dec["algorithmic_bytes_per_call"],
+                      decode_tok_s_16_layer_graph=dec["tok_s_16_layer_graph"], **extra),
     }
     print(json.dumps(line))
 
