@@ -212,7 +212,7 @@ def test_ffn_gemv_decode_shapes(T):
 @pytest.mark.parametrize("T,E,k,d,f", [(8, 4, 2, 320, 192), (8, 6, 3, 1088, 448), (5, 16, 4, 4160, 64),
                                        (1, 8, 8, 512, 2048), (7, 64, 6, 2048, 960),
                                        (24, 32, 4, 512, 256), (64, 64, 6, 384, 320),
-                                       (48, 128, 6, 512, 256)])
+                                       (48, 256, 6, 512, 256)])
 @pytest.mark.parametrize("ydt", [moe.MOE_F32, moe.MOE_BF16])
 def test_ffn_decode_dot_and_mfma_split(T, E, k, d, f, ydt):
     """Weight-streaming calls: up to 8 tokens every expert takes the dot-product kernels
@@ -224,6 +224,48 @@ def test_ffn_decode_dot_and_mfma_split(T, E, k, d, f, ydt):
     w = configs.Workload("dot_split", seed=23, T=T, d=d, E=E, k=k, f=f, dtype=gen.BF16, alpha=0.5)
     y, ref = _ffn_case(w, moe.MOE_PATH_GEMV, ydt)
     assert_close(y, ref, bf16_tol(ref), f"y_perm T={T} E={E} d={d} f={f}")
+
+
+@pytest.mark.parametrize("ydt", [moe.MOE_F32, moe.MOE_BF16])
+def test_ffn_split_stale_slot_skips_only_that_expert(ydt):
+    """Key-checked slots on the row-split path (T=48: more items than the looping launches'
+    workgroups): a stale slot of one few-row expert and of one many-row expert sets
+    MOE_ERANGE and leaves exactly those experts' rows unwritten; the looping workgroups go on
+    to the items after them, so every other row still equals the oracle."""
+    w = configs.Workload("split_stale", seed=29, T=48, d=512, E=256, k=6, f=256,
+                         dtype=gen.BF16, alpha=0.5)
+    x = configs.gen_x(w)
+    lg = configs.gen_logits(w)
+    ids, _ = oracle.route(lg, w.k)
+    counts, offsets, perm, inv = oracle.permute(ids, w.E)
+    few = [e for e in range(w.E) if 1 <= counts[e] <= 4]
+    many = [e for e in range(w.E) if counts[e] > 4]
+    assert few and many
+    stale = {few[len(few) // 2], many[0]}
+    arena = device_arena_all_experts(w)
+    slots = dev(np.arange(w.E, dtype=np.int32))
+    keys = np.arange(w.E, dtype=np.int32)
+    for e in stale:
+        keys[e] = -7
+    A = w.T * w.k
+    nws = moe.moe_expert_ffn_workspace_bytes(w.T, w.k, w.f, w.act_dtype)
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+    ytd = torch.float32 if ydt == moe.MOE_F32 else torch.bfloat16
+    y = torch.full((A, w.d), float("nan"), dtype=ytd, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    moe.moe_expert_ffn(x_device(w, x), w.act_dtype, dev(perm), dev(offsets), w.T, w.k, w.E, w.d,
+                       w.f, slots, arena, w.entry_bytes, w.dtype, None, dev(keys), 0, ws, nws, y,
+                       ydt, moe.MOE_PATH_AUTO, status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == moe.MOE_ERANGE
+    yv = np_of(y)
+    bad = np.zeros(A, dtype=bool)
+    for e in stale:
+        bad[offsets[e]:offsets[e + 1]] = True
+    assert np.isnan(yv[bad]).all()
+    table = oracle_table(w, sorted(set(ids.ravel().tolist())))
+    ref = oracle.expert_ffn(x, ids, table, perm)
+    assert_close(yv[~bad], ref[~bad], bf16_tol(ref), "rows of the other experts")
 
 
 @pytest.mark.parametrize("T,E,k,d,f", [(8, 16, 6, 512, 256), (1, 8, 4, 4096, 2048), (8, 4, 2, 320, 192),
