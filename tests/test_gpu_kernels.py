@@ -304,3 +304,78 @@ def test_ffn_gemm_wide_n_tiles():
                          alpha=1.0)
     y, ref = _ffn_case(w, moe.MOE_PATH_GEMM)
     assert_close(y, ref, bf16_tol(ref), "y_perm gemm")
+
+
+# ---------------------------------------------------------------- degenerate FFN calls
+def _ffn_masked(w, path, mask=None, ydt=moe.MOE_F32):
+    """As _ffn_case with an optional expert mask; returns (y, ref, offsets) with y NaN-filled
+    where nothing was written."""
+    x = configs.gen_x(w)
+    lg = configs.gen_logits(w)
+    ids, _ = oracle.route(lg, w.k)
+    counts, offsets, perm, inv = oracle.permute(ids, w.E)
+    arena = device_arena_all_experts(w)
+    A = w.T * w.k
+    nws = moe.moe_expert_ffn_workspace_bytes(w.T, w.k, w.f, w.act_dtype)
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+    ytd = torch.float32 if ydt == moe.MOE_F32 else torch.bfloat16
+    y = torch.full((A, w.d), float("nan"), dtype=ytd, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    moe.moe_expert_ffn(x_device(w, x), w.act_dtype, dev(perm), dev(offsets), w.T, w.k, w.E, w.d,
+                       w.f, None, arena, w.entry_bytes, w.dtype,
+                       None if mask is None else dev(mask.astype(np.uint8)), None, 0, ws, nws,
+                       y, ydt, path, status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    table = oracle_table(w, sorted(set(ids.ravel().tolist())))
+    return np_of(y), oracle.expert_ffn(x, ids, table, perm), offsets
+
+
+_PATHS = [moe.MOE_PATH_AUTO, moe.MOE_PATH_GEMV, moe.MOE_PATH_GEMM]
+
+
+@pytest.mark.parametrize("dtype", [gen.BF16, gen.MXFP4])
+@pytest.mark.parametrize("path", _PATHS)
+@pytest.mark.parametrize("T,E,k", [(5, 1, 1), (6, 4, 4), (24, 3, 3)])
+def test_ffn_single_expert_and_all_experts(T, E, k, path, dtype):
+    """E = 1 (every token to the one expert: a dense SwiGLU FFN) and k = E (every token to
+    every expert), on each path, bf16 and MXFP4 weights."""
+    w = configs.Workload("degenerate", seed=41 + T + E, T=T, d=192, E=E, k=k, f=128,
+                         dtype=dtype, alpha=0.5)
+    y, ref, _ = _ffn_masked(w, path)
+    assert_close(y, ref, bf16_tol(ref), f"E={E} k={k} path={path}")
+
+
+@pytest.mark.parametrize("dtype", [gen.BF16, gen.MXFP4])
+@pytest.mark.parametrize("path", _PATHS)
+def test_ffn_zero_tokens_writes_nothing(path, dtype):
+    w = configs.Workload("empty", seed=43, T=1, d=128, E=8, k=2, f=64, dtype=dtype, alpha=0.5)
+    arena = device_arena_all_experts(w)
+    y = torch.full((1, w.d), float("nan"), device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    one = dev(np.zeros(w.E + 1, dtype=np.int32))
+    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    xb = torch.zeros((1, w.d), dtype=torch.bfloat16, device="cuda")
+    moe.moe_expert_ffn(xb, w.act_dtype, one, one, 0, w.k, w.E, w.d, w.f, None, arena,
+                       w.entry_bytes, w.dtype, None, None, 0, ws, 256, y, moe.MOE_F32, path, status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0 and torch.isnan(y).all()
+
+
+@pytest.mark.parametrize("dtype", [gen.BF16, gen.MXFP4])
+@pytest.mark.parametrize("T,path", [(8, moe.MOE_PATH_GEMV), (48, moe.MOE_PATH_GEMV),
+                                    (100, moe.MOE_PATH_GEMV), (300, moe.MOE_PATH_GEMM)])
+def test_ffn_expert_mask_selects_experts(T, path, dtype):
+    """expert_mask runs only the flagged experts: their rows equal the oracle, every other
+    row is left as it was (one-item, looping row-split and grouped-GEMM launches)."""
+    w = configs.Workload("masked", seed=47 + T, T=T, d=512, E=256, k=6, f=256, dtype=dtype,
+                         alpha=0.5)
+    mask = np.zeros(w.E, dtype=bool)
+    mask[np.random.default_rng(T).permutation(w.E)[: w.E // 3]] = True
+    y, ref, offsets = _ffn_masked(w, path, mask)
+    on = np.zeros(w.T * w.k, dtype=bool)
+    for e in np.flatnonzero(mask):
+        on[offsets[e]:offsets[e + 1]] = True
+    assert on.any() and (~on).any()
+    assert np.isnan(y[~on]).all()
+    assert_close(y[on], ref[on], bf16_tol(ref), f"masked rows T={T} path={path}")
