@@ -45,11 +45,12 @@ def _mk_event(torch, stream, timing=False):
     return ev
 
 
-def _ffn_bytes(w, U):
+def _ffn_bytes(w, U, y_bytes=4):
     """Algorithmic HBM bytes of one expert-FFN call: every used expert entry once, token rows
-    gathered once per assignment, h written and read once (bf16), y written once (fp32)."""
+    gathered once per assignment, h written and read once (bf16), y written once (fp32, or
+    y_bytes per element)."""
     A = w.T * w.k
-    return U * w.entry_bytes + A * w.d * 2 + 2 * A * w.f * 2 + A * w.d * 4
+    return U * w.entry_bytes + A * w.d * 2 + 2 * A * w.f * 2 + A * w.d * y_bytes
 
 
 _STREAMS = {}
@@ -272,13 +273,17 @@ def bench_prefill(args, torch, moe, dtype=None):
         if status != 0:
             raise RuntimeError(f"prefill: device status {status}")
         fl = _ffn_flops(w)
-        byts = float(np.mean([_ffn_bytes(w, u) for u in U]))
+        byts = float(np.mean([_ffn_bytes(w, u, y_bytes=2) for u in U]))
+        # the binding roof: the larger of the MFMA-peak and HBM-peak times of the call
+        t_mfma, t_hbm = fl / (BF16_PEAK_TFLOPS * 1e12) * 1e3, byts / (HBM_PEAK_GBS * 1e9) * 1e3
         out[f"alpha_{alpha}"] = dict(
             T=w.T, ms_per_step=ms, tok_s=w.T / (ms * 1e-3), ffn_ms=ffn_ms, U_mean=float(np.mean(U)),
             max_tokens_per_expert=int(np.max(maxc)),
             ffn_tflops=fl / (ffn_ms * 1e-3) / 1e12, mfma_frac=fl / (ffn_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
             ffn_weight_gbs=byts / (ffn_ms * 1e-3) / 1e9,
-            hbm_frac=byts / (ffn_ms * 1e-3) / 1e9 / HBM_PEAK_GBS)
+            hbm_frac=byts / (ffn_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            roofline_bound="hbm" if t_hbm >= t_mfma else "mfma",
+            roofline_floor_ms=max(t_mfma, t_hbm), roofline_frac=max(t_mfma, t_hbm) / ffn_ms)
         del graphs, layers
     out["workload"] = base.name
     del arena
