@@ -461,3 +461,40 @@ def test_resize_shrink_grow_mid_trace_matches_oracle():
         _compare_tables(dc, sim)
         _arena_holds_pool(dc, arena, pool, w)
     assert int(dc.status.item()) == 0
+
+
+@pytest.mark.parametrize("sizes", [{0: 5}, {3: 1, 4: 7}, {5: 24}])
+def test_resize_edge_cases_match_oracle(sizes):
+    """Resize of a freshly initialised (empty) cache, a shrink to a single slot followed by a
+    grow, and a resize to the same slot count: tables equal LruSim.resized's, the arena keeps
+    the pool entries, and the later lookups match the simulator."""
+    w = configs.Workload("lru_resize_edge", seed=53, T=1, d=64, E=12, k=1, f=64,
+                         dtype=gen.BF16, L=2, S=24, alpha=0.5)
+    pool = host_pool(w)
+    steps = 8
+    ids, _ = gen.markov_routing(w.seed, steps, w.L, w.T, w.E, w.k, 0.6, 1.1)
+    ids_dev = dev(ids)
+    arena = torch.zeros((w.S, w.entry_elems), dtype=torch.bfloat16, device="cuda")
+    dc = DevCache(w.L, w.E, w.S, w.entry_bytes, arena, pool)
+    sim = LruSim(w.L, w.E, w.S)
+    for s in range(steps):
+        if s in sizes:
+            S2 = sizes[s]
+            arena2 = torch.zeros((S2, w.entry_elems), dtype=torch.bfloat16, device="cuda")
+            dc2 = DevCache(w.L, w.E, S2, w.entry_bytes, arena2, pool)
+            moe.cache_resize(dc.desc, dc2.desc)
+            torch.cuda.synchronize()
+            sim = sim.resized(S2)
+            dc, arena = dc2, arena2
+            _compare_tables(dc, sim)
+            _arena_holds_pool(dc, arena, pool, w)
+            assert int(dc.clock.item()) == sim.clock
+        for layer in range(w.L):
+            dc.lookup(layer, ids_dev[s, layer], w.T, w.k)
+            moe.cache_fill_device(dc.desc, dc.fills, dc.n_fills, w.E)
+            slot_ref, fills = sim.step(layer, ids[s, layer])
+            assert dc.fills_host() == [tuple(f) for f in fills], (s, layer)
+            np.testing.assert_array_equal(dc.expert_slot.cpu().numpy(), slot_ref)
+        _compare_tables(dc, sim)
+        _arena_holds_pool(dc, arena, pool, w)
+    assert int(dc.status.item()) == 0
