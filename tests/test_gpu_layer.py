@@ -138,12 +138,16 @@ def test_prefill_layer_full_size_sampled_mxfp4():
     del arena
 
 
-def test_layer_is_deterministic_and_graph_replayable():
-    """Two eager runs are bit-identical; a captured graph replayed on new logits matches eager."""
-    w = configs.with_(configs.DECODE, T=8, E=32, d=512, f=256)
+@pytest.mark.parametrize("T,E,dtype", [(8, 32, gen.BF16), (24, 256, gen.BF16), (48, 256, gen.BF16),
+                                       (300, 32, gen.BF16), (8, 32, gen.MXFP4), (300, 32, gen.MXFP4)])
+def test_layer_is_deterministic_and_graph_replayable(T, E, dtype):
+    """Two eager runs are bit-identical; a captured graph replayed on new logits matches eager
+    on every replay (one-item and looping weight-streaming launches, grouped GEMM; bf16 and
+    MXFP4 experts)."""
+    w = configs.with_(configs.DECODE, T=T, E=E, d=512, f=256, dtype=dtype)
     x = x_device(w, configs.gen_x(w))
     arena = device_arena_all_experts(w)
-    L = MoeLayer(w.T, w.E, w.k, w.d, w.f)
+    L = MoeLayer(w.T, w.E, w.k, w.d, w.f, w_dtype=w.dtype)
     lg_in = torch.empty((w.T, w.E), dtype=torch.float32, device="cuda")
     outs = []
     for rot in range(3):
