@@ -105,14 +105,16 @@ def test_prefill_layer_full_size_sampled(alpha, decode_arena):
     del arena
 
 
-def test_decode_layer_full_size_mxfp4():
-    """The decode layer with MXFP4 experts (E=256, k=6, d=4096, f=2048, T=8, all experts
-    resident): every output element against the oracle on the exactly dequantised weights."""
-    w = configs.with_(configs.DECODE, dtype=gen.MXFP4)
+@pytest.mark.parametrize("T,alpha", [(1, 0.2), (8, 0.2), (64, 1.0)])
+def test_decode_layer_full_size_mxfp4(T, alpha):
+    """The decode layer with MXFP4 experts (E=256, k=6, d=4096, f=2048, all experts
+    resident; T=1 splits each strip over 4 waves, T=8 and 64 give each wave whole strips):
+    every output element against the oracle on the exactly dequantised weights."""
+    w = configs.with_(configs.DECODE, dtype=gen.MXFP4, T=T, alpha=alpha)
     x, lg, L, arena = _run_layer(w)
     ids, wt, ref = oracle.moe_layer(x, lg, w.k, oracle_table(w, sorted(set(oracle.route(lg, w.k)[0].ravel().tolist()))))
     np.testing.assert_array_equal(L.ids.cpu().numpy(), ids)
-    assert_close(L.out.cpu().numpy(), ref, bf16_tol(ref), "decode mxfp4 T=8")
+    assert_close(L.out.cpu().numpy(), ref, bf16_tol(ref), f"decode mxfp4 T={T} alpha={alpha}")
     assert int(L.status.item()) == 0
     del arena
 
