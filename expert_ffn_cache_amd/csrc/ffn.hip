@@ -28,6 +28,7 @@ namespace {
 constexpr int kDotMaxT = 8;     // up to this many tokens per call every expert takes the dot path
 constexpr int kSplitMaxT = 64;  // up to this many, experts are split by rows between the paths
 constexpr int kDotMaxRows = 4;  // rows per expert the dot path takes when splitting
+constexpr int kMxMaxRows = 16;  // rows an MXFP4 expert may have on the weight-streaming path
 // Rounds of resident workgroups in the row-split dot-product launches (each loops over items).
 constexpr int kDotSplitRounds = 2;
 
@@ -129,7 +130,20 @@ extern "C" int moe_expert_ffn(const void* x, int act_dtype, const int32_t* perm,
   if (mx) {
     const bool gemm = path == MOE_PATH_GEMM || (path == MOE_PATH_AUTO && (long long)T * k > 8ll * E) ||
                       !ffn_mx_supported(d, f);
-    return gemm ? launch_ffn_mx_gemm(p, T, y_dtype, stream) : launch_ffn_mx(p, y_dtype, stream, std::min(E, T * k));
+    if (gemm) return launch_ffn_mx_gemm(p, T, y_dtype, stream);
+    const int A = T * k, experts = std::min(E, A);
+    // An expert has at most T rows (a token picks it once).  The weight-streaming MXFP4
+    // kernels stage 4 token rows per pass and stream the expert's weights once per pass, so
+    // above kMxMaxRows rows an expert goes to the grouped GEMM, which streams them once per
+    // 64 rows and pays a fixed start-up per workgroup instead.  At most A / (kMxMaxRows + 1)
+    // experts have more rows.
+    if (T <= kMxMaxRows) return launch_ffn_mx(p, y_dtype, stream, experts);
+    FfnArgs few = p, many = p;
+    few.nmax = kMxMaxRows;
+    many.nmin = kMxMaxRows + 1;
+    int rc = launch_ffn_mx(few, y_dtype, stream, experts);
+    if (rc == MOE_OK) rc = launch_ffn_mx_gemm(many, T, y_dtype, stream, std::max(1, A / (kMxMaxRows + 1)));
+    return rc;
   }
   // Past the GEMM's size limit the weight-streaming kernels (64-bit offsets) take the call.
   if (path == MOE_PATH_AUTO)

@@ -76,7 +76,8 @@ bool ffn_dot_supported(int d, int f);  // row lengths the dot-product path handl
 // MXFP4 weights (codes expanded in registers, products on the matrix cores)
 int launch_ffn_mx(const FfnArgs& p, int y_dtype, hipStream_t stream, int experts);
 bool ffn_mx_supported(int d, int f);  // shapes the weight-streaming MXFP4 kernels handle
-int launch_ffn_mx_gemm(const FfnArgs& p, int T, int y_dtype, hipStream_t stream);
+// `experts` > 0: at most that many experts pass the row filter (bounds the grid).
+int launch_ffn_mx_gemm(const FfnArgs& p, int T, int y_dtype, hipStream_t stream, int experts = 0);
 bool ffn_gemm_supported(long long T, int k, int d, int f);
 int launch_ffn_gemm(const FfnArgs& p, int y_dtype, hipStream_t stream);
 

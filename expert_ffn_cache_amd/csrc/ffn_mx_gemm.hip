@@ -296,10 +296,10 @@ __global__ __launch_bounds__(256) void mg_down(FfnArgs p) {
 
 }  // namespace
 
-int launch_ffn_mx_gemm(const FfnArgs& p, int T, int y_dtype, hipStream_t stream) {
+int launch_ffn_mx_gemm(const FfnArgs& p, int T, int y_dtype, hipStream_t stream, int experts) {
   // (expert, 64-row block) pairs: at most T*k/64 + (number of experts with rows)
   const long A = (long)T * p.k;
-  const long mbs = A / kMgM + std::min<long>(p.E, A);
+  const long mbs = A / kMgM + std::min<long>(experts > 0 ? std::min(experts, p.E) : p.E, A);
   auto grid = [&](int R) {
     const long g = mbs * ((R + kMgN - 1) / kMgN);
     return dim3((unsigned)((g + 7) / 8 * 8));

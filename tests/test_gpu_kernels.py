@@ -284,6 +284,21 @@ def test_ffn_mxfp4_parity(T, E, k, d, f, ydt):
     assert_close(y, ref, bf16_tol(ref), f"y_perm mxfp4 T={T} d={d} f={f}")
 
 
+@pytest.mark.parametrize("T,E,k,d,f,alpha", [(64, 64, 4, 512, 256, 1.0), (48, 256, 6, 1088, 320, 1.0),
+                                             (32, 32, 4, 320, 192, 0.5)])
+@pytest.mark.parametrize("ydt", [moe.MOE_F32, moe.MOE_BF16])
+def test_ffn_mxfp4_row_split_parity(T, E, k, d, f, alpha, ydt):
+    """MXFP4 decode-shaped calls above 16 tokens: experts with at most 16 rows stay on the
+    weight-streaming kernels, the others go to the grouped GEMM; both groups are present and
+    every row equals the oracle."""
+    w = configs.Workload("mx_split", seed=27, T=T, d=d, E=E, k=k, f=f, dtype=gen.MXFP4, alpha=alpha)
+    ids, _ = oracle.route(configs.gen_logits(w), w.k)
+    counts = np.bincount(ids.ravel(), minlength=w.E)
+    assert (counts > 16).any() and ((counts > 0) & (counts <= 16)).any()
+    y, ref = _ffn_case(w, moe.MOE_PATH_AUTO, ydt)
+    assert_close(y, ref, bf16_tol(ref), f"y_perm mxfp4 split T={T} E={E}")
+
+
 @pytest.mark.parametrize("T,E,k,d,f,alpha,path", [
     (300, 8, 2, 512, 256, 0.5, moe.MOE_PATH_AUTO),     # several 64-row blocks per expert
     (200, 6, 3, 320, 192, 0.5, moe.MOE_PATH_AUTO),     # short last tiles, partial weight blocks
