@@ -127,6 +127,7 @@ def bench_decode(args, torch, moe, T, alpha, arena, dtype=None):
     w = configs.with_(configs.DECODE, T=T, alpha=alpha)
     if dtype is not None:
         w = configs.with_(w, dtype=dtype)
+    path = {"auto": moe.MOE_PATH_AUTO, "gemv": moe.MOE_PATH_GEMV, "gemm": moe.MOE_PATH_GEMM}[args.ffn_path]
     R = 16
     x = torch.from_numpy(configs.gen_x(w).view(np.int16)).view(torch.bfloat16).cuda()
     logits = [torch.from_numpy(configs.gen_logits(w, rotation=r)).cuda() for r in range(R)]
@@ -135,19 +136,19 @@ def bench_decode(args, torch, moe, T, alpha, arena, dtype=None):
     graphs = []
     with torch.cuda.stream(s):
         for r in range(R):
-            layers[r].forward(x, logits[r], arena, w.entry_bytes, stream=s)
+            layers[r].forward(x, logits[r], arena, w.entry_bytes, path=path, stream=s)
         s.synchronize()
         U = [int((layers[r].counts > 0).sum().item()) for r in range(R)]
         if not args.no_graph:
             for r in range(R):
                 g = torch.cuda.CUDAGraph()
                 with torch.cuda.graph(g, stream=s):
-                    layers[r].forward(x, logits[r], arena, w.entry_bytes, stream=s)
+                    layers[r].forward(x, logits[r], arena, w.entry_bytes, path=path, stream=s)
                 graphs.append(g)
 
         def run(i):
             if args.no_graph:
-                layers[i % R].forward(x, logits[i % R], arena, w.entry_bytes, stream=s)
+                layers[i % R].forward(x, logits[i % R], arena, w.entry_bytes, path=path, stream=s)
             else:
                 graphs[i % R].replay()
         for i in range(args.warmup):
@@ -169,7 +170,7 @@ def bench_decode(args, torch, moe, T, alpha, arena, dtype=None):
             gm = torch.cuda.CUDAGraph()
             with torch.cuda.graph(gm, stream=s):
                 for r in range(R):
-                    layers[r].forward(x, logits[r], arena, w.entry_bytes, stream=s)
+                    layers[r].forward(x, logits[r], arena, w.entry_bytes, path=path, stream=s)
             gm.replay()
             s.synchronize()
             reps = max(1, args.steps // R)
@@ -191,7 +192,7 @@ def bench_decode(args, torch, moe, T, alpha, arena, dtype=None):
         for i in range(n):
             r = i % R
             starts[i].record(s)
-            layers[r].ffn(x, arena, w.entry_bytes, stream=s)
+            layers[r].ffn(x, arena, w.entry_bytes, path=path, stream=s)
             ends[i].record(s)
         torch.cuda.synchronize()
         ffn_ms = [starts[i].elapsed_time(ends[i]) for i in range(n)]
@@ -626,6 +627,8 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="eager launches instead of graph replay")
     ap.add_argument("--decode-T", type=int, default=8)
     ap.add_argument("--alpha", type=float, default=0.2)
+    ap.add_argument("--ffn-path", choices=["auto", "gemv", "gemm"], default="auto",
+                    help="expert-FFN path of the decode workload (auto: chosen by the library)")
     ap.add_argument("--lru-steps", type=int, default=512)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")

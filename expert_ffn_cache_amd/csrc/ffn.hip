@@ -29,6 +29,10 @@ constexpr int kDotMaxT = 8;     // up to this many tokens per call every expert 
 constexpr int kSplitMaxT = 64;  // up to this many, experts are split by rows between the paths
 constexpr int kDotMaxRows = 4;  // rows per expert the dot path takes when splitting
 constexpr int kMxMaxRows = 16;  // rows an MXFP4 expert may have on the weight-streaming path
+// AUTO path: bf16 experts take the grouped GEMM above this many rows per expert on average
+// (T*k / E), MXFP4 experts above kMxGemmMinRowsPerExpert (their streaming path, with the row
+// split above, stays ahead to about 5 rows per expert at Zipf 0.2 and beyond 8 when skewed).
+constexpr long long kGemmMinRowsPerExpert = 2, kMxGemmMinRowsPerExpert = 8;
 // Rounds of resident workgroups in the row-split dot-product launches (each loops over items).
 constexpr int kDotSplitRounds = 2;
 
@@ -128,7 +132,8 @@ extern "C" int moe_expert_ffn(const void* x, int act_dtype, const int32_t* perm,
     return MOE_OK;
   }
   if (mx) {
-    const bool gemm = path == MOE_PATH_GEMM || (path == MOE_PATH_AUTO && (long long)T * k > 8ll * E) ||
+    const bool gemm = path == MOE_PATH_GEMM ||
+                      (path == MOE_PATH_AUTO && (long long)T * k > kMxGemmMinRowsPerExpert * E) ||
                       !ffn_mx_supported(d, f);
     if (gemm) return launch_ffn_mx_gemm(p, T, y_dtype, stream);
     const int A = T * k, experts = std::min(E, A);
@@ -145,9 +150,12 @@ extern "C" int moe_expert_ffn(const void* x, int act_dtype, const int32_t* perm,
     if (rc == MOE_OK) rc = launch_ffn_mx_gemm(many, T, y_dtype, stream, std::max(1, A / (kMxMaxRows + 1)));
     return rc;
   }
-  // Past the GEMM's size limit the weight-streaming kernels (64-bit offsets) take the call.
+  // bf16: the grouped GEMM from more than 2 rows per expert on average (measured crossover
+  // near 2 at Zipf 0.2; with skewed routing the GEMM wins from fewer tokens still, as its
+  // 256-row tiles read a hot expert's weights once per 256 rows).  Past the GEMM's size limit
+  // the weight-streaming kernels (64-bit offsets) take the call.
   if (path == MOE_PATH_AUTO)
-    path = (long long)T * k <= 8ll * E || !bf16_gemm_fits ? MOE_PATH_GEMV : MOE_PATH_GEMM;
+    path = (long long)T * k <= kGemmMinRowsPerExpert * E || !bf16_gemm_fits ? MOE_PATH_GEMV : MOE_PATH_GEMM;
   if (path == MOE_PATH_GEMM) return launch_ffn_gemm(p, y_dtype, stream);
   const int A = T * k, experts = std::min(E, A);
   if (T > kSplitMaxT || !ffn_dot_supported(d, f))

@@ -149,7 +149,8 @@ size_t moe_entry_bytes(int d, int f, int w_dtype);
 /* Workspace bytes moe_expert_ffn needs (the SwiGLU intermediate, [T*k][f]). */
 size_t moe_expert_ffn_workspace_bytes(int T, int k, int f, int act_dtype);
 
-#define MOE_PATH_AUTO 0 /* chosen from T*k/E on the host */
+#define MOE_PATH_AUTO 0 /* chosen from T*k/E on the host: the grouped GEMM above 2 rows per \
+                           expert on average for bf16 weights, above 8 for MXFP4 */
 #define MOE_PATH_GEMV 1 /* weight-streaming skinny path (decode-shaped counts) */
 #define MOE_PATH_GEMM 2 /* LDS-tiled grouped GEMM (prefill-shaped counts) */
 
