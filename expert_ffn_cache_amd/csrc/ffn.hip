@@ -9,8 +9,8 @@
 //  * fp32 (MOE_F32 weights): plain fp32 FMA loops in this file; small shapes only.
 //  * GEMV (bf16, decode-shaped counts, a few tokens per expert): weight streaming from
 //    HBM into registers; up to 8 tokens per call with packed bf16 dot products and whole
-//    1 KB row loads (ffn_dot.hip), up to 64 tokens split by rows per expert between those
-//    and MFMA (ffn_gemv.hip), above that MFMA alone.
+//    1 KB row loads (ffn_dot.hip), above that split by rows per expert between those and
+//    MFMA (ffn_gemv.hip).
 //  * GEMM (bf16, prefill-shaped counts): LDS-tiled grouped GEMM with direct global->LDS
 //    loads and persistent XCD-aware workgroups, ffn_gemm.hip.
 //  * MXFP4 weights (bf16 activations): codes expanded to bf16 in registers and multiplied
@@ -26,7 +26,6 @@ using namespace moe;
 namespace {
 
 constexpr int kDotMaxT = 8;     // up to this many tokens per call every expert takes the dot path
-constexpr int kSplitMaxT = 64;  // up to this many, experts are split by rows between the paths
 constexpr int kDotMaxRows = 4;  // rows per expert the dot path takes when splitting
 constexpr int kMxMaxRows = 16;  // rows an MXFP4 expert may have on the weight-streaming path
 // AUTO path: bf16 experts take the grouped GEMM above this many rows per expert on average
@@ -158,10 +157,9 @@ extern "C" int moe_expert_ffn(const void* x, int act_dtype, const int32_t* perm,
     path = (long long)T * k <= kGemmMinRowsPerExpert * E || !bf16_gemm_fits ? MOE_PATH_GEMV : MOE_PATH_GEMM;
   if (path == MOE_PATH_GEMM) return launch_ffn_gemm(p, y_dtype, stream);
   const int A = T * k, experts = std::min(E, A);
-  if (T > kSplitMaxT || !ffn_dot_supported(d, f))
-    return launch_ffn_gemv(p, T, y_dtype, stream, experts, 3);
+  if (!ffn_dot_supported(d, f)) return launch_ffn_gemv(p, T, y_dtype, stream, experts, 3);
   if (T <= kDotMaxT) return launch_ffn_dot(p, y_dtype, stream, experts, 3);
-  // More tokens: split the experts by rows (counted on the device).  Up to kDotMaxRows rows
+  // More tokens: split the experts by rows (counted on the device), up to the GEMM switch.  Up to kDotMaxRows rows
   // the dot-product kernels stream an expert's weights once at full rate; above that the
   // MFMA kernels take the expert (their cost per row is far lower).  At most
   // A / (kDotMaxRows + 1) experts have more rows, which bounds the second grid.  The first
