@@ -193,7 +193,7 @@ def _random_shapes(n, seed):
 
 
 @pytest.mark.parametrize("dtype", [gen.BF16, gen.MXFP4])
-@pytest.mark.parametrize("T,E,k,d,f,alpha", _random_shapes(10, 1))
+@pytest.mark.parametrize("T,E,k,d,f,alpha", _random_shapes(10, 1) + _random_shapes(10, 2))
 def test_layer_random_shapes(T, E, k, d, f, alpha, dtype):
     """Whole layer (routing and grouping, expert FFN on the path the host picks, combine)
     on seeded random shapes, bf16 and MXFP4 experts, against the oracle."""
