@@ -90,20 +90,33 @@ __global__ __launch_bounds__(1024) void permute_scan(int nchunk, int E, int32_t*
                                                      int32_t* __restrict__ offsets) {
   __shared__ int s_wave[16];
   __shared__ int s_total;
+  constexpr int kU = 8;  // chunk counts in flight per thread (independent loads)
   const int e = threadIdx.x;
   int run = 0;
   if (e < E) {
-    for (int b = 0; b < nchunk; ++b) {
-      const int c = ws[(size_t)b * E + e];
-      ws[(size_t)b * E + e] = run;
-      run += c;
+    for (int b0 = 0; b0 < nchunk; b0 += kU) {
+      int c[kU];
+#pragma unroll
+      for (int q = 0; q < kU; ++q) c[q] = b0 + q < nchunk ? ws[(size_t)(b0 + q) * E + e] : 0;
+#pragma unroll
+      for (int q = 0; q < kU; ++q) {
+        if (b0 + q < nchunk) ws[(size_t)(b0 + q) * E + e] = run;
+        run += c[q];
+      }
     }
   }
   const int off = block_exclusive_scan<1024>(e < E ? run : 0, s_wave, &s_total);
   if (e < E) {
     counts[e] = run;
     offsets[e] = off;
-    for (int b = 0; b < nchunk; ++b) ws[(size_t)b * E + e] += off;
+    for (int b0 = 0; b0 < nchunk; b0 += kU) {
+      int c[kU];
+#pragma unroll
+      for (int q = 0; q < kU; ++q) c[q] = b0 + q < nchunk ? ws[(size_t)(b0 + q) * E + e] : 0;
+#pragma unroll
+      for (int q = 0; q < kU; ++q)
+        if (b0 + q < nchunk) ws[(size_t)(b0 + q) * E + e] = c[q] + off;
+    }
   }
   if (e == 0) offsets[E] = s_total;
 }
