@@ -140,7 +140,8 @@ def test_route_permute_equals_route_then_permute(T, E, k, kind):
 
 # ---------------------------------------------------------------- combine
 @pytest.mark.parametrize("ydt", [moe.MOE_F32, moe.MOE_BF16])
-@pytest.mark.parametrize("T,k,d", [(16, 2, 256), (8, 6, 4096), (777, 8, 2048), (1, 1, 64)])
+@pytest.mark.parametrize("T,k,d", [(16, 2, 256), (8, 6, 4096), (777, 8, 2048), (1, 1, 64),
+                                   (5, 16, 192), (33, 9, 2112)])
 def test_combine_parity(T, k, d, ydt):
     r = np.random.default_rng(T + k + d)
     y32 = gen.normal(11, gen.TAG_MISC, 0, (T * k, d))
