@@ -158,7 +158,9 @@ extern "C" int moe_expert_ffn(const void* x, int act_dtype, const int32_t* perm,
   if (path == MOE_PATH_GEMM) return launch_ffn_gemm(p, y_dtype, stream);
   const int A = T * k, experts = std::min(E, A);
   if (!ffn_dot_supported(d, f)) return launch_ffn_gemv(p, T, y_dtype, stream, experts, 3);
-  if (T <= kDotMaxT) return launch_ffn_dot(p, y_dtype, stream, experts, 3);
+  // One token: k experts give only ~2 rounds of workgroups; one persistent round of looping
+  // workgroups trims the second round's tail (about 1.5% of the layer).
+  if (T <= kDotMaxT) return launch_ffn_dot(p, y_dtype, stream, experts, 3, T == 1 ? 1 : 0);
   // More tokens: split the experts by rows (counted on the device), up to the GEMM switch.  Up to kDotMaxRows rows
   // the dot-product kernels stream an expert's weights once at full rate; above that the
   // MFMA kernels take the expert (their cost per row is far lower).  At most
