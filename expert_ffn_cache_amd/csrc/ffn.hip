@@ -161,9 +161,9 @@ extern "C" int moe_expert_ffn(const void* x, int act_dtype, const int32_t* perm,
   // One token: k experts give only ~2 rounds of workgroups; one persistent round of looping
   // workgroups trims the second round's tail (about 1.5% of the layer).
   if (T <= kDotMaxT) return launch_ffn_dot(p, y_dtype, stream, experts, 3, T == 1 ? 1 : 0);
-  // More tokens: split the experts by rows (counted on the device), up to the GEMM switch.  Up to kDotMaxRows rows
-  // the dot-product kernels stream an expert's weights once at full rate; above that the
-  // MFMA kernels take the expert (their cost per row is far lower).  At most
+  // More tokens: split the experts by rows (counted on the device), up to the GEMM switch.
+  // Up to kDotMaxRows rows the dot-product kernels stream an expert's weights once at full
+  // rate; above that the MFMA kernels take the expert (their cost per row is far lower).  At most
   // A / (kDotMaxRows + 1) experts have more rows, which bounds the second grid.  The first
   // class has no host-side bound below min(E, A) experts, most of them absent when routing
   // is skewed, so its launches are capped grids of looping workgroups: an absent item costs
