@@ -6,7 +6,7 @@ route -> permute -> expert FFN (weight-streaming path) -> combine, replayed
 from captured HIP graphs over 16 pre-drawn routing sets.  value = tokens/s.
 
 Extra measurements in the same JSON line ("extra"): the decode layer at
-T = 1 and 64 and at Zipf alpha 1, the T=8192 prefill layer (grouped-GEMM path), the 16-layer decode loop through the bounded LRU
+T = 1, 64 and 128 and at Zipf alpha 1, the T=8192 prefill layer (grouped-GEMM path), the 16-layer decode loop through the bounded LRU
 expert cache with PCIe miss fills, and the 8-layer prefill with full-layer
 double-buffered streaming.  All inputs are seeded synthetic tensors shaped
 like the FreeToken pages' models; weights are random.
@@ -664,7 +664,7 @@ def main():
                 f"{dec['ms_per_layer_in_16_layer_graph'] * 1e3:.1f} us/layer")
         if not args.no_sweep and wfmt is None:
             sweep = {}
-            for T, alpha in ((1, 0.2), (64, 0.2), (8, 1.0), (64, 1.0)):
+            for T, alpha in ((1, 0.2), (64, 0.2), (8, 1.0), (64, 1.0), (128, 0.2), (128, 1.0)):
                 r = bench_decode(args, torch, moe, T, alpha, arena)
                 sweep[f"T{T}_alpha{alpha}"] = dict(
                     tok_s=r["tok_s"], us_per_layer=r["ms_per_step"] * 1e3, ffn_us=r["ffn_ms"] * 1e3,
@@ -678,7 +678,7 @@ def main():
             # MXFP4 routed experts (the pages' DeepSeek-V4-Flash deployment format)
             arena = decode_arena(torch, gen.MXFP4)
             mx = {}
-            for T, alpha in ((8, 0.2), (1, 0.2), (64, 0.2), (8, 1.0)):
+            for T, alpha in ((8, 0.2), (1, 0.2), (64, 0.2), (8, 1.0), (64, 1.0)):
                 r = bench_decode(args, torch, moe, T, alpha, arena, gen.MXFP4)
                 mx[f"T{T}_alpha{alpha}"] = dict(
                     tok_s=r["tok_s"], us_per_layer=r["ms_per_step"] * 1e3, ffn_us=r["ffn_ms"] * 1e3,
