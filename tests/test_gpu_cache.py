@@ -498,3 +498,46 @@ def test_resize_edge_cases_match_oracle(sizes):
         _compare_tables(dc, sim)
         _arena_holds_pool(dc, arena, pool, w)
     assert int(dc.status.item()) == 0
+
+
+def test_lru_split_and_resize_at_maximum_sizes():
+    """The library's limits: E = 1024 experts (one lookup thread each), S = 4096 slots (every
+    slot's key sorted in LDS, 4 slots per thread in the resize scan) and k = 16.  A trace with
+    evictions from the second step, a resize below residency (4096 -> 1500 slots) and back to
+    4096, then split lookups: every call's expert_slot and fill records, and all tables after
+    every step and resize, equal the simulator's."""
+    L, E, S, T, k, steps = 8, 1024, 4096, 64, 16, 8
+    ids, _ = gen.markov_routing(97, steps, L, T, E, k, 0.5, 1.05)
+    ids_dev = dev(ids)
+    eb = 16  # tables only: a 16-byte arena entry per slot for the resize copy
+    dc = DevCache(L, E, S, eb, torch.zeros(S * eb, dtype=torch.uint8, device="cuda"))
+    sim = LruSim(L, E, S)
+    host_mask = torch.empty(E, dtype=torch.uint8, device="cuda")
+    sizes = {3: 1500, 5: 4096}
+    evicted = 0
+    for s in range(steps):
+        if s in sizes:
+            S2 = sizes[s]
+            dc2 = DevCache(L, E, S2, eb, torch.zeros(S2 * eb, dtype=torch.uint8, device="cuda"))
+            moe.cache_resize(dc.desc, dc2.desc)
+            torch.cuda.synchronize()
+            sim, dc = sim.resized(S2), dc2
+            _compare_tables(dc, sim)
+        for layer in range(L):
+            if s < 6:
+                dc.lookup(layer, ids_dev[s, layer], T, k)
+                slot_ref, fills = sim.step(layer, ids[s, layer])
+            else:
+                moe.cache_lookup_update_split(dc.desc, layer, ids_dev[s, layer], T, k, 57000,
+                                              30000, dc.expert_slot, dc.fills, dc.n_fills,
+                                              host_mask)
+                slot_ref, fills, to_host = sim.step_split(layer, ids[s, layer], 57000, 30000)
+                want = np.zeros(E, dtype=np.uint8)
+                want[to_host] = 1
+                np.testing.assert_array_equal(host_mask.cpu().numpy(), want)
+            assert dc.fills_host() == [tuple(f) for f in fills], (s, layer)
+            np.testing.assert_array_equal(dc.expert_slot.cpu().numpy(), slot_ref)
+            evicted += sum(1 for f in fills if f[3] >= 0)
+        _compare_tables(dc, sim)
+    assert evicted > 0
+    assert int(dc.status.item()) == 0
