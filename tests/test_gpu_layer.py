@@ -197,6 +197,19 @@ def _random_shapes(n, seed):
 def test_layer_random_shapes(T, E, k, d, f, alpha, dtype):
     """Whole layer (routing and grouping, expert FFN on the path the host picks, combine)
     on seeded random shapes, bf16 and MXFP4 experts, against the oracle."""
+    _check_layer(T, E, k, d, f, alpha, dtype)
+
+
+@pytest.mark.parametrize("dtype", [gen.BF16, gen.MXFP4])
+@pytest.mark.parametrize("T", [1, 8, 16, 100, 200, 600])
+def test_layer_at_maximum_experts_and_k(T, dtype):
+    """The library's limits, E = 1024 experts and k = 16, through every path: one-launch
+    routing (T <= 16), weight streaming, the row split, and the grouped GEMMs (bf16 above
+    2048 assignments, MXFP4 above 8192), against the oracle."""
+    _check_layer(T, 1024, 16, 128, 64, 0.5, dtype)
+
+
+def _check_layer(T, E, k, d, f, alpha, dtype):
     w = configs.Workload("rand", seed=T * 7 + E + d, T=T, d=d, E=E, k=k, f=f, dtype=dtype,
                          alpha=alpha)
     x, lg, L, arena = _run_layer(w)
