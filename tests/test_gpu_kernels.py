@@ -50,6 +50,25 @@ def test_route_parity(T, E, k, kind):
     assert_close(w.cpu().numpy(), ref_w, 1e-5 * float(np.abs(ref_w).max()), "topk_w")
 
 
+@pytest.mark.parametrize("T,d,E", [(1, 1, 1), (3, 7, 65), (300, 256, 8), (17, 512, 1024)])
+def test_router_logits_parity(T, d, E):
+    """Router logits (fp32) against the oracle's double-precision product, element by element,
+    on ragged shapes (one element, d not a multiple of anything, the largest E)."""
+    r = np.random.default_rng(T * 31 + d + E)
+    x = r.standard_normal((T, d)).astype(np.float32)
+    wr = (r.standard_normal((E, d)) / np.sqrt(d)).astype(np.float32)
+    out = torch.full((T + 1, E), 7.0, dtype=torch.float32, device="cuda")
+    moe.moe_router_logits(dev(x), dev(wr), moe.MOE_F32, T, d, E, out)
+    torch.cuda.synchronize()
+    ref = oracle.router_logits(x, wr)
+    got = out.cpu().numpy()
+    assert_close(got[:T], ref, 1e-5 * float(np.abs(ref).max()) + 1e-6, "router logits")
+    assert (got[T:] == 7.0).all()
+    moe.moe_router_logits(dev(x), dev(wr), moe.MOE_F32, 0, d, E, out)  # T = 0: no work
+    torch.cuda.synchronize()
+    assert (out.cpu().numpy()[T:] == 7.0).all()
+
+
 def test_route_empty_and_invalid_args():
     moe.moe_route(None, 0, 8, 2, None, None)  # T = 0 is a no-op
     with pytest.raises(moe.MoeError):
