@@ -414,3 +414,24 @@ def test_ffn_expert_mask_selects_experts(T, path, dtype):
     assert on.any() and (~on).any()
     assert np.isnan(y[~on]).all()
     assert_close(y[on], ref[on], bf16_tol(ref), f"masked rows T={T} path={path}")
+
+
+# ---------------------------------------------------------------- measurement probes
+@pytest.mark.parametrize("nbytes", [16, 2048 * 16 + 16, 3 * (1 << 20) + 48, (200 << 20) + 16])
+def test_probes_read_and_copy_every_byte_once(nbytes):
+    """The read probe's per-workgroup words XOR to the XOR of every 32-bit word of the source
+    (a word read twice or skipped would change it), and the copy probe's destination equals
+    the source with nothing past it written; sizes leave partial chunks, and the largest takes
+    the read probe's grid-stride loop twice."""
+    r = np.random.default_rng(nbytes)
+    src_np = r.integers(0, 1 << 32, size=nbytes // 4, dtype=np.uint32)
+    src = dev(src_np.view(np.int32))
+    sink = torch.zeros(4096, dtype=torch.int32, device="cuda")
+    moe.moe_hbm_read_probe(src, nbytes, sink)
+    dst = torch.full((nbytes // 4 + 16,), -1, dtype=torch.int32, device="cuda")
+    moe.moe_copy_probe(src, dst, nbytes)
+    torch.cuda.synchronize()
+    assert np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32)) == np.bitwise_xor.reduce(src_np)
+    got = dst.cpu().numpy()
+    np.testing.assert_array_equal(got[:nbytes // 4].view(np.uint32), src_np)
+    assert (got[nbytes // 4:] == -1).all()
