@@ -315,7 +315,7 @@ def bench_lru(args, torch, moe, dtype=None, with_resize=True):
     slot_of, key_of = torch.empty(w.L * w.E, **i32), torch.empty(w.S, **i32)
     stamp, clock, stats = torch.empty(w.S, **i64), torch.empty(1, **i64), torch.empty(4, **i64)
     status = torch.zeros(1, **i32)
-    desc = moe.moe_cache_t(w.L, w.E, w.S, 0, w.entry_bytes, slot_of.data_ptr(), key_of.data_ptr(),
+    desc = moe.moe_cache_t(w.L, w.E, w.S, w.L * w.E, w.entry_bytes, slot_of.data_ptr(), key_of.data_ptr(),
                            stamp.data_ptr(), clock.data_ptr(), stats.data_ptr(), status.data_ptr(),
                            arena.data_ptr(), pool.data_ptr())
     expert_slot = torch.empty(w.E, **i32)
@@ -437,7 +437,7 @@ def bench_lru(args, torch, moe, dtype=None, with_resize=True):
                  stamp=torch.empty(S2, **i64), clock=torch.empty(1, **i64),
                  stats=torch.empty(4, **i64), status=torch.zeros(1, **i32),
                  arena=torch.empty((S2, w.entry_elems), dtype=torch_dtype(w), device="cuda"))
-        d = moe.moe_cache_t(w.L, w.E, S2, 0, w.entry_bytes, *(t[n].data_ptr() for n in (
+        d = moe.moe_cache_t(w.L, w.E, S2, w.L * w.E, w.entry_bytes, *(t[n].data_ptr() for n in (
             "slot_of", "key_of", "stamp", "clock", "stats", "status", "arena")), pool.data_ptr())
         return d, t
     resize = {}

@@ -49,7 +49,7 @@ class MoeError(RuntimeError):
 class moe_cache_t(ctypes.Structure):
     _fields_ = [
         ("L", ctypes.c_int32), ("E", ctypes.c_int32), ("S", ctypes.c_int32),
-        ("reserved", ctypes.c_int32), ("entry_bytes", ctypes.c_size_t),
+        ("pool_entries", ctypes.c_int32), ("entry_bytes", ctypes.c_size_t),
         ("slot_of", ctypes.c_void_p), ("key_of", ctypes.c_void_p), ("stamp", ctypes.c_void_p),
         ("clock", ctypes.c_void_p), ("stats", ctypes.c_void_p), ("status", ctypes.c_void_p),
         ("arena", ctypes.c_void_p), ("host_pool", ctypes.c_void_p),

@@ -211,7 +211,7 @@ __global__ __launch_bounds__(kFillThreads) void fill_from_pool(moe_cache_t c,
     const size_t it = w - (size_t)i * iters;
     const moe_fill_t f = fills[i];
     if (f.slot < 0 || f.slot >= c.S || f.layer < 0 || f.layer >= c.L || f.expert < 0 ||
-        f.expert >= c.E) {
+        f.expert >= c.E || (long long)f.layer * c.E + f.expert >= c.pool_entries) {
       if (it == 0 && threadIdx.x == 0) set_status(c.status, MOE_ERANGE);
       continue;
     }
@@ -417,7 +417,7 @@ extern "C" int cache_fill(const moe_cache_t* cache, const moe_fill_t* fills_host
   for (int i = 0; i < n_fills; ++i) {
     const moe_fill_t& f = fills_host[i];
     if (f.slot < 0 || f.slot >= cache->S || f.layer < 0 || f.layer >= cache->L || f.expert < 0 ||
-        f.expert >= cache->E)
+        f.expert >= cache->E || (long long)f.layer * cache->E + f.expert >= cache->pool_entries)
       return MOE_ERANGE;
   }
   const size_t eb = cache->entry_bytes;

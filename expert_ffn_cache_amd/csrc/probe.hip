@@ -82,4 +82,4 @@ extern "C" const char* moe_strerror(int status) {
   }
 }
 
-extern "C" int moe_abi_version(void) { return 1; }
+extern "C" int moe_abi_version(void) { return 2; }

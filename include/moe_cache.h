@@ -185,7 +185,12 @@ int moe_expert_ffn(const void* x, int act_dtype, const int32_t* perm, const int3
 
 /* Weighted combine: out[t][:] = sum_{j=0..k-1} topk_w[t][j] * y_perm[inv[t*k+j]][:],
  * j ascending, fp32, a gather (no atomics, deterministic).  y_perm [T*k][d]
- * in y_dtype (MOE_F32 or MOE_BF16), out [T][d] fp32. */
+ * in y_dtype (MOE_F32 or MOE_BF16), out [T][d] fp32.
+ * The pages name no combine rule; this is a reading: each token's output is
+ * the gate-weighted sum of the outputs of the experts it selected (the step
+ * that completes a token once its chosen experts have run, RTX-4090 page,
+ * "How the MoE memory hierarchy works": a token activates only its selected
+ * experts), with the gate weights of moe_route. */
 int moe_combine(const void* y_perm, int y_dtype, const int32_t* inv, const float* topk_w, int T,
                 int k, int d, float* out, hipStream_t stream);
 
@@ -200,11 +205,15 @@ int moe_combine(const void* y_perm, int y_dtype, const int32_t* inv, const float
  *   stats   [4]   int64: accesses, hits, misses, fill bytes (accumulated)
  *   status  [1]   int32: sticky device error word
  *   arena: S entries of entry_bytes each (device)
- *   host_pool: L*E entries, layer-major, pinned host memory (the ground-truth
- *   copy of every routed expert: vram page, opening section) */
+ *   host_pool: pinned host memory holding pool_entries whole entries,
+ *   layer-major (entry (layer, e) at byte (layer*E + e) * entry_bytes): the
+ *   ground-truth copy of every routed expert (vram page, opening section).
+ *   pool_entries: entries host_pool holds (normally L*E).  A fill of
+ *   (layer, e) with layer*E + e >= pool_entries is out of range, so a record
+ *   can never read past a short pool; 0 when the cache has no pool. */
 typedef struct {
   int32_t L, E, S;
-  int32_t reserved;
+  int32_t pool_entries;
   size_t entry_bytes;
   int32_t* slot_of;
   int32_t* key_of;
@@ -223,6 +232,10 @@ typedef struct {
 } moe_fill_t;
 
 /* Empty cache: slot_of = key_of = -1, stamp = clock = stats = 0, status = 0.
+ * The pages describe the GPU cache as filled by recent routing rather than fixed
+ * at start-up (RTX-4090 page, "How the MoE memory hierarchy works"; llama page,
+ * "Official project overview"); the reading taken here is that it starts empty
+ * (cold) and every entry arrives through a miss fill.
  * Runs a fill kernel (no memset nodes), so it may be captured.  1 <= S <= 4096
  * (the lookup sorts one key per slot in LDS). */
 int cache_init(const moe_cache_t* cache, hipStream_t stream);
@@ -273,7 +286,8 @@ int cache_lookup_update_split(const moe_cache_t* cache, int layer, const int32_t
  * by cache_lookup_update.  Issues hipMemcpyAsync host-to-device on
  * copy_stream, merging records whose slots and pool entries are both
  * consecutive.  Returns MOE_ERANGE (nothing enqueued) for a record outside
- * [0, S) x [0, L) x [0, E).  Not capture-safe (the count is host data). */
+ * [0, S) x [0, L) x [0, E) or past the pool (layer*E + expert >= pool_entries).
+ * Not capture-safe (the count is host data). */
 int cache_fill(const moe_cache_t* cache, const moe_fill_t* fills_host, int n_fills,
                hipStream_t copy_stream);
 
@@ -292,8 +306,9 @@ int cache_fill(const moe_cache_t* cache, const moe_fill_t* fills_host, int n_fil
  *   fills, n_fills: device memory; max_fills: capacity of fills (host int).
  * Device errors (sticky, in cache->status): *n_fills outside [0, max_fills]
  * sets MOE_ERANGE and copies nothing; a record outside [0, S) x [0, L) x [0, E)
- * sets MOE_ERANGE and is skipped (the others are copied).  max_fills = 0 is a
- * no-op.  Enqueued on `stream`; capture-safe. */
+ * or past the pool (layer*E + expert >= pool_entries) sets MOE_ERANGE and is
+ * skipped (the others are copied), so no read leaves the pool.  max_fills = 0
+ * is a no-op.  Enqueued on `stream`; capture-safe. */
 int cache_fill_device(const moe_cache_t* cache, const moe_fill_t* fills, const int32_t* n_fills,
                       int max_fills, hipStream_t stream);
 

@@ -32,7 +32,7 @@ def test_strerror_and_version():
     for code in (moe.MOE_EINVAL, moe.MOE_EUNSUPPORTED, moe.MOE_EHIP, moe.MOE_ECAPACITY,
                  moe.MOE_ERANGE):
         assert moe.strerror(code) not in ("ok", "unknown status")
-    assert moe.abi_version() == 1
+    assert moe.abi_version() == 2
 
 
 def test_entry_bytes():
@@ -110,6 +110,14 @@ def test_cache_host_validation():
     assert moe.lib().cache_fill(ctypes.byref(c), ctypes.addressof(bad), 2, None) == moe.MOE_ERANGE
     bad[1] = moe.moe_fill_t(1, 2, 1, -1)
     assert moe.lib().cache_fill(ctypes.byref(c), ctypes.addressof(bad), 2, None) == moe.MOE_ERANGE
+    # a record valid for (L, E) but past a short pool is rejected before anything is enqueued
+    # (the descriptor's addresses are dummies: an accepted call would have to copy from them)
+    short = moe.moe_cache_t(2, 4, 8, 5, 64, 1, 1, 1, 1, 1, 1, 1, 1)  # pool holds entries 0..4
+    past = (moe.moe_fill_t * 2)(moe.moe_fill_t(0, 0, 1, -1), moe.moe_fill_t(1, 1, 1, -1))
+    assert moe.lib().cache_fill(ctypes.byref(short), ctypes.addressof(past), 2, None) == moe.MOE_ERANGE
+    nopool = moe.moe_cache_t(2, 4, 8, 0, 64, 1, 1, 1, 1, 1, 1, 1, 1)  # pool_entries = 0
+    one = (moe.moe_fill_t * 1)(moe.moe_fill_t(0, 0, 0, -1))
+    assert moe.lib().cache_fill(ctypes.byref(nopool), ctypes.addressof(one), 1, None) == moe.MOE_ERANGE
     assert moe.lib().layer_stream_prefetch(None, None, 16, 1, None, None, None) == moe.MOE_EINVAL
     # device-driven fills: aligned dummy addresses; max_fills = 0 returns before any launch
     ok = moe.moe_cache_t(2, 4, 8, 0, 64, 4096, 4096, 4096, 4096, 4096, 4096, 4096, 4096)

@@ -21,7 +21,7 @@ pytestmark = pytest.mark.gpu
 class DevCache:
     """Device tables + descriptor for a cache of S slots over L x E entries."""
 
-    def __init__(self, L, E, S, entry_bytes, arena=None, pool=None):
+    def __init__(self, L, E, S, entry_bytes, arena=None, pool=None, pool_entries=None):
         i32 = dict(dtype=torch.int32, device="cuda")
         i64 = dict(dtype=torch.int64, device="cuda")
         self.slot_of = torch.empty(L * E, **i32)
@@ -34,8 +34,10 @@ class DevCache:
         self.fills = torch.empty((max(E, 1), 4), **i32)
         self.n_fills = torch.empty(1, **i32)
         self.arena, self.pool = arena, pool
+        if pool_entries is None:
+            pool_entries = 0 if pool is None else L * E
         self.desc = moe.moe_cache_t(
-            L, E, S, 0, entry_bytes, self.slot_of.data_ptr(), self.key_of.data_ptr(),
+            L, E, S, pool_entries, entry_bytes, self.slot_of.data_ptr(), self.key_of.data_ptr(),
             self.stamp.data_ptr(), self.clock.data_ptr(), self.stats.data_ptr(),
             self.status.data_ptr(), 0 if arena is None else arena.data_ptr(),
             0 if pool is None else pool.data_ptr())
@@ -305,6 +307,33 @@ def test_device_fill_error_records():
     torch.cuda.synchronize()
     assert int(dc2.status.item()) == moe.MOE_ERANGE
     assert int(dc2.arena.view(torch.int16).abs().sum().item()) == 0
+
+
+def test_fills_past_a_short_pool_are_rejected():
+    """The pool holds every (layer, expert) entry but declares only the first L*E - 1: a record
+    for the last entry is out of range on both fill paths.  The host path returns MOE_ERANGE
+    before enqueueing anything; the device path sets MOE_ERANGE, skips that record and copies
+    the others.  (The undeclared entry is still inside the allocation, so a wrong read could
+    not leave it.)"""
+    w = configs.Workload("fill_short", seed=38, T=1, d=64, E=2, k=1, f=64, dtype=gen.BF16, L=2, S=2)
+    pool = host_pool(w)
+    arena = torch.zeros((w.S, w.entry_elems), dtype=torch.bfloat16, device="cuda")
+    dc = DevCache(w.L, w.E, w.S, w.entry_bytes, arena, pool, pool_entries=w.L * w.E - 1)
+    last = (moe.moe_fill_t * 2)(moe.moe_fill_t(0, 0, 1, -1), moe.moe_fill_t(1, 1, 1, -1))
+    with pytest.raises(moe.MoeError) as ei:
+        moe.cache_fill(dc.desc, ctypes.addressof(last), 2)
+    assert ei.value.status == moe.MOE_ERANGE
+    torch.cuda.synchronize()
+    assert int(arena.view(torch.int16).abs().sum().item()) == 0  # nothing was enqueued
+    dc.fills[0] = torch.tensor([0, 0, 1, -1], dtype=torch.int32)  # entry 1: declared
+    dc.fills[1] = torch.tensor([1, 1, 1, -1], dtype=torch.int32)  # entry 3: past the count
+    dc.n_fills.fill_(2)
+    moe.cache_fill_device(dc.desc, dc.fills, dc.n_fills, 2)
+    torch.cuda.synchronize()
+    assert int(dc.status.item()) == moe.MOE_ERANGE
+    got = arena[0].view(torch.int16).cpu().numpy().view(np.uint16)
+    np.testing.assert_array_equal(got, _pool_entry(pool, w, 0, 1))
+    assert int(arena[1].view(torch.int16).abs().sum().item()) == 0
 
 
 def test_fill_masks_split_requested_experts():
