@@ -21,6 +21,7 @@ MOE_EUNSUPPORTED = -2
 MOE_EHIP = -3
 MOE_ECAPACITY = -4
 MOE_ERANGE = -5
+MOE_ETOOBIG = -6
 
 MOE_F32 = 0
 MOE_BF16 = 1
@@ -34,7 +35,8 @@ EXPORTS = [
     "moe_strerror", "moe_abi_version", "moe_router_logits", "moe_route",
     "moe_permute_workspace_bytes", "moe_permute", "moe_route_permute", "moe_entry_bytes",
     "moe_expert_ffn_workspace_bytes",
-    "moe_expert_ffn", "moe_combine", "cache_init", "cache_lookup_update",
+    "moe_expert_ffn", "moe_expert_ffn_noalloc", "moe_expert_ffn_noalloc_max_bytes",
+    "moe_combine", "cache_init", "cache_lookup_update",
     "cache_lookup_update_split", "cache_fill",
     "cache_fill_device", "cache_fill_masks", "cache_resize", "layer_stream_prefetch", "moe_hbm_read_probe", "moe_copy_probe",
 ]
@@ -85,6 +87,9 @@ def lib():
             "moe_expert_ffn_workspace_bytes": ([i32, i32, i32, i32], sz),
             "moe_expert_ffn": ([vp, i32, vp, vp, i32, i32, i32, i32, i32, vp, vp, sz, i32, vp, vp,
                                 i32, vp, sz, vp, i32, i32, vp, vp], i32),
+            "moe_expert_ffn_noalloc": ([vp, i32, vp, vp, i32, i32, i32, i32, i32, vp, vp, sz, i32,
+                                        vp, vp, i32, vp, i32, i32, vp, vp], i32),
+            "moe_expert_ffn_noalloc_max_bytes": ([], sz),
             "moe_combine": ([vp, i32, vp, vp, i32, i32, i32, vp, vp], i32),
             "cache_init": ([ctypes.POINTER(moe_cache_t), vp], i32),
             "cache_lookup_update": ([ctypes.POINTER(moe_cache_t), i32, vp, i32, i32, vp, vp, vp,
@@ -187,6 +192,19 @@ def moe_expert_ffn(x, act_dtype, perm, offsets, T, k, E, d, f, expert_slot, aren
         _p(x), act_dtype, _p(perm), _p(offsets), T, k, E, d, f, _p(expert_slot), _p(arena),
         entry_stride, w_dtype, _p(expert_mask), _p(slot_key), key_base, _p(ws), ws_bytes,
         _p(y_perm), y_dtype, path, _p(status), _s(stream)))
+
+
+def moe_expert_ffn_noalloc(x, act_dtype, perm, offsets, T, k, E, d, f, expert_slot, arena,
+                           entry_stride, w_dtype, expert_mask, slot_key, key_base, y_perm, y_dtype,
+                           path=MOE_PATH_AUTO, status=None, stream=None):
+    _check("moe_expert_ffn_noalloc", lib().moe_expert_ffn_noalloc(
+        _p(x), act_dtype, _p(perm), _p(offsets), T, k, E, d, f, _p(expert_slot), _p(arena),
+        entry_stride, w_dtype, _p(expert_mask), _p(slot_key), key_base, _p(y_perm), y_dtype, path,
+        _p(status), _s(stream)))
+
+
+def moe_expert_ffn_noalloc_max_bytes():
+    return lib().moe_expert_ffn_noalloc_max_bytes()
 
 
 def moe_combine(y_perm, y_dtype, inv, topk_w, T, k, d, out, stream=None):

@@ -18,6 +18,7 @@
 //    counts (ffn_mx.hip), a grouped GEMM for prefill-shaped ones (ffn_mx_gemm.hip).
 // Both bf16 paths fuse SiLU(g)*u into the gate/up epilogue and write h once as bf16.
 #include <algorithm>
+#include <mutex>
 
 #include "ffn_args.h"
 
@@ -177,4 +178,50 @@ extern "C" int moe_expert_ffn(const void* x, int act_dtype, const int32_t* perm,
   if (rc == MOE_OK) rc = launch_ffn_dot(few, y_dtype, stream, experts, 2, kDotSplitRounds);
   if (rc == MOE_OK) rc = launch_ffn_gemv(many, T, y_dtype, stream, many_max, 2);
   return rc;
+}
+
+// ---------------------------------------------------------------- no-allocation variant
+// The SwiGLU intermediate of moe_expert_ffn_noalloc lives in this file-scope device array:
+// every GPU the library runs on holds its own copy from module load to process end.  In host
+// code the name `scratch` is only a host-side stand-in, so its device address is looked up
+// once per device (with that device current) and only that address is ever passed on.
+namespace {
+
+constexpr size_t kScratchBytes = size_t(8) << 20;
+constexpr int kMaxDevices = 64;
+__device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device, once looked up
+
+// Device address of this device's scratch array, or nullptr if it cannot be obtained.
+void* scratch_ptr() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" size_t moe_expert_ffn_noalloc_max_bytes(void) { return kScratchBytes; }
+
+extern "C" int moe_expert_ffn_noalloc(const void* x, int act_dtype, const int32_t* perm,
+                                      const int32_t* offsets, int T, int k, int E, int d, int f,
+                                      const int32_t* expert_slot, const void* arena,
+                                      size_t entry_stride, int w_dtype, const uint8_t* expert_mask,
+                                      const int32_t* slot_key, int key_base, void* y_perm,
+                                      int y_dtype, int path, int32_t* status, hipStream_t stream) {
+  if (T < 0 || k <= 0 || f <= 0) return MOE_EINVAL;
+  if (moe_expert_ffn_workspace_bytes(T, k, f, act_dtype) > kScratchBytes) return MOE_ETOOBIG;
+  void* ws = scratch_ptr();
+  if (!ws) return MOE_EHIP;
+  return moe_expert_ffn(x, act_dtype, perm, offsets, T, k, E, d, f, expert_slot, arena,
+                        entry_stride, w_dtype, expert_mask, slot_key, key_base, ws, kScratchBytes,
+                        y_perm, y_dtype, path, status, stream);
 }

@@ -78,6 +78,7 @@ extern "C" const char* moe_strerror(int status) {
     case MOE_EHIP: return "HIP launch or copy failed";
     case MOE_ECAPACITY: return "more unique experts requested than cache slots";
     case MOE_ERANGE: return "id, layer or slot out of range, or stale cache slot";
+    case MOE_ETOOBIG: return "request larger than a fixed library limit (no-allocation scratch)";
     default: return "unknown status";
   }
 }

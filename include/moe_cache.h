@@ -27,7 +27,9 @@
  *  - Returns an int status: MOE_OK or a negative MOE_E* code.  Nothing throws.
  *  - Host-detected errors return before anything is enqueued.
  *  - All work is asynchronous on the caller's stream; the library allocates
- *    nothing and keeps no global mutable state.  The caller owns all memory.
+ *    nothing and the caller owns all memory.  The only global state is the
+ *    fixed scratch array of moe_expert_ffn_noalloc (one per GPU, part of the
+ *    loaded code object) and the cached device address of each GPU's copy.
  *  - Device pointers must be 16-byte aligned.  Errors found on the device are
  *    written to a caller-provided int32 device status word, sticky: the first
  *    error code is kept (compare-and-swap from 0); the caller reads it after a
@@ -59,6 +61,7 @@ extern "C" {
 #define MOE_EHIP (-3)         /* a HIP launch or copy failed */
 #define MOE_ECAPACITY (-4)    /* more unique experts requested than cache slots */
 #define MOE_ERANGE (-5)       /* id, layer or slot out of range; stale cache slot */
+#define MOE_ETOOBIG (-6)      /* larger than a fixed library limit (no-allocation scratch) */
 
 #define MOE_F32 0   /* IEEE binary32 */
 #define MOE_BF16 1  /* bfloat16 (upper half of binary32) */
@@ -182,6 +185,27 @@ int moe_expert_ffn(const void* x, int act_dtype, const int32_t* perm, const int3
                    const uint8_t* expert_mask, const int32_t* slot_key, int key_base, void* ws,
                    size_t ws_bytes, void* y_perm, int y_dtype, int path, int32_t* status,
                    hipStream_t stream);
+
+/* moe_expert_ffn without a workspace argument, for callers that cannot allocate device
+ * memory (code under graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * The SwiGLU intermediate lives in a fixed library-owned device array of
+ * moe_expert_ffn_noalloc_max_bytes() bytes (8 MiB) on each GPU, held from the library's load
+ * until the process ends; nothing is allocated by the call (its first call on a device looks
+ * up that device's array address once).  Every other argument, result and error is as for
+ * moe_expert_ffn.  A call whose intermediate (moe_expert_ffn_workspace_bytes(T, k, f,
+ * act_dtype)) exceeds the array returns MOE_ETOOBIG before anything is enqueued.  All calls on
+ * one GPU share its array and each overwrites it: calls that may overlap in time on one GPU
+ * (different streams, or different host threads) race and give undefined results; order them
+ * on one stream.  No part of the array needs to start at zero. */
+int moe_expert_ffn_noalloc(const void* x, int act_dtype, const int32_t* perm,
+                           const int32_t* offsets, int T, int k, int E, int d, int f,
+                           const int32_t* expert_slot, const void* arena, size_t entry_stride,
+                           int w_dtype, const uint8_t* expert_mask, const int32_t* slot_key,
+                           int key_base, void* y_perm, int y_dtype, int path, int32_t* status,
+                           hipStream_t stream);
+
+/* Size in bytes of moe_expert_ffn_noalloc's fixed scratch array (its largest intermediate). */
+size_t moe_expert_ffn_noalloc_max_bytes(void);
 
 /* Weighted combine: out[t][:] = sum_{j=0..k-1} topk_w[t][j] * y_perm[inv[t*k+j]][:],
  * j ascending, fp32, a gather (no atomics, deterministic).  y_perm [T*k][d]

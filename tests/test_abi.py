@@ -30,7 +30,7 @@ def test_every_declared_symbol_is_exported():
 def test_strerror_and_version():
     assert moe.strerror(moe.MOE_OK) == "ok"
     for code in (moe.MOE_EINVAL, moe.MOE_EUNSUPPORTED, moe.MOE_EHIP, moe.MOE_ECAPACITY,
-                 moe.MOE_ERANGE):
+                 moe.MOE_ERANGE, moe.MOE_ETOOBIG):
         assert moe.strerror(code) not in ("ok", "unknown status")
     assert moe.abi_version() == 2
 
@@ -164,3 +164,17 @@ def test_python_binding_raises():
     with pytest.raises(moe.MoeError) as ei:
         moe.moe_route(0, 4, 8, 9, 0, 0, stream=0)
     assert ei.value.status == moe.MOE_EINVAL
+
+
+def test_noalloc_ffn_limit_is_checked_on_the_host():
+    """The no-allocation FFN's scratch limit (8 MiB) is checked before any HIP call: a request
+    whose SwiGLU intermediate exceeds it returns MOE_ETOOBIG (no GPU needed)."""
+    L = moe.lib()
+    assert L.moe_expert_ffn_noalloc_max_bytes() == 8 << 20
+    T, k, f = 2048, 4, 1024  # 2048 * 4 * 1024 * 2 bytes = 16 MiB
+    assert moe.moe_expert_ffn_workspace_bytes(T, k, f, moe.MOE_BF16) > 8 << 20
+    args = [None, moe.MOE_BF16, None, None, T, k, 16, 256, f, None, None, 3 * 256 * f * 2,
+            moe.MOE_BF16, None, None, 0, None, moe.MOE_F32, moe.MOE_PATH_AUTO, None, None]
+    assert L.moe_expert_ffn_noalloc(*args) == moe.MOE_ETOOBIG
+    bad = list(args); bad[4] = -1
+    assert L.moe_expert_ffn_noalloc(*bad) == moe.MOE_EINVAL
