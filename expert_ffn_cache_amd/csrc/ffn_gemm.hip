@@ -29,7 +29,7 @@ namespace {
 constexpr int QBM = 256, QBN = 256, QBK = 64;
 constexpr int kGateUp = 0, kDown = 1;
 
-// Element index of 16-byte chunk c (0..3) of row r in a 64-byte-row tile; the XOR spreads
+// Element index of 16-byte chunk c (0..7) of row r in a 128-byte-row tile; the XOR spreads
 // the 16 rows served by one ds_read_b128 cycle over all LDS banks.
 __device__ __forceinline__ int qswz(int r, int c) { return r * QBK + ((c ^ ((r >> 1) & 7)) << 3); }
 
@@ -41,11 +41,16 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // 16 bytes per lane, global -> LDS (lane i lands at lds + 16 i; lds is wave-uniform).  Issued
 // from inline assembly so the compiler does not drain every outstanding load before each
 // LDS read (it cannot tell which stage a direct load writes); stage readiness is tracked
-// with explicit s_waitcnt vmcnt below.  Sets M0 itself (nothing else in these kernels uses
-// M0); has no output registers.
+// with explicit s_waitcnt vmcnt below.  Writes M0, declared clobbered (clang warns that M0
+// is a reserved register; listing it is what tells the compiler that any value it kept there
+// is gone); has no output registers.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void g2lds16(const uint16_t* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" :: "s"(lds), "v"(g) : "memory");
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" :: "s"(lds), "v"(g)
+               : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
