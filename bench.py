@@ -89,7 +89,23 @@ def sources_sha256(paths):
     return h.hexdigest()
 
 
-def _counter_traffic(kernel_srcs, name):
+# sources of the prefill grouped GEMMs (bf16, MXFP4) and the headers they include
+PREFILL_GEMM_SOURCES = [os.path.join(CSRC, n) for n in ("common.h", "ffn_args.h", "ffn_gemm.hip")]
+MXFP4_GEMM_SOURCES = [os.path.join(CSRC, n) for n in ("common.h", "ffn_args.h", "ffn_mx_gemm.hip")]
+PREFILL_TRAFFIC = "gemm_prefill_e256_k6_d4096_f2048_T8192_traffic.txt"
+
+
+def _prefill_traffic(dtype, alpha):
+    """HBM bytes per prefill FFN call at Zipf alpha from the committed counter summary, if it
+    was taken on the current GEMM sources; else None."""
+    import gen
+    mx = dtype == gen.MXFP4
+    key = f"{'mxfp4' if mx else 'bf16'}_alpha_{alpha}_hbm_bytes_per_call"
+    return _counter_traffic(MXFP4_GEMM_SOURCES if mx else PREFILL_GEMM_SOURCES, PREFILL_TRAFFIC,
+                            key=key, sha_key=f"{'mxfp4' if mx else 'bf16'}_kernel_source_sha256")
+
+
+def _counter_traffic(kernel_srcs, name, key="hbm_bytes_per_call", sha_key="kernel_source_sha256"):
     """HBM bytes per FFN call from the committed rocprofv3 counter summary, if it was taken
     on the current kernel sources (sha256 match); else None."""
     path = os.path.join(PROFILES, name)
@@ -101,9 +117,9 @@ def _counter_traffic(kernel_srcs, name):
         if ":" in line and not line.lstrip().startswith("#"):
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
-    if vals.get("kernel_source_sha256") != sha or "hbm_bytes_per_call" not in vals:
+    if vals.get(sha_key) != sha or key not in vals:
         return None
-    return float(vals["hbm_bytes_per_call"])
+    return float(vals[key])
 
 
 # ------------------------------------------------------------------------ decode layer
@@ -202,6 +218,8 @@ def bench_decode(args, torch, moe, T, alpha, arena, dtype=None):
         raise RuntimeError(f"decode: device status {status}")
     ffn_avg_ms = float(np.mean(ffn_ms))
     achieved = float(np.sum(byts) / (np.sum(ffn_ms) * 1e-3) / 1e9)
+    A = w.T * w.k
+    step_bytes = float(np.mean(byts)) + w.T * w.E * 4 + A * w.d * 4 + w.T * w.d * 4
     traffic = None
     if T == 8 and alpha == 0.2:  # what the committed counter summaries cover
         if dtype is None:
@@ -218,7 +236,10 @@ def bench_decode(args, torch, moe, T, alpha, arena, dtype=None):
         roofline=dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
                       frac=achieved / HBM_PEAK_GBS,
                       traffic=None if traffic is None else traffic),
-        algorithmic_bytes_per_call=float(np.mean(byts)))
+        algorithmic_bytes_per_call=float(np.mean(byts)),
+        # the whole step (route + group + FFN + combine) against the same roof: the FFN's
+        # bytes plus the logits read, y read back by the combine and out written
+        step_bytes=step_bytes, step_hbm_frac=step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS)
 
 
 # ------------------------------------------------------------------------ prefill layer
@@ -233,7 +254,8 @@ def bench_prefill(args, torch, moe, dtype=None):
     arena = device_arena_all_experts(base)
     log(f"[prefill] arena generated in {time.time() - t0:.1f}s")
     x = torch.from_numpy(configs.gen_x(base).view(np.int16)).view(torch.bfloat16).cuda()
-    for alpha in (0.2, 1.0):
+    alphas = (0.2, 1.0) if args.prefill_alpha is None else (args.prefill_alpha,)
+    for alpha in alphas:
         w = configs.with_(base, alpha=alpha)
         R = 2
         logits = [torch.from_numpy(configs.gen_logits(w, rotation=r)).cuda() for r in range(R)]
@@ -285,6 +307,10 @@ def bench_prefill(args, torch, moe, dtype=None):
             hbm_frac=byts / (ffn_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             roofline_bound="hbm" if t_hbm >= t_mfma else "mfma",
             roofline_floor_ms=max(t_mfma, t_hbm), roofline_frac=max(t_mfma, t_hbm) / ffn_ms)
+        traffic = _prefill_traffic(dtype, alpha)
+        if traffic is not None:  # HBM bytes of the call from the committed counter summary
+            out[f"alpha_{alpha}"].update(traffic_bytes=traffic, algorithmic_bytes=byts,
+                                         traffic_over_algorithmic=traffic / byts)
         del graphs, layers
     out["workload"] = base.name
     del arena
@@ -592,10 +618,23 @@ def bench_probe(args, torch, moe):
 
 
 # ------------------------------------------------------------------------ CPU baseline
+def _oracle_rate(layer_fn, tokens_per_call, seconds, max_calls=4096):
+    spent, tokens, calls = 0.0, 0, 0
+    while spent < seconds and calls < max_calls:
+        t0 = time.perf_counter()
+        layer_fn(calls)
+        spent += time.perf_counter() - t0
+        tokens += tokens_per_call
+        calls += 1
+    return tokens / spent, calls, spent
+
+
 def cpu_baseline(args):
-    """The oracle (plain double-precision C, OpenMP over tokens) on the decode layer, timed on
-    the host cores for whole T=8 layers, cycling over 16 rotated routing sets until about
-    args.cpu_seconds of CPU time has been spent (weights generated once, untimed)."""
+    """The oracle (plain double-precision C; OpenMP over the (token, expert) FFNs of a layer,
+    the same arithmetic at any thread count) on whole decode layers, timed on the host cores,
+    cycling over 16 rotated routing sets until about args.cpu_seconds of time has been spent
+    (weights generated once, untimed).  Also on one core: the same decode layer and the tiny
+    fp32 layer, a few seconds each."""
     from gen import configs
     import oracle
 
@@ -604,17 +643,28 @@ def cpu_baseline(args):
     lgs = [configs.gen_logits(w, rotation=r) for r in range(16)]
     used = sorted(set(int(e) for lg in lgs for e in oracle.route(lg, w.k)[0].ravel()))
     table = oracle.ExpertTable(w.E, {e: configs.gen_expert(w, 0, e) for e in used})
-    spent, tokens, layers = 0.0, 0, 0
-    while spent < args.cpu_seconds and layers < 4096:
-        t0 = time.perf_counter()
-        oracle.moe_layer(x, lgs[layers % 16], w.k, table)
-        spent += time.perf_counter() - t0
-        tokens += w.T
-        layers += 1
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    return dict(value=tokens / spent, unit="tokens/s", cores=min(w.T, threads), kind="oracle",
+    threads = oracle.max_threads()
+    rate, layers, spent = _oracle_rate(lambda i: oracle.moe_layer(x, lgs[i % 16], w.k, table),
+                                       w.T, args.cpu_seconds)
+    tw = configs.TINY
+    tx, tlg = configs.gen_x(tw), configs.gen_logits(tw)
+    ttab = oracle.ExpertTable(tw.E, {e: configs.gen_expert(tw, 0, e) for e in range(tw.E)})
+    oracle.set_threads(1)
+    one_dec, n1, s1 = _oracle_rate(lambda i: oracle.moe_layer(x, lgs[i % 16], w.k, table), w.T,
+                                   max(2.0, args.cpu_seconds / 4))
+    one_tiny, n2, s2 = _oracle_rate(lambda i: oracle.moe_layer(tx, tlg, tw.k, ttab), tw.T, 2.0)
+    oracle.set_threads(threads)
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = os.cpu_count()
+    return dict(value=rate, unit="tokens/s", cores=min(w.T * w.k, threads), kind="oracle",
                 sample=f"{layers} whole decode layers (T={w.T}, E={w.E}, k={w.k}, d={w.d}, "
-                       f"f={w.f}, bf16 weights) cycling 16 routing sets, {spent:.1f} s of oracle time")
+                       f"f={w.f}, bf16 weights) cycling 16 routing sets, {spent:.1f} s of oracle "
+                       f"time on {threads} threads",
+                nproc=os.cpu_count(), affinity_cpus=affinity, omp_threads=threads,
+                one_core=dict(decode_tok_s=one_dec, decode_layers=n1,
+                              tiny_fp32_tok_s=one_tiny, tiny_layers=n2))
 
 
 def main():
@@ -634,6 +684,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true",
                     help="primary lines only: no decode T/alpha sweep and no MXFP4 extras")
+    ap.add_argument("--prefill-alpha", type=float, default=None,
+                    help="run the prefill workload at this Zipf alpha only (default: 0.2 and 1)")
     ap.add_argument("--weights", choices=["bf16", "mxfp4"], default="bf16",
                     help="expert weight format of the primary decode line (--workload decode)")
     args = ap.parse_args()
@@ -731,7 +783,9 @@ def main():
         "cpu_baseline": cpu,
         "extra": dict(decode_ffn_ms=dec["ffn_ms"], decode_unique_experts=dec["U_mean"],
                       decode_algorithmic_bytes_per_ffn=dec["algorithmic_bytes_per_call"],
-                      decode_tok_s_16_layer_graph=dec["tok_s_16_layer_graph"], **extra),
+                      decode_tok_s_16_layer_graph=dec["tok_s_16_layer_graph"],
+                      decode_step_bytes=dec["step_bytes"],
+                      decode_step_hbm_frac=dec["step_hbm_frac"], **extra),
     }
     print(json.dumps(line))
 

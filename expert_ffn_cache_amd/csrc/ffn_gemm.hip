@@ -59,6 +59,12 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("" ::: "memory");
 }
 
+// SiLU(g) * u with the hardware reciprocal (about 1 ulp in fp32): h is rounded to bf16 right
+// after, so an exact division would change nothing but the cost.
+__device__ __forceinline__ float swiglu(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
+
 template <int MODE, int YDT>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_tile256(FfnArgs p, int n_ntiles) {
@@ -126,7 +132,13 @@ void gemm_tile256(FfnArgs p, int n_ntiles) {
     const int e = lo;
     const int m_e = s_pref[e + 1] - s_pref[e];
     const int local = j - s_pref[e] * n_ntiles;
-    const int nt = local / m_e, mt = local - nt * m_e;
+    // items of one expert in groups of up to 4 m-tiles x all n-tiles, m-tile fastest: the 32
+    // consecutive items one XCD runs together form a 4 x 8 block of tiles, so each token slice
+    // and each weight slice of a step is fetched into that XCD's L2 once and read from it by
+    // 8 (resp. 4) workgroups (10% fewer L2 miss bytes than n-tile-major order)
+    const int grp = local / (4 * n_ntiles), first_m = grp * 4;
+    const int gsz = min(4, m_e - first_m), in = local - grp * 4 * n_ntiles;
+    const int nt = in / gsz, mt = first_m + (in - nt * gsz);
     const char* wbase = entry_of(p, e);
     if (!wbase) continue;
     const uint16_t* W = (const uint16_t*)wbase;
@@ -262,7 +274,7 @@ void gemm_tile256(FfnArgs p, int n_ntiles) {
         if (MODE == kGateUp) {
           const int unit = nt * (QBN / 2) + wn * 32 + r32;
           if (unit < p.f)
-            ((uint16_t*)p.h)[(size_t)(n0 + m) * ld + unit] = f32_to_bf16(silu(acc[i][0][v]) * acc[i][1][v]);
+            ((uint16_t*)p.h)[(size_t)(n0 + m) * ld + unit] = f32_to_bf16(swiglu(acc[i][0][v], acc[i][1][v]));
         } else {
 #pragma unroll
           for (int jn = 0; jn < 2; ++jn) {

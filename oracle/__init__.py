@@ -38,6 +38,10 @@ def lib():
         L.oracle_moe_layer.restype = None
         L.oracle_combine.argtypes = [vp, vp, vp, i32, i32, i32, vp]
         L.oracle_combine.restype = None
+        L.oracle_set_threads.argtypes = [i32]
+        L.oracle_set_threads.restype = None
+        L.oracle_max_threads.argtypes = []
+        L.oracle_max_threads.restype = i32
         _lib = L
     return _lib
 
@@ -172,3 +176,12 @@ def combine(yperm, inv, w):
     out = np.empty((T, d), dtype=np.float64)
     lib().oracle_combine(_p(yperm), _p(inv), _p(w), T, k, d, _p(out))
     return out
+
+
+def set_threads(n):
+    """Threads the oracle's parallel loops use from now on (1 = single core)."""
+    lib().oracle_set_threads(int(n))
+
+
+def max_threads():
+    return int(lib().oracle_max_threads())

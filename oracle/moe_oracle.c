@@ -33,6 +33,7 @@
  * fp32 (dtype 0) or bf16 bit patterns (dtype 1, upcast exactly).
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -157,32 +158,49 @@ void oracle_expert_ffn(const void* x, int xdtype, int d, int f, int k, const int
 }
 
 /* Whole layer for a list of tokens: out[q] = sum_j w[t][j] * FFN_{ids[t][j]}(x[t]),
- * j ascending, t = tokens[q].  Routes every token (ids, w written for all T). */
+ * j ascending, t = tokens[q].  Routes every token (ids, w written for all T).
+ * The (token, j) expert FFNs are independent, so they run in parallel, 64 tokens at a time;
+ * each token's weighted sum is then formed in j order.  Every output element is the same
+ * arithmetic however many threads run. */
 void oracle_moe_layer(const void* x, int xdtype, const float* logits, int T, int d, int E, int k,
                       int f, const void* const* wg, const void* const* wu, const void* const* wd,
                       int wdtype, int n_tok, const int32_t* tokens, int32_t* ids, double* w,
                       double* out) {
   oracle_route(logits, T, E, k, ids, w);
+  enum { CHUNK = 64 };
+  double* y = (double*)malloc(sizeof(double) * (size_t)CHUNK * k * d);
+  for (int q0 = 0; q0 < n_tok; q0 += CHUNK) {
+    const int nq = n_tok - q0 < CHUNK ? n_tok - q0 : CHUNK;
 #pragma omp parallel
-  {
-    double* h = (double*)malloc(sizeof(double) * (size_t)f);
-    double* y = (double*)malloc(sizeof(double) * (size_t)d);
+    {
+      double* h = (double*)malloc(sizeof(double) * (size_t)f);
 #pragma omp for schedule(dynamic, 1)
-    for (int q = 0; q < n_tok; ++q) {
-      const int t = tokens[q];
-      double* o = out + (int64_t)q * d;
+      for (int qj = 0; qj < nq * k; ++qj) {
+        const int t = tokens[q0 + qj / k], j = qj % k;
+        const int32_t e = ids[(int64_t)t * k + j];
+        expert_ffn(x, xdtype, (int64_t)t * d, wg[e], wu[e], wd[e], wdtype, d, f, h,
+                   y + (int64_t)qj * d);
+      }
+      free(h);
+    }
+#pragma omp parallel for schedule(static)
+    for (int qq = 0; qq < nq; ++qq) {
+      const int t = tokens[q0 + qq];
+      double* o = out + (int64_t)(q0 + qq) * d;
       for (int c = 0; c < d; ++c) o[c] = 0.0;
       for (int j = 0; j < k; ++j) {
-        const int32_t e = ids[(int64_t)t * k + j];
-        expert_ffn(x, xdtype, (int64_t)t * d, wg[e], wu[e], wd[e], wdtype, d, f, h, y);
         const double wj = w[(int64_t)t * k + j];
-        for (int c = 0; c < d; ++c) o[c] += wj * y[c];
+        const double* yj = y + ((int64_t)qq * k + j) * d;
+        for (int c = 0; c < d; ++c) o[c] += wj * yj[c];
       }
     }
-    free(h);
-    free(y);
   }
+  free(y);
 }
+
+/* Thread count of the parallel loops above (benchmark baselines time 1 and all cores). */
+void oracle_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
+int oracle_max_threads(void) { return omp_get_max_threads(); }
 
 /* a7 alone: out[t] = sum_j w[t][j] * yperm[inv[t*k+j]], j ascending (double). */
 void oracle_combine(const double* yperm, const int32_t* inv, const double* w, int T, int k, int d,
