@@ -53,6 +53,12 @@ def _ffn_bytes(w, U, y_bytes=4):
     return U * w.entry_bytes + A * w.d * 2 + 2 * A * w.f * 2 + A * w.d * y_bytes
 
 
+def _token_bytes(w, U):
+    """Algorithmic HBM bytes of one single-token one-launch layer: every used expert entry
+    once, the logits and x read, h written and read once (bf16), out written (fp32)."""
+    return U * w.entry_bytes + w.E * 4 + w.d * 2 + 2 * w.k * w.f * 2 + w.d * 4
+
+
 _STREAMS = {}
 
 
@@ -154,7 +160,10 @@ def bench_decode(args, torch, moe, T, alpha, arena, dtype=None):
         for r in range(R):
             layers[r].forward(x, logits[r], arena, w.entry_bytes, path=path, stream=s)
         s.synchronize()
-        U = [int((layers[r].counts > 0).sum().item()) for r in range(R)]
+        # experts each layer reads (from the routed ids: the one-launch single-token path
+        # leaves counts untouched)
+        U = [int(torch.unique(layers[r].ids).numel()) for r in range(R)]
+        fused = [layers[r].fusable and path == moe.MOE_PATH_AUTO for r in range(R)]
         if not args.no_graph:
             for r in range(R):
                 g = torch.cuda.CUDAGraph()
@@ -199,8 +208,8 @@ def bench_decode(args, torch, moe, T, alpha, arena, dtype=None):
             torch.cuda.synchronize()
             ms_multi = e2.elapsed_time(e3) / (reps * R)
             del gm
-    # the dominant entry point (expert FFN: gate/up + down weight-streaming kernels), timed
-    # per call with events on its stream
+    # the dominant entry point, timed per call with events on its stream: the expert FFN
+    # (gate/up + down weight-streaming kernels), or for one token the one-launch layer
     ffn_ms = []
     with torch.cuda.stream(s):
         n = max(args.steps, 2 * R)
@@ -208,18 +217,24 @@ def bench_decode(args, torch, moe, T, alpha, arena, dtype=None):
         for i in range(n):
             r = i % R
             starts[i].record(s)
-            layers[r].ffn(x, arena, w.entry_bytes, path=path, stream=s)
+            if fused[r]:
+                layers[r].decode_token(x, logits[r], arena, w.entry_bytes, stream=s)
+            else:
+                layers[r].ffn(x, arena, w.entry_bytes, path=path, stream=s)
             ends[i].record(s)
         torch.cuda.synchronize()
         ffn_ms = [starts[i].elapsed_time(ends[i]) for i in range(n)]
-        byts = [_ffn_bytes(w, U[i % R]) for i in range(n)]
+        byts = [(_token_bytes if fused[i % R] else _ffn_bytes)(w, U[i % R]) for i in range(n)]
     status = max(int(layers[r].status.item()) for r in range(R))
     if status != 0:
         raise RuntimeError(f"decode: device status {status}")
     ffn_avg_ms = float(np.mean(ffn_ms))
     achieved = float(np.sum(byts) / (np.sum(ffn_ms) * 1e-3) / 1e9)
     A = w.T * w.k
-    step_bytes = float(np.mean(byts)) + w.T * w.E * 4 + A * w.d * 4 + w.T * w.d * 4
+    if all(fused):
+        step_bytes = float(np.mean(byts))  # the launch is the whole step
+    else:
+        step_bytes = float(np.mean(byts)) + w.T * w.E * 4 + A * w.d * 4 + w.T * w.d * 4
     traffic = None
     if T == 8 and alpha == 0.2:  # what the committed counter summaries cover
         if dtype is None:
@@ -230,6 +245,7 @@ def bench_decode(args, torch, moe, T, alpha, arena, dtype=None):
     torch.cuda.empty_cache()
     return dict(
         workload=w.name, T=w.T, ms_per_step=ms, tok_s=w.T / (ms * 1e-3), U_mean=float(np.mean(U)),
+        dominant="moe_decode_token" if all(fused) else "moe_expert_ffn",
         ffn_ms=ffn_avg_ms,
         ms_per_layer_in_16_layer_graph=ms_multi,
         tok_s_16_layer_graph=None if ms_multi is None else w.T / (ms_multi * 1e-3),

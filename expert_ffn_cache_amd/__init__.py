@@ -22,6 +22,7 @@ MOE_EHIP = -3
 MOE_ECAPACITY = -4
 MOE_ERANGE = -5
 MOE_ETOOBIG = -6
+MOE_ETIMEOUT = -7
 
 MOE_F32 = 0
 MOE_BF16 = 1
@@ -36,7 +37,7 @@ EXPORTS = [
     "moe_permute_workspace_bytes", "moe_permute", "moe_route_permute", "moe_entry_bytes",
     "moe_expert_ffn_workspace_bytes",
     "moe_expert_ffn", "moe_expert_ffn_noalloc", "moe_expert_ffn_noalloc_max_bytes",
-    "moe_combine", "cache_init", "cache_lookup_update",
+    "moe_combine", "moe_decode_token_workspace_bytes", "moe_decode_token", "cache_init", "cache_lookup_update",
     "cache_lookup_update_split", "cache_fill",
     "cache_fill_device", "cache_fill_masks", "cache_resize", "layer_stream_prefetch", "moe_hbm_read_probe", "moe_copy_probe",
 ]
@@ -91,6 +92,9 @@ def lib():
                                         vp, vp, i32, vp, i32, i32, vp, vp], i32),
             "moe_expert_ffn_noalloc_max_bytes": ([], sz),
             "moe_combine": ([vp, i32, vp, vp, i32, i32, i32, vp, vp], i32),
+            "moe_decode_token_workspace_bytes": ([i32, i32], sz),
+            "moe_decode_token": ([vp, vp, i32, i32, i32, i32, vp, vp, sz, i32, vp, i32, vp, vp, vp,
+                                  sz, vp, vp, vp], i32),
             "cache_init": ([ctypes.POINTER(moe_cache_t), vp], i32),
             "cache_lookup_update": ([ctypes.POINTER(moe_cache_t), i32, vp, i32, i32, vp, vp, vp,
                                      vp], i32),
@@ -210,6 +214,18 @@ def moe_expert_ffn_noalloc_max_bytes():
 def moe_combine(y_perm, y_dtype, inv, topk_w, T, k, d, out, stream=None):
     _check("moe_combine", lib().moe_combine(_p(y_perm), y_dtype, _p(inv), _p(topk_w), T, k, d,
                                             _p(out), _s(stream)))
+
+
+def moe_decode_token_workspace_bytes(k, f):
+    return lib().moe_decode_token_workspace_bytes(k, f)
+
+
+def moe_decode_token(logits, x, E, k, d, f, expert_slot, arena, entry_stride, w_dtype, slot_key,
+                     key_base, topk_ids, topk_w, ws, ws_bytes, out, status=None, stream=None):
+    _check("moe_decode_token", lib().moe_decode_token(
+        _p(logits), _p(x), E, k, d, f, _p(expert_slot), _p(arena), entry_stride, w_dtype,
+        _p(slot_key), key_base, _p(topk_ids), _p(topk_w), _p(ws), ws_bytes, _p(out), _p(status),
+        _s(stream)))
 
 
 def cache_init(cache, stream=None):

@@ -1,0 +1,448 @@
+// One token through a routed-MoE layer in a single launch: top-k softmax routing, the k
+// selected experts' SwiGLU FFNs and the gate-weighted combine (bf16 weights).
+//
+// A one-token decode step reads k whole experts (302 MB at k = 6, d = 4096, f = 2048) and
+// does next to no arithmetic on them, so its time is the weight stream plus whatever stops
+// that stream.  Run as separate launches (routing, gate/up, down, combine) it stops at every
+// boundary: each launch pays its ramp and its tail, and the routing and combine launches move
+// almost no bytes at all.  Here one grid of G workgroups, all resident at once, walks a fixed
+// list of work items (workgroup b takes items b, b + G, b + 2G, ...):
+//   gate/up item (j, b): the units u of block b of the j-th selected expert,
+//       h_j[u] = SiLU(x . W_gate_j[u]) * (x . W_up_j[u])      (fp32 sums, h rounded to bf16)
+//   down item b: the output channels o of block b,
+//       out[o] = sum_j w_j * (h_j . W_down_j[o])               (j ascending, fp32)
+// and every workgroup routes the token itself first (the logits are only 4E bytes), so no
+// launch waits for another.  Gate/up items come first in the list.  A down item needs all of
+// h, so each workgroup, once its gate/up items are done, raises its own flag; a down item
+// issues its weight loads first and only then waits, once per workgroup, for every flag, so
+// the weight stream runs on through the change of phase.
+//
+// Cross-workgroup traffic stays cheap on this chip: the eight L2 caches are not coherent
+// with one another, and the fences that would make ordinary stores visible across them
+// (write back or invalidate a whole L2) cost more than the layer when hundreds of workgroups
+// issue them, as does a device-scope atomic per work item on one counter (each is
+// serialised at the memory side).  So h is written and read with device-coherent accesses
+// (they bypass the non-coherent L2 copies), a wave waits for its own h stores to be
+// acknowledged before the workgroup raises its flag, and the flags are plain
+// device-coherent stores, one per workgroup, each in its own 128-byte line.  A flag holds the
+// launch's epoch (one more than the epoch word in the workspace, which workgroup 0 advances
+// once it has seen every flag), so nothing is reset between calls or graph replays.  The
+// wait ends once every workgroup has run its gate/up items, which needs the G workgroups to
+// be resident together: G is the occupancy bound for this kernel on an otherwise idle GPU.
+// The wait is bounded all the same (MOE_ETIMEOUT), so calls that share the GPU with another
+// launch that never yields fail rather than hang.
+//
+// The dot products are those of the multi-token weight-streaming kernels (lane l takes the
+// 16-byte chunks l, l + 64, ... of a row; packed bf16 products with fp32 accumulation; one
+// cross-lane sum per row) in the same order, so `out` is bit-identical to routing, grouping,
+// the expert FFN with fp32 outputs and the combine run as separate calls.
+#include <algorithm>
+
+#include "ffn_args.h"
+#include "route_dev.h"
+#include "wave.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr int kTokThreads = 256;     // four waves
+constexpr int kTokDownCh = 4;        // output channels per down item, one per wave
+constexpr int kTokMaxGrid = 2048;    // workgroups (flags) at most
+constexpr int kTokLine = 128;        // bytes per flag (one cache line each)
+constexpr size_t kTokHdrBytes = (size_t)kTokLine * (kTokMaxGrid + 2);  // epoch, then the flags
+constexpr unsigned kTokSpinLimit = 1u << 18;  // polls of the flags (well over a second)
+
+struct TokArgs {
+  const float* logits;  // [E] fp32, or nullptr: ids and weights are read from topk_ids / topk_w
+  const uint16_t* x;    // [d] bf16
+  int E, k, d, f;
+  const int32_t* expert_slot;
+  const char* arena;
+  size_t stride;
+  const int32_t* slot_key;
+  int key_base;
+  int32_t* topk_ids;
+  float* topk_w;
+  char* hdr;      // epoch word at 0, flag of workgroup b at kTokLine * (b + 1)
+  uint16_t* h;    // [k][f] bf16
+  float* out;     // [d] fp32
+  int32_t* status;
+  int n_gu, n_items;
+};
+
+// Device-coherent 32-bit accesses (relaxed atomics at device scope: served past the
+// per-XCD L2 caches, so other XCDs see them without any cache maintenance).
+__device__ __forceinline__ uint32_t coh_load(const uint32_t* a) {
+  return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void coh_store(uint32_t* a, uint32_t v) {
+  __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void coh_store16(uint16_t* a, uint16_t v) {
+  __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t* flag_of(const TokArgs& p, int b) {
+  return (uint32_t*)(p.hdr + (size_t)kTokLine * (b + 1));
+}
+
+// acc + a . b over 8 bf16 pairs, four packed products in element order (the pairs taken
+// with shufflevector, as the multi-token kernels take them).
+__device__ __forceinline__ float dot8(u32x4 a, u32x4 b, float acc) {
+  const bf16x8 x = as_bf16x8(a), y = as_bf16x8(b);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 0, 1),
+                                        __builtin_shufflevector(y, y, 0, 1), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 2, 3),
+                                        __builtin_shufflevector(y, y, 2, 3), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 4, 5),
+                                        __builtin_shufflevector(y, y, 4, 5), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 6, 7),
+                                        __builtin_shufflevector(y, y, 6, 7), acc, false);
+  return acc;
+}
+
+// Wave index as a scalar, so row addresses built from it stay in scalar registers.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// A pointer every lane holds the same value of, moved to scalar registers.
+__device__ __forceinline__ const char* uniform_ptr(const char* q) {
+  const uint64_t v = (uint64_t)q;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const char*)(((uint64_t)hi << 32) | lo);
+}
+
+// Byte offset of lane chunk i of a row of nck 16-byte chunks: chunk lane + 64 i, clamped to
+// the last one (a lane past the row re-reads it and leaves it out of its sums), so that every
+// load of a row is issued without a per-lane branch.
+__device__ __forceinline__ uint32_t chunk_off(int i, int nck) {
+  return (uint32_t)min((int)(threadIdx.x & 63) + 64 * i, nck - 1) * 16u;
+}
+
+__device__ __forceinline__ u32x4 ldrow(const void* row, uint32_t off) {
+  return ldg16_nt((const char*)row + off);
+}
+
+// Lane chunk i of a row staged in LDS, or zeros for a lane past the row (a select, not a
+// branch: every product below is taken by every lane, so no load is left pending on a path
+// that skips it).
+__device__ __forceinline__ u32x4 lds_chunk(const uint16_t* row, int i, int nck) {
+  const u32x4 v = *(const u32x4*)((const char*)row + chunk_off(i, nck));
+  const bool in = (int)(threadIdx.x & 63) + 64 * i < nck;
+  return u32x4{in ? v[0] : 0u, in ? v[1] : 0u, in ? v[2] : 0u, in ? v[3] : 0u};
+}
+
+// Gate/up item: UPW units per wave of the a-th selected expert; lane 0 stores the wave's
+// h values device-coherently.
+template <int NCHD, int UPW>
+__device__ __forceinline__ void gateup_item(const TokArgs& p, const uint16_t* xs,
+                                            const char* const* ent, int item) {
+  constexpr int UPB = 4 * UPW;
+  const int nub = p.f / UPB;
+  const int a = item / nub, ub = item - a * nub;
+  const int wave = wave_id();
+  const int d = p.d, nck = d >> 3;
+  const char* e = uniform_ptr(ent[a]);
+  const int u0 = ub * UPB + wave * UPW;
+  u32x4 wg[UPW][NCHD], wu[UPW][NCHD];
+  if (e) {
+#pragma unroll
+    for (int uu = 0; uu < UPW; ++uu) {
+      const uint16_t* pg = (const uint16_t*)e + (size_t)(u0 + uu) * d;
+      const uint16_t* pu = pg + (size_t)p.f * d;
+#pragma unroll
+      for (int i = 0; i < NCHD; ++i) {
+        wg[uu][i] = ldrow(pg, chunk_off(i, nck));
+        wu[uu][i] = ldrow(pu, chunk_off(i, nck));
+      }
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);  // the loads stay ahead of what follows
+  if (!e) return;
+  float g[UPW], u[UPW];
+#pragma unroll
+  for (int uu = 0; uu < UPW; ++uu) g[uu] = u[uu] = 0.f;
+#pragma unroll
+  for (int i = 0; i < NCHD; ++i) {
+    const u32x4 xv = lds_chunk(xs, i, nck);
+#pragma unroll
+    for (int uu = 0; uu < UPW; ++uu) {
+      g[uu] = dot8(xv, wg[uu][i], g[uu]);
+      u[uu] = dot8(xv, wu[uu][i], u[uu]);
+    }
+  }
+  uint16_t hv[UPW];
+#pragma unroll
+  for (int uu = 0; uu < UPW; ++uu) hv[uu] = f32_to_bf16(silu(wave_sum_f32(g[uu])) * wave_sum_f32(u[uu]));
+  if ((threadIdx.x & 63) == 0) {
+    uint16_t* dst = p.h + (size_t)a * p.f + u0;
+    if (UPW == 2)  // two adjacent units: one 32-bit store (u0 is even)
+      coh_store((uint32_t*)dst, (uint32_t)hv[0] | ((uint32_t)hv[UPW - 1] << 16));
+    else
+#pragma unroll
+      for (int uu = 0; uu < UPW; ++uu) coh_store16(dst + uu, hv[uu]);
+  }
+}
+
+// Raises this workgroup's flag once every wave's h stores are acknowledged (device-coherent
+// stores count as done only when the device-wide copy holds them).
+__device__ __forceinline__ void publish(const TokArgs& p, uint32_t epoch) {
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 7, 15));  // this wave's stores
+  __syncthreads();
+  if (threadIdx.x == 0) coh_store(flag_of(p, blockIdx.x), epoch);
+}
+
+// Wave 0 polls the flags of all G workgroups until each holds `epoch` (eight 128-byte lines
+// per lane per round, all loads in flight together).  Returns false on giving up.
+__device__ __forceinline__ bool wait_flags(const TokArgs& p, uint32_t epoch) {
+  const int G = gridDim.x, lane = threadIdx.x & 63;
+  for (unsigned polls = 0; polls < kTokSpinLimit; ++polls) {
+    bool all = true;
+    for (int b0 = 0; b0 < G; b0 += 64 * 8) {
+      uint32_t v[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) v[r] = coh_load(flag_of(p, min(b0 + 64 * r + lane, G - 1)));
+#pragma unroll
+      for (int r = 0; r < 8; ++r) all &= v[r] == epoch;
+    }
+    if (__all(all)) return true;
+    __builtin_amdgcn_s_sleep(8);
+  }
+  return false;
+}
+
+// Waits for every flag, then stages all k rows of h in LDS with device-coherent loads.
+__device__ __forceinline__ void wait_and_stage_h(const TokArgs& p, uint16_t* hs, uint32_t epoch) {
+  if (threadIdx.x < 64 && !wait_flags(p, epoch) && threadIdx.x == 0)
+    set_status(p.status, MOE_ETIMEOUT);
+  __syncthreads();
+  const int n = p.k * p.f / 2;  // 32-bit words
+  const uint32_t* src = (const uint32_t*)p.h;
+  uint32_t* dst = (uint32_t*)hs;
+  for (int q0 = 0; q0 < n; q0 += 8 * kTokThreads) {
+    uint32_t v[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) v[r] = coh_load(src + min(q0 + r * kTokThreads + (int)threadIdx.x, n - 1));
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int q = q0 + r * kTokThreads + threadIdx.x;
+      if (q < n) dst[q] = v[r];
+    }
+  }
+  __syncthreads();
+}
+
+// Down rows of output channel o of the selected experts j0 .. j0 + JG - 1 into registers.
+template <int NCHF, int JG>
+__device__ __forceinline__ void down_load(const TokArgs& p, const char* const* ent, int j0, int o,
+                                          u32x4 (&wv)[JG][NCHF]) {
+  const int nck = p.f >> 3;
+#pragma unroll
+  for (int jj = 0; jj < JG; ++jj) {
+    const int j = j0 + jj;
+    if (j < p.k) {
+      const char* e = uniform_ptr(ent[j]);
+      if (e) {
+        const char* row = e + (2 * (size_t)p.f * p.d + (size_t)o * p.f) * 2;
+#pragma unroll
+        for (int i = 0; i < NCHF; ++i) wv[jj][i] = ldrow(row, chunk_off(i, nck));
+      }
+    }
+  }
+}
+
+// acc after adding w_j * (h_j . W_down_j[o]) for those experts, j ascending.
+template <int NCHF, int JG>
+__device__ __forceinline__ float down_dot(const TokArgs& p, const uint16_t* hs,
+                                          const char* const* ent, const float* wj, int j0,
+                                          const u32x4 (&wv)[JG][NCHF], float acc) {
+  const int f = p.f, nck = f >> 3;
+#pragma unroll
+  for (int jj = 0; jj < JG; ++jj) {
+    const int j = j0 + jj;
+    if (j < p.k && ent[j]) {
+      float s = 0.f;
+#pragma unroll
+      for (int i = 0; i < NCHF; ++i) s = dot8(lds_chunk(hs + j * f, i, nck), wv[jj][i], s);
+      acc = fmaf(wj[j], wave_sum_f32(s), acc);
+    }
+  }
+  return acc;
+}
+
+// Down item: wave w takes output channel 4b + w for all k experts, JG experts' rows at a
+// time in registers (one group when k <= JG); the first group's loads are in flight before
+// any wait for h.
+template <int NCHF, int JG>
+__device__ __forceinline__ void down_item(const TokArgs& p, uint16_t* hs, const char* const* ent,
+                                          const float* wj, int b, bool staged, uint32_t epoch) {
+  const int o = b * kTokDownCh + wave_id();
+  u32x4 wv[JG][NCHF];
+  down_load<NCHF, JG>(p, ent, 0, o, wv);
+  __builtin_amdgcn_sched_barrier(0);  // the loads stay ahead of what follows
+  if (!staged) wait_and_stage_h(p, hs, epoch);
+  float acc = down_dot<NCHF, JG>(p, hs, ent, wj, 0, wv, 0.f);
+  for (int j0 = JG; j0 < p.k; j0 += JG) {
+    down_load<NCHF, JG>(p, ent, j0, o, wv);
+    acc = down_dot<NCHF, JG>(p, hs, ent, wj, j0, wv, acc);
+  }
+  if ((threadIdx.x & 63) == 0) p.out[o] = acc;
+}
+
+// NPL: logits per lane in the routing wave (E <= 64 * NPL); NCHD / NCHF: 16-byte chunks per
+// lane of a gate/up row (d <= 512 * NCHD) and of a down row (f <= 512 * NCHF); UPW: units per
+// wave in a gate/up item; JG: experts per register group in a down item.
+template <int NPL, int NCHD, int UPW, int NCHF, int JG>
+__global__ __launch_bounds__(kTokThreads) __attribute__((amdgpu_waves_per_eu(NCHF == 4 && JG <= 6 ? 2 : 1)))
+void decode_token(TokArgs p) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];  // x [d], then h [k][f]
+  __shared__ int32_t s_id[kMaxK];
+  __shared__ float s_w[kMaxK];
+  __shared__ const char* s_ent[kMaxK];
+  __shared__ uint32_t s_epoch;
+  uint16_t* xs = lds;
+  uint16_t* hs = lds + p.d;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int k = p.k;
+  uint32_t epoch = 0;
+  if (wave == 0) {
+    if (tid == 0) epoch = coh_load((const uint32_t*)p.hdr) + 1u;  // this launch's flag value
+    if (p.logits) {
+      unsigned long long key[NPL];
+      route_keys<NPL>(p.logits, p.E, key);
+      route_pick<NPL>(key, k, s_id, s_w, nullptr);
+    } else if (lane < k) {
+      s_id[lane] = p.topk_ids[lane];
+      s_w[lane] = p.topk_w[lane];
+    }
+  } else {
+    // waves 1..3 stage x: every load in flight before the first LDS write
+    constexpr int XR = (NCHD * 64 + kTokThreads - 65) / (kTokThreads - 64);
+    const int nck = p.d >> 3;
+    u32x4 xv[XR];
+#pragma unroll
+    for (int r = 0; r < XR; ++r) {
+      const int q = tid - 64 + r * (kTokThreads - 64);
+      if (q < nck) xv[r] = ldg16(p.x + (size_t)q * 8);
+    }
+#pragma unroll
+    for (int r = 0; r < XR; ++r) {
+      const int q = tid - 64 + r * (kTokThreads - 64);
+      if (q < nck) *(u32x4*)&xs[q * 8] = xv[r];
+    }
+  }
+  if (tid == 0) s_epoch = epoch;
+  __syncthreads();
+  if (tid < k) {
+    const int e = s_id[tid];
+    const char* ent = nullptr;
+    if (e >= 0 && e < p.E) {
+      const int s = p.expert_slot ? p.expert_slot[e] : e;
+      if (s >= 0 && (!p.slot_key || p.slot_key[s] == p.key_base + e))
+        ent = p.arena + (size_t)s * p.stride;
+    }
+    if (!ent) set_status(p.status, MOE_ERANGE);
+    s_ent[tid] = ent;
+    if (blockIdx.x == 0 && p.logits) {
+      if (p.topk_ids) p.topk_ids[tid] = e;
+      if (p.topk_w) p.topk_w[tid] = s_w[tid];
+    }
+  }
+  __syncthreads();
+  epoch = s_epoch;
+
+  // Items b, b + G, ...: the gate/up ones (below n_gu) first, then the down ones.
+  const int G = gridDim.x;
+  int item = blockIdx.x;
+  for (; item < p.n_gu; item += G) gateup_item<NCHD, UPW>(p, xs, s_ent, item);
+  publish(p, epoch);
+  bool staged = false;
+  for (; item < p.n_items; item += G) {
+    down_item<NCHF, JG>(p, hs, s_ent, s_w, item - p.n_gu, staged, epoch);
+    staged = true;
+  }
+  if (blockIdx.x == 0) {
+    // every workgroup has read the epoch word (each raised its flag after reading it):
+    // advance it for the next launch
+    if (!staged && tid < 64 && !wait_flags(p, epoch) && tid == 0) set_status(p.status, MOE_ETIMEOUT);
+    if (tid == 0) coh_store((uint32_t*)p.hdr, epoch);
+  }
+}
+
+template <int NPL, int NCHD, int UPW, int NCHF, int JG>
+int launch_token(const TokArgs& p, size_t lds, hipStream_t stream) {
+  auto kern = decode_token<NPL, NCHD, UPW, NCHF, JG>;
+  int occ = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, kTokThreads, lds) != hipSuccess ||
+      occ <= 0)
+    occ = 1;
+  // Two workgroups per compute unit (eight waves, each with 24-32 KB of weight loads in
+  // flight, is enough to keep HBM busy): at d = 4096, f = 2048, k = 6 the 1536 gate/up and
+  // 1024 down items then divide evenly, 3 and 2 per workgroup, so no workgroup runs a tail
+  // of extra items.
+  const int grid = std::min(std::min(p.n_items, std::min(occ, 2) * num_cus()), kTokMaxGrid);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kTokThreads), lds, stream, p);
+  MOE_LAUNCH_CHECK();
+  return MOE_OK;
+}
+
+template <int NPL, int NCHD, int UPW>
+int launch_token_f(TokArgs p, size_t lds, hipStream_t stream) {
+  p.n_gu = p.k * (p.f / (4 * UPW));
+  p.n_items = p.n_gu + p.d / kTokDownCh;
+  if (p.f > 2048) return launch_token<NPL, NCHD, UPW, 16, 2>(p, lds, stream);
+  if (p.k <= 4) return launch_token<NPL, NCHD, UPW, 4, 4>(p, lds, stream);
+  if (p.k <= 6) return launch_token<NPL, NCHD, UPW, 4, 6>(p, lds, stream);
+  return launch_token<NPL, NCHD, UPW, 4, 8>(p, lds, stream);
+}
+
+template <int NPL>
+int launch_token_d(const TokArgs& p, size_t lds, hipStream_t stream) {
+  if (p.d <= 4096) return launch_token_f<NPL, 8, 2>(p, lds, stream);
+  return launch_token_f<NPL, 16, 1>(p, lds, stream);
+}
+
+}  // namespace
+
+extern "C" size_t moe_decode_token_workspace_bytes(int k, int f) {
+  if (k <= 0 || f <= 0) return kTokHdrBytes;
+  return kTokHdrBytes + ((size_t)k * f * 2 + 255) / 256 * 256;
+}
+
+extern "C" int moe_decode_token(const float* logits, const void* x, int E, int k, int d, int f,
+                                const int32_t* expert_slot, const void* arena, size_t entry_stride,
+                                int w_dtype, const int32_t* slot_key, int key_base,
+                                int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes,
+                                float* out, int32_t* status, hipStream_t stream) {
+  if (E <= 0 || E > kMaxE || k <= 0 || k > kMaxK || k > E) return MOE_EINVAL;
+  if (d <= 0 || f <= 0 || d % 64 != 0 || f % 64 != 0) return MOE_EINVAL;
+  if (w_dtype != MOE_BF16) return MOE_EUNSUPPORTED;
+  if (d > 8192 || f > 8192 || ((size_t)d + (size_t)k * f) * 2 > 65536) return MOE_EUNSUPPORTED;
+  if (entry_stride < 3 * (size_t)d * f * 2 || entry_stride % 16 != 0) return MOE_EINVAL;
+  if (!x || !arena || !ws || !out) return MOE_EINVAL;
+  if (!logits && (!topk_ids || !topk_w)) return MOE_EINVAL;
+  if (!moe_aligned16(x) || !moe_aligned16(arena) || !moe_aligned16(ws) || !moe_aligned16(out))
+    return MOE_EINVAL;
+  if (ws_bytes < moe_decode_token_workspace_bytes(k, f)) return MOE_EINVAL;
+  TokArgs p{};
+  p.logits = logits;
+  p.x = (const uint16_t*)x;
+  p.E = E;
+  p.k = k;
+  p.d = d;
+  p.f = f;
+  p.expert_slot = expert_slot;
+  p.arena = (const char*)arena;
+  p.stride = entry_stride;
+  p.slot_key = slot_key;
+  p.key_base = key_base;
+  p.topk_ids = topk_ids;
+  p.topk_w = topk_w;
+  p.hdr = (char*)ws;
+  p.h = (uint16_t*)((char*)ws + kTokHdrBytes);
+  p.out = out;
+  p.status = status;
+  const size_t lds = ((size_t)d + (size_t)k * f) * 2;
+  if (E <= 256) return launch_token_d<4>(p, lds, stream);
+  return launch_token_d<16>(p, lds, stream);
+}

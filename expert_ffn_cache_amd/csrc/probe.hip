@@ -79,8 +79,9 @@ extern "C" const char* moe_strerror(int status) {
     case MOE_ECAPACITY: return "more unique experts requested than cache slots";
     case MOE_ERANGE: return "id, layer or slot out of range, or stale cache slot";
     case MOE_ETOOBIG: return "request larger than a fixed library limit (no-allocation scratch)";
+    case MOE_ETIMEOUT: return "a bounded device wait gave up";
     default: return "unknown status";
   }
 }
 
-extern "C" int moe_abi_version(void) { return 2; }
+extern "C" int moe_abi_version(void) { return 3; }

@@ -29,14 +29,19 @@ __device__ __forceinline__ float from_order_bits(uint32_t k) {
 }
 
 // Keys of one token's E logits at row (lane l: experts l, l+64, ...); called by a full wave.
+// All NPL loads are issued before the first is used (a lane past E reads logit E - 1 and
+// gets key 0), so the row costs one memory round trip.
 template <int NPL>
 __device__ __forceinline__ void route_keys(const float* __restrict__ row, int E,
                                            unsigned long long (&key)[NPL]) {
   const int lane = threadIdx.x & 63;
+  float v[NPL];
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) v[i] = row[min(lane + 64 * i, E - 1)];
 #pragma unroll
   for (int i = 0; i < NPL; ++i) {
     const int e = lane + 64 * i;
-    key[i] = e < E ? ((unsigned long long)order_bits(row[e]) << 32) | (uint32_t)(~(uint32_t)e) : 0ull;
+    key[i] = e < E ? ((unsigned long long)order_bits(v[i]) << 32) | (uint32_t)(~(uint32_t)e) : 0ull;
   }
 }
 

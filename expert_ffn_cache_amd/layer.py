@@ -1,7 +1,8 @@
 """One routed-MoE layer forward as a sequence of library calls on caller-owned buffers.
 
 route + permute (one launch for small T) -> expert FFN -> combine, each a libmoecache.so
-entry point.
+entry point; a single token with bf16 weights takes moe_decode_token instead, which does all
+of it in one launch (same result, bit for bit, with fp32 expert outputs).
 Device memory comes from torch; this class only allocates the intermediate
 buffers once and forwards pointers.
 """
@@ -9,7 +10,14 @@ import torch
 
 from . import (MOE_F32, MOE_BF16, MOE_PATH_AUTO, moe_route, moe_permute, moe_route_permute,
                moe_permute_workspace_bytes, moe_expert_ffn, moe_expert_ffn_workspace_bytes,
-               moe_combine)
+               moe_combine, moe_decode_token, moe_decode_token_workspace_bytes)
+
+
+def decode_token_supported(T, k, d, f, dtype, w_dtype, y_dtype):
+    """Shapes and types moe_decode_token takes (one token, bf16 activations and weights, fp32
+    expert outputs, x and h within 64 KB of LDS)."""
+    return (T == 1 and dtype == MOE_BF16 and w_dtype == MOE_BF16 and y_dtype == MOE_F32
+            and d <= 8192 and f <= 8192 and (d + k * f) * 2 <= 65536)
 
 
 def _tdtype(code):
@@ -39,6 +47,11 @@ class MoeLayer:
         self.ffn_ws = torch.empty(self.ffn_ws_bytes, dtype=torch.uint8, device=dev)
         self.y_perm = torch.empty((max(A, 1), d), dtype=_tdtype(y_dtype), device=dev)
         self.out = torch.empty((T, d), dtype=torch.float32, device=dev)
+        self.fusable = decode_token_supported(T, k, d, f, dtype, self.w_dtype, y_dtype)
+        if self.fusable:
+            # counters of the one-launch path: zero before the first call, zero after each
+            self.tok_ws_bytes = moe_decode_token_workspace_bytes(k, f)
+            self.tok_ws = torch.zeros(self.tok_ws_bytes, dtype=torch.uint8, device=dev)
 
     def route(self, logits, stream=None):
         moe_route(logits, self.T, self.E, self.k, self.ids, self.w, stream)
@@ -64,8 +77,23 @@ class MoeLayer:
         moe_combine(self.y_perm, self.y_dtype, self.inv, self.w, self.T, self.k, self.d,
                     self.out, stream)
 
+    def decode_token(self, x, logits, arena, entry_stride, expert_slot=None, slot_key=None,
+                     key_base=0, stream=None):
+        """The whole layer for one token in one launch (logits None: route with self.ids and
+        self.w as they stand).  Leaves counts/offsets/perm/inv untouched."""
+        moe_decode_token(logits, x, self.E, self.k, self.d, self.f, expert_slot, arena,
+                         entry_stride, self.w_dtype, slot_key, key_base, self.ids, self.w,
+                         self.tok_ws, self.tok_ws_bytes, self.out, self.status, stream)
+        return self.out
+
     def forward(self, x, logits, arena, entry_stride, expert_slot=None, path=MOE_PATH_AUTO,
-                stream=None):
+                stream=None, fused=None):
+        """fused: None = the one-launch path where it applies (path AUTO), True = require it,
+        False = separate launches."""
+        if fused is None:
+            fused = self.fusable and path == MOE_PATH_AUTO
+        if fused:
+            return self.decode_token(x, logits, arena, entry_stride, expert_slot, stream=stream)
         self.route_permute(logits, stream)
         self.ffn(x, arena, entry_stride, expert_slot, path=path, stream=stream)
         self.combine(stream)

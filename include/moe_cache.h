@@ -62,6 +62,7 @@ extern "C" {
 #define MOE_ECAPACITY (-4)    /* more unique experts requested than cache slots */
 #define MOE_ERANGE (-5)       /* id, layer or slot out of range; stale cache slot */
 #define MOE_ETOOBIG (-6)      /* larger than a fixed library limit (no-allocation scratch) */
+#define MOE_ETIMEOUT (-7)     /* a bounded device wait gave up (see moe_decode_token) */
 
 #define MOE_F32 0   /* IEEE binary32 */
 #define MOE_BF16 1  /* bfloat16 (upper half of binary32) */
@@ -217,6 +218,49 @@ size_t moe_expert_ffn_noalloc_max_bytes(void);
  * experts), with the gate weights of moe_route. */
 int moe_combine(const void* y_perm, int y_dtype, const int32_t* inv, const float* topk_w, int T,
                 int k, int d, float* out, hipStream_t stream);
+
+/* Workspace bytes moe_decode_token needs: a 262400-byte header (a launch
+ * epoch word and one 128-byte flag per workgroup), then the SwiGLU
+ * intermediate [k][f] bf16. */
+size_t moe_decode_token_workspace_bytes(int k, int f);
+
+/* One token's routed-MoE layer in a single launch: moe_route_permute,
+ * moe_expert_ffn and moe_combine for T = 1 (a decode step of one sequence:
+ * the token activates only its k selected experts, RTX-4090 page, "How the
+ * MoE memory hierarchy works"), with MOE_BF16 weights and activations.
+ *   logits [E] fp32: the token is routed as by moe_route (top-k, softmax over
+ *   the k winners) and the ids and weights are written to topk_ids [k] and
+ *   topk_w [k] when those are not NULL.  logits NULL: topk_ids and topk_w
+ *   are inputs instead (ids routed earlier, e.g. before a cache lookup).
+ *   x [d] bf16; the weights of expert e at arena + expert_slot[e]*entry_stride
+ *   (expert_slot NULL = identity), laid out as for moe_expert_ffn.
+ *   out [d] fp32: out = sum_{j ascending} topk_w[j] * FFN_{topk_ids[j]}(x), the
+ *   FFN as in moe_expert_ffn with h rounded to bf16 and each expert's output
+ *   kept in fp32; bit-identical to moe_route_permute + moe_expert_ffn
+ *   (y_dtype MOE_F32) + moe_combine on the same device.
+ *   An id outside [0, E), a negative slot, or (slot_key not NULL) a slot
+ *   whose key is not key_base + e sets *status = MOE_ERANGE and leaves that
+ *   expert's term out of the sum.
+ *   ws: moe_decode_token_workspace_bytes(k, f) bytes, 16-byte aligned,
+ *   zero-filled by the caller before its first use and not written by the
+ *   caller afterwards (each call advances the epoch word at its head by one;
+ *   nothing needs clearing between calls or graph replays).  Calls that share
+ *   a workspace must not overlap in time (order them on one stream).
+ *   The launch is one grid of workgroups, as many as fit on the GPU at once,
+ *   that run all gate/up work before any down work; a workgroup's first down
+ *   item waits (bounded) until every workgroup has finished its gate/up
+ *   work.  That needs all of them resident together: a call that overlaps
+ *   another moe_decode_token call on the same GPU, or a launch that holds the
+ *   compute units and never finishes, can make the wait give up, which sets
+ *   *status = MOE_ETIMEOUT (the result is then undefined).
+ * Shapes: d, f multiples of 64, d <= 8192, f <= 8192 and (d + k*f)*2 <= 65536
+ * bytes (x and h are held in LDS), else MOE_EUNSUPPORTED; other weight types
+ * MOE_EUNSUPPORTED.  Argument errors return before anything is enqueued. */
+int moe_decode_token(const float* logits, const void* x, int E, int k, int d, int f,
+                     const int32_t* expert_slot, const void* arena, size_t entry_stride,
+                     int w_dtype, const int32_t* slot_key, int key_base, int32_t* topk_ids,
+                     float* topk_w, void* ws, size_t ws_bytes, float* out, int32_t* status,
+                     hipStream_t stream);
 
 /* ---- global LRU expert cache over (layer, expert) entries ------------------ */
 

@@ -30,9 +30,9 @@ def test_every_declared_symbol_is_exported():
 def test_strerror_and_version():
     assert moe.strerror(moe.MOE_OK) == "ok"
     for code in (moe.MOE_EINVAL, moe.MOE_EUNSUPPORTED, moe.MOE_EHIP, moe.MOE_ECAPACITY,
-                 moe.MOE_ERANGE, moe.MOE_ETOOBIG):
+                 moe.MOE_ERANGE, moe.MOE_ETOOBIG, moe.MOE_ETIMEOUT):
         assert moe.strerror(code) not in ("ok", "unknown status")
-    assert moe.abi_version() == 2
+    assert moe.abi_version() == 3
 
 
 def test_entry_bytes():
@@ -178,3 +178,41 @@ def test_noalloc_ffn_limit_is_checked_on_the_host():
     assert L.moe_expert_ffn_noalloc(*args) == moe.MOE_ETOOBIG
     bad = list(args); bad[4] = -1
     assert L.moe_expert_ffn_noalloc(*bad) == moe.MOE_EINVAL
+
+
+def test_decode_token_arguments_are_checked_on_the_host():
+    """moe_decode_token rejects bad arguments and shapes it does not take before any HIP call
+    (fake but 16-byte aligned addresses: nothing is dereferenced on these paths)."""
+    L = moe.lib()
+    hdr = 128 * (2048 + 2)  # epoch word, then one 128-byte flag per workgroup (2048 at most)
+    assert moe.moe_decode_token_workspace_bytes(6, 2048) == hdr + 6 * 2048 * 2
+    assert moe.moe_decode_token_workspace_bytes(0, 2048) == hdr
+    A = 1 << 20  # stand-in address
+
+    def call(E=256, k=6, d=4096, f=2048, logits=A, x=A, arena=A, stride=None, wdt=moe.MOE_BF16,
+             ids=A, w=A, ws=A, ws_bytes=None, out=A):
+        stride = 3 * d * f * 2 if stride is None else stride
+        ws_bytes = moe.moe_decode_token_workspace_bytes(k, f) if ws_bytes is None else ws_bytes
+        return L.moe_decode_token(logits, x, E, k, d, f, None, arena, stride, wdt, None, 0, ids,
+                                  w, ws, ws_bytes, out, None, None)
+
+    assert call(k=0) == moe.MOE_EINVAL
+    assert call(k=17, E=1024) == moe.MOE_EINVAL
+    assert call(E=4, k=5) == moe.MOE_EINVAL
+    assert call(E=1025) == moe.MOE_EINVAL
+    assert call(d=100) == moe.MOE_EINVAL
+    assert call(f=96) == moe.MOE_EINVAL
+    assert call(wdt=moe.MOE_MXFP4) == moe.MOE_EUNSUPPORTED
+    assert call(wdt=moe.MOE_F32) == moe.MOE_EUNSUPPORTED
+    assert call(d=8256) == moe.MOE_EUNSUPPORTED
+    assert call(f=8256, k=1) == moe.MOE_EUNSUPPORTED
+    assert call(k=16, E=256, f=2048) == moe.MOE_EUNSUPPORTED   # x and h past 64 KB of LDS
+    assert call(stride=3 * 4096 * 2048 * 2 - 16) == moe.MOE_EINVAL
+    assert call(stride=3 * 4096 * 2048 * 2 + 8) == moe.MOE_EINVAL
+    assert call(x=None) == moe.MOE_EINVAL
+    assert call(out=None) == moe.MOE_EINVAL
+    assert call(ws=None) == moe.MOE_EINVAL
+    assert call(x=A + 8) == moe.MOE_EINVAL
+    assert call(ws_bytes=hdr) == moe.MOE_EINVAL
+    assert call(logits=None, ids=None) == moe.MOE_EINVAL
+    assert call(logits=None, w=None) == moe.MOE_EINVAL
