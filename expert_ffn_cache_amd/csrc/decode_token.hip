@@ -13,24 +13,24 @@
 //       out[o] = sum_j w_j * (h_j . W_down_j[o])               (j ascending, fp32)
 // and every workgroup routes the token itself first (the logits are only 4E bytes), so no
 // launch waits for another.  Gate/up items come first in the list.  A down item needs all of
-// h, so each workgroup, once its gate/up items are done, raises its own flag; a down item
-// issues its weight loads first and only then waits, once per workgroup, for every flag, so
-// the weight stream runs on through the change of phase.
+// h, so a workgroup's first down item issues its weight loads and only then waits, once per
+// workgroup, until all of h is there; the weight stream runs on through the change of phase.
 //
 // Cross-workgroup traffic stays cheap on this chip: the eight L2 caches are not coherent
 // with one another, and the fences that would make ordinary stores visible across them
 // (write back or invalidate a whole L2) cost more than the layer when hundreds of workgroups
 // issue them, as does a device-scope atomic per work item on one counter (each is
-// serialised at the memory side).  So h is written and read with device-coherent accesses
-// (they bypass the non-coherent L2 copies), a wave waits for its own h stores to be
-// acknowledged before the workgroup raises its flag, and the flags are plain
-// device-coherent stores, one per workgroup, each in its own 128-byte line.  A flag holds the
-// launch's epoch (one more than the epoch word in the workspace, which workgroup 0 advances
-// once it has seen every flag), so nothing is reset between calls or graph replays.  The
-// wait ends once every workgroup has run its gate/up items, which needs the G workgroups to
-// be resident together: G is the occupancy bound for this kernel on an otherwise idle GPU.
-// The wait is bounded all the same (MOE_ETIMEOUT), so calls that share the GPU with another
-// launch that never yields fail rather than hang.
+// serialised at the memory side), and so does waiting for stores to be acknowledged before
+// raising a flag.  So every h value carries its own flag: each UPW-unit group of h is one
+// 8-byte device-coherent store of the values and the launch's epoch (single-copy atomic),
+// and a reader loads the entries device-coherently and takes them once every epoch
+// matches.  The epoch word at the head of the workspace is one less than the launch's
+// epoch; workgroup 0 advances it once it has seen every entry of this launch (so every
+// workgroup has read it), and nothing is reset between calls or graph replays.  The wait
+// ends once every workgroup has run its gate/up items, which needs the G workgroups to be
+// resident together: G is within the occupancy bound for this kernel on an otherwise idle
+// GPU.  The wait is bounded all the same (MOE_ETIMEOUT), so calls that share the GPU with
+// another launch that never yields fail rather than hang.
 //
 // The dot products are those of the multi-token weight-streaming kernels (lane l takes the
 // 16-byte chunks l, l + 64, ... of a row; packed bf16 products with fp32 accumulation; one
@@ -48,10 +48,8 @@ namespace {
 
 constexpr int kTokThreads = 256;     // four waves
 constexpr int kTokDownCh = 4;        // output channels per down item, one per wave
-constexpr int kTokMaxGrid = 2048;    // workgroups (flags) at most
-constexpr int kTokLine = 128;        // bytes per flag (one cache line each)
-constexpr size_t kTokHdrBytes = (size_t)kTokLine * (kTokMaxGrid + 2);  // epoch, then the flags
-constexpr unsigned kTokSpinLimit = 1u << 18;  // polls of the flags (well over a second)
+constexpr size_t kTokHdrBytes = 256;  // the epoch word, then padding
+constexpr unsigned kTokSpinLimit = 1u << 18;  // polls of h (well over a second)
 
 struct TokArgs {
   const float* logits;  // [E] fp32, or nullptr: ids and weights are read from topk_ids / topk_w
@@ -64,8 +62,8 @@ struct TokArgs {
   int key_base;
   int32_t* topk_ids;
   float* topk_w;
-  char* hdr;      // epoch word at 0, flag of workgroup b at kTokLine * (b + 1)
-  uint16_t* h;    // [k][f] bf16
+  uint32_t* epoch_word;
+  uint64_t* hent;  // h entries: UPW units of h (bf16, low half first) | launch epoch << 32
   float* out;     // [d] fp32
   int32_t* status;
   int n_gu, n_items;
@@ -79,11 +77,11 @@ __device__ __forceinline__ uint32_t coh_load(const uint32_t* a) {
 __device__ __forceinline__ void coh_store(uint32_t* a, uint32_t v) {
   __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void coh_store16(uint16_t* a, uint16_t v) {
-  __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ uint64_t coh_load64(const uint64_t* a) {
+  return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ uint32_t* flag_of(const TokArgs& p, int b) {
-  return (uint32_t*)(p.hdr + (size_t)kTokLine * (b + 1));
+__device__ __forceinline__ void coh_store64(uint64_t* a, uint64_t v) {
+  __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // acc + a . b over 8 bf16 pairs, four packed products in element order (the pairs taken
@@ -133,10 +131,10 @@ __device__ __forceinline__ u32x4 lds_chunk(const uint16_t* row, int i, int nck) 
 }
 
 // Gate/up item: UPW units per wave of the a-th selected expert; lane 0 stores the wave's
-// h values device-coherently.
+// h values with the launch's epoch in one device-coherent 8-byte entry.
 template <int NCHD, int UPW>
 __device__ __forceinline__ void gateup_item(const TokArgs& p, const uint16_t* xs,
-                                            const char* const* ent, int item) {
+                                            const char* const* ent, int item, uint32_t epoch) {
   constexpr int UPB = 4 * UPW;
   const int nub = p.f / UPB;
   const int a = item / nub, ub = item - a * nub;
@@ -175,61 +173,44 @@ __device__ __forceinline__ void gateup_item(const TokArgs& p, const uint16_t* xs
 #pragma unroll
   for (int uu = 0; uu < UPW; ++uu) hv[uu] = f32_to_bf16(silu(wave_sum_f32(g[uu])) * wave_sum_f32(u[uu]));
   if ((threadIdx.x & 63) == 0) {
-    uint16_t* dst = p.h + (size_t)a * p.f + u0;
-    if (UPW == 2)  // two adjacent units: one 32-bit store (u0 is even)
-      coh_store((uint32_t*)dst, (uint32_t)hv[0] | ((uint32_t)hv[UPW - 1] << 16));
-    else
-#pragma unroll
-      for (int uu = 0; uu < UPW; ++uu) coh_store16(dst + uu, hv[uu]);
+    uint32_t v = hv[0];
+    if (UPW == 2) v |= (uint32_t)hv[UPW - 1] << 16;
+    coh_store64(p.hent + ((size_t)a * p.f + u0) / UPW, (uint64_t)v | ((uint64_t)epoch << 32));
   }
 }
 
-// Raises this workgroup's flag once every wave's h stores are acknowledged (device-coherent
-// stores count as done only when the device-wide copy holds them).
-__device__ __forceinline__ void publish(const TokArgs& p, uint32_t epoch) {
-  __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 7, 15));  // this wave's stores
-  __syncthreads();
-  if (threadIdx.x == 0) coh_store(flag_of(p, blockIdx.x), epoch);
-}
-
-// Wave 0 polls the flags of all G workgroups until each holds `epoch` (eight 128-byte lines
-// per lane per round, all loads in flight together).  Returns false on giving up.
-__device__ __forceinline__ bool wait_flags(const TokArgs& p, uint32_t epoch) {
-  const int G = gridDim.x, lane = threadIdx.x & 63;
+// Stages all k rows of h in LDS once every entry carries this launch's epoch: each thread
+// loads its entries (eight in flight at a time) and writes the values; the workgroup repeats
+// until no thread found a stale entry.  Returns false on giving up.
+template <int UPW>
+__device__ __forceinline__ bool stage_h(const TokArgs& p, uint16_t* hs, uint32_t epoch) {
+  const int n = p.k * p.f / UPW;
   for (unsigned polls = 0; polls < kTokSpinLimit; ++polls) {
-    bool all = true;
-    for (int b0 = 0; b0 < G; b0 += 64 * 8) {
-      uint32_t v[8];
+    int stale = 0;
+    for (int q0 = 0; q0 < n; q0 += 8 * kTokThreads) {
+      uint64_t v[8];
 #pragma unroll
-      for (int r = 0; r < 8; ++r) v[r] = coh_load(flag_of(p, min(b0 + 64 * r + lane, G - 1)));
+      for (int r = 0; r < 8; ++r)
+        v[r] = coh_load64(p.hent + min(q0 + r * kTokThreads + (int)threadIdx.x, n - 1));
 #pragma unroll
-      for (int r = 0; r < 8; ++r) all &= v[r] == epoch;
+      for (int r = 0; r < 8; ++r) {
+        const int q = q0 + r * kTokThreads + threadIdx.x;
+        if (q < n) {
+          stale |= (uint32_t)(v[r] >> 32) != epoch;
+          if (UPW == 2) ((uint32_t*)hs)[q] = (uint32_t)v[r];
+          else hs[q] = (uint16_t)v[r];
+        }
+      }
     }
-    if (__all(all)) return true;
+    if (!__syncthreads_or(stale)) return true;
     __builtin_amdgcn_s_sleep(8);
   }
   return false;
 }
 
-// Waits for every flag, then stages all k rows of h in LDS with device-coherent loads.
+template <int UPW>
 __device__ __forceinline__ void wait_and_stage_h(const TokArgs& p, uint16_t* hs, uint32_t epoch) {
-  if (threadIdx.x < 64 && !wait_flags(p, epoch) && threadIdx.x == 0)
-    set_status(p.status, MOE_ETIMEOUT);
-  __syncthreads();
-  const int n = p.k * p.f / 2;  // 32-bit words
-  const uint32_t* src = (const uint32_t*)p.h;
-  uint32_t* dst = (uint32_t*)hs;
-  for (int q0 = 0; q0 < n; q0 += 8 * kTokThreads) {
-    uint32_t v[8];
-#pragma unroll
-    for (int r = 0; r < 8; ++r) v[r] = coh_load(src + min(q0 + r * kTokThreads + (int)threadIdx.x, n - 1));
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int q = q0 + r * kTokThreads + threadIdx.x;
-      if (q < n) dst[q] = v[r];
-    }
-  }
-  __syncthreads();
+  if (!stage_h<UPW>(p, hs, epoch) && threadIdx.x == 0) set_status(p.status, MOE_ETIMEOUT);
 }
 
 // Down rows of output channel o of the selected experts j0 .. j0 + JG - 1 into registers.
@@ -273,14 +254,14 @@ __device__ __forceinline__ float down_dot(const TokArgs& p, const uint16_t* hs,
 // Down item: wave w takes output channel 4b + w for all k experts, JG experts' rows at a
 // time in registers (one group when k <= JG); the first group's loads are in flight before
 // any wait for h.
-template <int NCHF, int JG>
+template <int NCHF, int JG, int UPW>
 __device__ __forceinline__ void down_item(const TokArgs& p, uint16_t* hs, const char* const* ent,
                                           const float* wj, int b, bool staged, uint32_t epoch) {
   const int o = b * kTokDownCh + wave_id();
   u32x4 wv[JG][NCHF];
   down_load<NCHF, JG>(p, ent, 0, o, wv);
   __builtin_amdgcn_sched_barrier(0);  // the loads stay ahead of what follows
-  if (!staged) wait_and_stage_h(p, hs, epoch);
+  if (!staged) wait_and_stage_h<UPW>(p, hs, epoch);
   float acc = down_dot<NCHF, JG>(p, hs, ent, wj, 0, wv, 0.f);
   for (int j0 = JG; j0 < p.k; j0 += JG) {
     down_load<NCHF, JG>(p, ent, j0, o, wv);
@@ -306,7 +287,7 @@ void decode_token(TokArgs p) {
   const int k = p.k;
   uint32_t epoch = 0;
   if (wave == 0) {
-    if (tid == 0) epoch = coh_load((const uint32_t*)p.hdr) + 1u;  // this launch's flag value
+    if (tid == 0) epoch = coh_load(p.epoch_word) + 1u;  // this launch's epoch
     if (p.logits) {
       unsigned long long key[NPL];
       route_keys<NPL>(p.logits, p.E, key);
@@ -354,18 +335,17 @@ void decode_token(TokArgs p) {
   // Items b, b + G, ...: the gate/up ones (below n_gu) first, then the down ones.
   const int G = gridDim.x;
   int item = blockIdx.x;
-  for (; item < p.n_gu; item += G) gateup_item<NCHD, UPW>(p, xs, s_ent, item);
-  publish(p, epoch);
+  for (; item < p.n_gu; item += G) gateup_item<NCHD, UPW>(p, xs, s_ent, item, epoch);
   bool staged = false;
   for (; item < p.n_items; item += G) {
-    down_item<NCHF, JG>(p, hs, s_ent, s_w, item - p.n_gu, staged, epoch);
+    down_item<NCHF, JG, UPW>(p, hs, s_ent, s_w, item - p.n_gu, staged, epoch);
     staged = true;
   }
   if (blockIdx.x == 0) {
-    // every workgroup has read the epoch word (each raised its flag after reading it):
-    // advance it for the next launch
-    if (!staged && tid < 64 && !wait_flags(p, epoch) && tid == 0) set_status(p.status, MOE_ETIMEOUT);
-    if (tid == 0) coh_store((uint32_t*)p.hdr, epoch);
+    // every workgroup has a gate/up item and read the epoch word before storing its h: once
+    // all of h is of this launch, advance the word for the next one
+    if (!staged) wait_and_stage_h<UPW>(p, hs, epoch);
+    if (tid == 0) coh_store(p.epoch_word, epoch);
   }
 }
 
@@ -380,7 +360,7 @@ int launch_token(const TokArgs& p, size_t lds, hipStream_t stream) {
   // flight, is enough to keep HBM busy): at d = 4096, f = 2048, k = 6 the 1536 gate/up and
   // 1024 down items then divide evenly, 3 and 2 per workgroup, so no workgroup runs a tail
   // of extra items.
-  const int grid = std::min(std::min(p.n_items, std::min(occ, 2) * num_cus()), kTokMaxGrid);
+  const int grid = std::min(p.n_gu, std::min(occ, 2) * num_cus());  // each has a gate/up item
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kTokThreads), lds, stream, p);
   MOE_LAUNCH_CHECK();
   return MOE_OK;
@@ -406,7 +386,7 @@ int launch_token_d(const TokArgs& p, size_t lds, hipStream_t stream) {
 
 extern "C" size_t moe_decode_token_workspace_bytes(int k, int f) {
   if (k <= 0 || f <= 0) return kTokHdrBytes;
-  return kTokHdrBytes + ((size_t)k * f * 2 + 255) / 256 * 256;
+  return kTokHdrBytes + (size_t)k * f * 8;  // an 8-byte entry per unit at most (UPW = 1)
 }
 
 extern "C" int moe_decode_token(const float* logits, const void* x, int E, int k, int d, int f,
@@ -438,8 +418,8 @@ extern "C" int moe_decode_token(const float* logits, const void* x, int E, int k
   p.key_base = key_base;
   p.topk_ids = topk_ids;
   p.topk_w = topk_w;
-  p.hdr = (char*)ws;
-  p.h = (uint16_t*)((char*)ws + kTokHdrBytes);
+  p.epoch_word = (uint32_t*)ws;
+  p.hent = (uint64_t*)((char*)ws + kTokHdrBytes);
   p.out = out;
   p.status = status;
   const size_t lds = ((size_t)d + (size_t)k * f) * 2;

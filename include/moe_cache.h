@@ -219,9 +219,9 @@ size_t moe_expert_ffn_noalloc_max_bytes(void);
 int moe_combine(const void* y_perm, int y_dtype, const int32_t* inv, const float* topk_w, int T,
                 int k, int d, float* out, hipStream_t stream);
 
-/* Workspace bytes moe_decode_token needs: a 262400-byte header (a launch
- * epoch word and one 128-byte flag per workgroup), then the SwiGLU
- * intermediate [k][f] bf16. */
+/* Workspace bytes moe_decode_token needs: a 256-byte header (the launch epoch
+ * word), then the SwiGLU intermediate as 8-byte entries (up to two bf16 values
+ * and the epoch of the launch that wrote them), k*f entries at most. */
 size_t moe_decode_token_workspace_bytes(int k, int f);
 
 /* One token's routed-MoE layer in a single launch: moe_route_permute,
@@ -246,7 +246,7 @@ size_t moe_decode_token_workspace_bytes(int k, int f);
  *   caller afterwards (each call advances the epoch word at its head by one;
  *   nothing needs clearing between calls or graph replays).  Calls that share
  *   a workspace must not overlap in time (order them on one stream).
- *   The launch is one grid of workgroups, as many as fit on the GPU at once,
+ *   The launch is one grid of workgroups, no more than fit on the GPU at once,
  *   that run all gate/up work before any down work; a workgroup's first down
  *   item waits (bounded) until every workgroup has finished its gate/up
  *   work.  That needs all of them resident together: a call that overlaps

@@ -184,8 +184,8 @@ def test_decode_token_arguments_are_checked_on_the_host():
     """moe_decode_token rejects bad arguments and shapes it does not take before any HIP call
     (fake but 16-byte aligned addresses: nothing is dereferenced on these paths)."""
     L = moe.lib()
-    hdr = 128 * (2048 + 2)  # epoch word, then one 128-byte flag per workgroup (2048 at most)
-    assert moe.moe_decode_token_workspace_bytes(6, 2048) == hdr + 6 * 2048 * 2
+    hdr = 256  # the launch epoch word, then an 8-byte entry per unit of h at most
+    assert moe.moe_decode_token_workspace_bytes(6, 2048) == hdr + 6 * 2048 * 8
     assert moe.moe_decode_token_workspace_bytes(0, 2048) == hdr
     A = 1 << 20  # stand-in address
 
