@@ -83,7 +83,7 @@ CSRC = os.path.join(ROOT, "expert_ffn_cache_amd", "csrc")
 # include), which the committed counter summary was taken on
 DECODE_FFN_SOURCES = [os.path.join(CSRC, n) for n in ("common.h", "ffn_args.h", "wave.h", "ffn_dot.hip")]
 # the same for MXFP4 weights (FP4-expanding MFMA kernels)
-MXFP4_FFN_SOURCES = [os.path.join(CSRC, n) for n in ("common.h", "ffn_args.h", "ffn_mx.hip")]
+MXFP4_FFN_SOURCES = [os.path.join(CSRC, n) for n in ("common.h", "ffn_args.h", "mx_dev.h", "ffn_mx.hip")]
 
 
 def sources_sha256(paths):

@@ -1,5 +1,5 @@
 // One token through a routed-MoE layer in a single launch: top-k softmax routing, the k
-// selected experts' SwiGLU FFNs and the gate-weighted combine (bf16 weights).
+// selected experts' SwiGLU FFNs and the gate-weighted combine (bf16 or MXFP4 weights).
 //
 // A one-token decode step reads k whole experts (302 MB at k = 6, d = 4096, f = 2048) and
 // does next to no arithmetic on them, so its time is the weight stream plus whatever stops
@@ -39,6 +39,7 @@
 #include <algorithm>
 
 #include "ffn_args.h"
+#include "mx_dev.h"
 #include "route_dev.h"
 #include "wave.h"
 
@@ -270,19 +271,19 @@ __device__ __forceinline__ void down_item(const TokArgs& p, uint16_t* hs, const 
   if ((threadIdx.x & 63) == 0) p.out[o] = acc;
 }
 
-// NPL: logits per lane in the routing wave (E <= 64 * NPL); NCHD / NCHF: 16-byte chunks per
-// lane of a gate/up row (d <= 512 * NCHD) and of a down row (f <= 512 * NCHF); UPW: units per
-// wave in a gate/up item; JG: experts per register group in a down item.
-template <int NPL, int NCHD, int UPW, int NCHF, int JG>
-__global__ __launch_bounds__(kTokThreads) __attribute__((amdgpu_waves_per_eu(NCHF == 4 && JG <= 6 ? 2 : 1)))
-void decode_token(TokArgs p) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];  // x [d], then h [k][f]
-  __shared__ int32_t s_id[kMaxK];
-  __shared__ float s_w[kMaxK];
-  __shared__ const char* s_ent[kMaxK];
-  __shared__ uint32_t s_epoch;
-  uint16_t* xs = lds;
-  uint16_t* hs = lds + p.d;
+// Shared memory of a workgroup besides the dynamic x / h rows.
+struct TokShared {
+  int32_t id[kMaxK];
+  float w[kMaxK];
+  const char* ent[kMaxK];
+  uint32_t epoch;
+};
+
+// Every workgroup's start: wave 0 reads the epoch word and routes the token (or takes the
+// given ids and weights) while waves 1..3 stage x in LDS (NCHD: 16-byte chunks per lane of a
+// row, d <= 512 * NCHD); then the k entries are looked up.  Returns this launch's epoch.
+template <int NPL, int NCHD>
+__device__ __forceinline__ uint32_t tok_prologue(const TokArgs& p, uint16_t* xs, TokShared& sh) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int k = p.k;
   uint32_t epoch = 0;
@@ -291,13 +292,13 @@ void decode_token(TokArgs p) {
     if (p.logits) {
       unsigned long long key[NPL];
       route_keys<NPL>(p.logits, p.E, key);
-      route_pick<NPL>(key, k, s_id, s_w, nullptr);
+      route_pick<NPL>(key, k, sh.id, sh.w, nullptr);
     } else if (lane < k) {
-      s_id[lane] = p.topk_ids[lane];
-      s_w[lane] = p.topk_w[lane];
+      sh.id[lane] = p.topk_ids[lane];
+      sh.w[lane] = p.topk_w[lane];
     }
   } else {
-    // waves 1..3 stage x: every load in flight before the first LDS write
+    // every load in flight before the first LDS write
     constexpr int XR = (NCHD * 64 + kTokThreads - 65) / (kTokThreads - 64);
     const int nck = p.d >> 3;
     u32x4 xv[XR];
@@ -312,10 +313,10 @@ void decode_token(TokArgs p) {
       if (q < nck) *(u32x4*)&xs[q * 8] = xv[r];
     }
   }
-  if (tid == 0) s_epoch = epoch;
+  if (tid == 0) sh.epoch = epoch;
   __syncthreads();
   if (tid < k) {
-    const int e = s_id[tid];
+    const int e = sh.id[tid];
     const char* ent = nullptr;
     if (e >= 0 && e < p.E) {
       const int s = p.expert_slot ? p.expert_slot[e] : e;
@@ -323,48 +324,200 @@ void decode_token(TokArgs p) {
         ent = p.arena + (size_t)s * p.stride;
     }
     if (!ent) set_status(p.status, MOE_ERANGE);
-    s_ent[tid] = ent;
+    sh.ent[tid] = ent;
     if (blockIdx.x == 0 && p.logits) {
       if (p.topk_ids) p.topk_ids[tid] = e;
-      if (p.topk_w) p.topk_w[tid] = s_w[tid];
+      if (p.topk_w) p.topk_w[tid] = sh.w[tid];
     }
   }
   __syncthreads();
-  epoch = s_epoch;
+  return sh.epoch;
+}
 
+// Workgroup 0's last step: every workgroup has a gate/up item and read the epoch word before
+// storing its h; once all of h is of this launch, advance the word for the next one.
+template <int UPW>
+__device__ __forceinline__ void tok_epilogue(const TokArgs& p, uint16_t* hs, uint32_t epoch,
+                                             bool staged) {
+  if (blockIdx.x != 0) return;
+  if (!staged) wait_and_stage_h<UPW>(p, hs, epoch);
+  if (threadIdx.x == 0) coh_store(p.epoch_word, epoch);
+}
+
+// bf16 weights.  NPL: logits per lane in the routing wave (E <= 64 * NPL); NCHD / NCHF:
+// 16-byte chunks per lane of a gate/up row (d <= 512 * NCHD) and of a down row
+// (f <= 512 * NCHF); UPW: units per wave in a gate/up item; JG: experts per register group in
+// a down item.
+template <int NPL, int NCHD, int UPW, int NCHF, int JG>
+__global__ __launch_bounds__(kTokThreads) __attribute__((amdgpu_waves_per_eu(NCHF == 4 && JG <= 6 ? 2 : 1)))
+void decode_token(TokArgs p) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];  // x [d], then h [k][f]
+  __shared__ TokShared sh;
+  uint16_t* xs = lds;
+  uint16_t* hs = lds + p.d;
+  const uint32_t epoch = tok_prologue<NPL, NCHD>(p, xs, sh);
   // Items b, b + G, ...: the gate/up ones (below n_gu) first, then the down ones.
   const int G = gridDim.x;
   int item = blockIdx.x;
-  for (; item < p.n_gu; item += G) gateup_item<NCHD, UPW>(p, xs, s_ent, item, epoch);
+  for (; item < p.n_gu; item += G) gateup_item<NCHD, UPW>(p, xs, sh.ent, item, epoch);
   bool staged = false;
   for (; item < p.n_items; item += G) {
-    down_item<NCHF, JG, UPW>(p, hs, s_ent, s_w, item - p.n_gu, staged, epoch);
+    down_item<NCHF, JG, UPW>(p, hs, sh.ent, sh.w, item - p.n_gu, staged, epoch);
     staged = true;
   }
-  if (blockIdx.x == 0) {
-    // every workgroup has a gate/up item and read the epoch word before storing its h: once
-    // all of h is of this launch, advance the word for the next one
-    if (!staged) wait_and_stage_h<UPW>(p, hs, epoch);
-    if (tid == 0) coh_store(p.epoch_word, epoch);
-  }
+  tok_epilogue<UPW>(p, hs, epoch, staged);
 }
 
-template <int NPL, int NCHD, int UPW, int NCHF, int JG>
-int launch_token(const TokArgs& p, size_t lds, hipStream_t stream) {
-  auto kern = decode_token<NPL, NCHD, UPW, NCHF, JG>;
+// ------------------------------------------------------------------ MXFP4 weights
+// Entry: [codes W_gate][codes W_up][codes W_down][scales W_gate][scales W_up][scales W_down],
+// tiles of 16 rows x 128 elements (mx_dev.h).  Both item kinds give a 16-row strip to the
+// workgroup's four waves, wave ks taking tiles ks, ks + 4, ... (all of them in flight at
+// once) and the partial sums meeting in LDS: the split and order of the weight-streaming
+// MXFP4 kernels for one token, so the results are theirs bit for bit.
+
+// Gate/up item (a, rt): units 16 rt .. 16 rt + 15 of the a-th selected expert.  GT: tiles
+// per wave per matrix (d <= 512 * GT).
+template <int GT>
+__device__ __forceinline__ void mx_gateup_item(const TokArgs& p, const uint16_t* xs,
+                                               const char* const* ent, int item, uint32_t epoch) {
+  const int nbg = p.f / 16;
+  const int a = item / nbg, rt = item - a * nbg;
+  const int lane = threadIdx.x & 63, ks = wave_id(), q = lane >> 4;
+  const int K = p.d, nk = (K + 127) >> 7, krem = (K & 127) >> 5, kshort = krem ? nk - 1 : -1;
+  const uint8_t* W = (const uint8_t*)uniform_ptr(ent[a]);
+  MxTile<2> t[GT];
+  if (W) {
+    const size_t fd = (size_t)p.f * K;
+    const uint8_t* const cb[2] = {W + (size_t)rt * 8 * K, W + fd / 2 + (size_t)rt * 8 * K};
+    const uint8_t* const sb[2] = {W + 3 * fd / 2 + (size_t)rt * (K / 2),
+                                  W + 3 * fd / 2 + fd / 32 + (size_t)rt * (K / 2)};
+#pragma unroll
+    for (int r = 0; r < GT; ++r) {
+      const int kt = ks + 4 * r;
+      if (kt < nk) mx_load_tile<2>(t[r], cb, sb, kt, lane, kt != kshort || q < krem);
+    }
+  }
+  f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  if (W) {
+#pragma unroll
+    for (int r = 0; r < GT; ++r) {
+      const int kt = ks + 4 * r;
+      if (kt < nk) {
+        const bool ok = kt != kshort || q < krem;
+        mx_tile_mma<2>(t[r], xs + kt * 128 + (ok ? 32 * q : 0), acc);
+      }
+    }
+  }
+  mx_reduce<2, 4>(acc, 0, ks, lane);
+  // lane l < 16 of wave 0 holds the token's row of unit 16 rt + l
+  if (W && ks == 0 && lane < 16) {
+    const uint16_t hv = f32_to_bf16(silu(acc[0][0]) * acc[1][0]);
+    coh_store64(p.hent + (size_t)a * p.f + 16 * rt + lane, (uint64_t)hv | ((uint64_t)epoch << 32));
+  }
+  __syncthreads();  // the partial sums are read before the next item's waves store theirs
+}
+
+// Down item rt: output channels 16 rt .. 16 rt + 15, all k experts (KMAX >= k), every
+// expert's tiles in flight before any wait for h; out = sum_j w_j y_j, j ascending.  DT:
+// tiles per wave per expert (f <= 512 * DT).
+template <int DT, int KMAX>
+__device__ __forceinline__ void mx_down_item(const TokArgs& p, uint16_t* hs,
+                                             const char* const* ent, const float* wj, int rt,
+                                             bool staged, uint32_t epoch) {
+  const int lane = threadIdx.x & 63, ks = wave_id(), q = lane >> 4;
+  const int K = p.f, nk = (K + 127) >> 7, krem = (K & 127) >> 5, kshort = krem ? nk - 1 : -1;
+  const size_t fd = (size_t)K * p.d;
+  MxTile<1> t[KMAX][DT];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    const uint8_t* W = j < p.k ? (const uint8_t*)uniform_ptr(ent[j]) : nullptr;
+    if (W) {
+      const uint8_t* const cb[1] = {W + fd + (size_t)rt * 8 * K};
+      const uint8_t* const sb[1] = {W + 3 * fd / 2 + 2 * (fd / 32) + (size_t)rt * (K / 2)};
+#pragma unroll
+      for (int r = 0; r < DT; ++r) {
+        const int kt = ks + 4 * r;
+        if (kt < nk) mx_load_tile<1>(t[j][r], cb, sb, kt, lane, kt != kshort || q < krem);
+      }
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);  // the loads stay ahead of what follows
+  if (!staged) wait_and_stage_h<1>(p, hs, epoch);
+  float o = 0.f;
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    if (j < p.k) {
+      const bool have = ent[j] != nullptr;
+      f32x4 acc[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
+      if (have) {
+#pragma unroll
+        for (int r = 0; r < DT; ++r) {
+          const int kt = ks + 4 * r;
+          if (kt < nk) {
+            const bool ok = kt != kshort || q < krem;
+            mx_tile_mma<1>(t[j][r], hs + j * K + kt * 128 + (ok ? 32 * q : 0), acc);
+          }
+        }
+      }
+      mx_reduce<1, 4>(acc, 0, ks, lane);
+      if (have) o = fmaf(wj[j], acc[0][0], o);
+      __syncthreads();  // the partial sums are read before the next expert's are stored
+    }
+  }
+  if (ks == 0 && lane < 16) p.out[16 * rt + lane] = o;
+}
+
+template <int NPL, int KMAX>
+__global__ __launch_bounds__(kTokThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void decode_token_mx(TokArgs p) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];  // x [d], then h [k][f]
+  __shared__ TokShared sh;
+  uint16_t* xs = lds;
+  uint16_t* hs = lds + p.d;
+  const uint32_t epoch = tok_prologue<NPL, 8>(p, xs, sh);
+  const int G = gridDim.x;
+  int item = blockIdx.x;
+  for (; item < p.n_gu; item += G) mx_gateup_item<8>(p, xs, sh.ent, item, epoch);
+  bool staged = false;
+  for (; item < p.n_items; item += G) {
+    mx_down_item<4, KMAX>(p, hs, sh.ent, sh.w, item - p.n_gu, staged, epoch);
+    staged = true;
+  }
+  tok_epilogue<1>(p, hs, epoch, staged);
+}
+
+// Grid: two workgroups per compute unit where the occupancy allows (eight waves, each with
+// 24-32 KB of weight loads in flight, keep HBM busy; at d = 4096, f = 2048, k = 6 the bf16
+// items then divide evenly, 3 gate/up and 2 down per workgroup), and no more workgroups than
+// gate/up items (each must store some of h before workgroup 0 may advance the epoch).
+template <typename K>
+int launch_grid(K kern, const TokArgs& p, size_t lds, hipStream_t stream) {
   int occ = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, kTokThreads, lds) != hipSuccess ||
       occ <= 0)
     occ = 1;
-  // Two workgroups per compute unit (eight waves, each with 24-32 KB of weight loads in
-  // flight, is enough to keep HBM busy): at d = 4096, f = 2048, k = 6 the 1536 gate/up and
-  // 1024 down items then divide evenly, 3 and 2 per workgroup, so no workgroup runs a tail
-  // of extra items.
-  const int grid = std::min(p.n_gu, std::min(occ, 2) * num_cus());  // each has a gate/up item
+  const int grid = std::min(p.n_gu, std::min(occ, 2) * num_cus());
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kTokThreads), lds, stream, p);
   MOE_LAUNCH_CHECK();
   return MOE_OK;
 }
+
+template <int NPL, int NCHD, int UPW, int NCHF, int JG>
+int launch_token(const TokArgs& p, size_t lds, hipStream_t stream) {
+  return launch_grid(decode_token<NPL, NCHD, UPW, NCHF, JG>, p, lds, stream);
+}
+
+template <int NPL>
+int launch_token_mx(TokArgs p, size_t lds, hipStream_t stream) {
+  p.n_gu = p.k * (p.f / 16);
+  p.n_items = p.n_gu + p.d / 16;
+  if (p.k <= 6) return launch_grid(decode_token_mx<NPL, 6>, p, lds, stream);
+  return launch_grid(decode_token_mx<NPL, 8>, p, lds, stream);
+}
+
+// MXFP4 shapes the one-launch kernel takes: gate/up strips of d <= 4096 and down strips of
+// f <= 2048 held whole in registers, k <= 8.
+bool token_mx_supported(int k, int d, int f) { return d <= 4096 && f <= 2048 && k <= 8; }
 
 template <int NPL, int NCHD, int UPW>
 int launch_token_f(TokArgs p, size_t lds, hipStream_t stream) {
@@ -396,9 +549,11 @@ extern "C" int moe_decode_token(const float* logits, const void* x, int E, int k
                                 float* out, int32_t* status, hipStream_t stream) {
   if (E <= 0 || E > kMaxE || k <= 0 || k > kMaxK || k > E) return MOE_EINVAL;
   if (d <= 0 || f <= 0 || d % 64 != 0 || f % 64 != 0) return MOE_EINVAL;
-  if (w_dtype != MOE_BF16) return MOE_EUNSUPPORTED;
+  const bool mx = w_dtype == MOE_MXFP4;
+  if (w_dtype != MOE_BF16 && !mx) return MOE_EUNSUPPORTED;
   if (d > 8192 || f > 8192 || ((size_t)d + (size_t)k * f) * 2 > 65536) return MOE_EUNSUPPORTED;
-  if (entry_stride < 3 * (size_t)d * f * 2 || entry_stride % 16 != 0) return MOE_EINVAL;
+  if (mx && !token_mx_supported(k, d, f)) return MOE_EUNSUPPORTED;
+  if (entry_stride < moe_entry_bytes(d, f, w_dtype) || entry_stride % 16 != 0) return MOE_EINVAL;
   if (!x || !arena || !ws || !out) return MOE_EINVAL;
   if (!logits && (!topk_ids || !topk_w)) return MOE_EINVAL;
   if (!moe_aligned16(x) || !moe_aligned16(arena) || !moe_aligned16(ws) || !moe_aligned16(out))
@@ -423,6 +578,7 @@ extern "C" int moe_decode_token(const float* logits, const void* x, int E, int k
   p.out = out;
   p.status = status;
   const size_t lds = ((size_t)d + (size_t)k * f) * 2;
+  if (mx) return E <= 256 ? launch_token_mx<4>(p, lds, stream) : launch_token_mx<16>(p, lds, stream);
   if (E <= 256) return launch_token_d<4>(p, lds, stream);
   return launch_token_d<16>(p, lds, stream);
 }

@@ -1,23 +1,29 @@
 """One routed-MoE layer forward as a sequence of library calls on caller-owned buffers.
 
 route + permute (one launch for small T) -> expert FFN -> combine, each a libmoecache.so
-entry point; a single token with bf16 weights takes moe_decode_token instead, which does all
-of it in one launch (same result, bit for bit, with fp32 expert outputs).
+entry point; a single token takes moe_decode_token instead where it applies, which does all
+of it in one launch.
 Device memory comes from torch; this class only allocates the intermediate
 buffers once and forwards pointers.
 """
 import torch
 
-from . import (MOE_F32, MOE_BF16, MOE_PATH_AUTO, moe_route, moe_permute, moe_route_permute,
+from . import (MOE_F32, MOE_BF16, MOE_MXFP4, MOE_PATH_AUTO, moe_route, moe_permute, moe_route_permute,
                moe_permute_workspace_bytes, moe_expert_ffn, moe_expert_ffn_workspace_bytes,
                moe_combine, moe_decode_token, moe_decode_token_workspace_bytes)
 
 
 def decode_token_supported(T, k, d, f, dtype, w_dtype, y_dtype):
-    """Shapes and types moe_decode_token takes (one token, bf16 activations and weights, fp32
-    expert outputs, x and h within 64 KB of LDS)."""
-    return (T == 1 and dtype == MOE_BF16 and w_dtype == MOE_BF16 and y_dtype == MOE_F32
-            and d <= 8192 and f <= 8192 and (d + k * f) * 2 <= 65536)
+    """Shapes and types moe_decode_token takes (one token, bf16 activations, bf16 or MXFP4
+    weights, fp32 expert outputs, x and h within 64 KB of LDS; MXFP4 strips held whole in
+    registers: d <= 4096, f <= 2048, k <= 8)."""
+    if T != 1 or dtype != MOE_BF16 or y_dtype != MOE_F32:
+        return False
+    if d > 8192 or f > 8192 or (d + k * f) * 2 > 65536:
+        return False
+    if w_dtype == MOE_MXFP4:
+        return d <= 4096 and f <= 2048 and k <= 8
+    return w_dtype == MOE_BF16
 
 
 def _tdtype(code):

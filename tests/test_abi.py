@@ -202,7 +202,11 @@ def test_decode_token_arguments_are_checked_on_the_host():
     assert call(E=1025) == moe.MOE_EINVAL
     assert call(d=100) == moe.MOE_EINVAL
     assert call(f=96) == moe.MOE_EINVAL
-    assert call(wdt=moe.MOE_MXFP4) == moe.MOE_EUNSUPPORTED
+    mx = moe.moe_entry_bytes(4096, 2048, moe.MOE_MXFP4)
+    assert call(wdt=moe.MOE_MXFP4, f=2560, stride=mx * 2) == moe.MOE_EUNSUPPORTED  # f > 2048
+    assert call(wdt=moe.MOE_MXFP4, d=4160, f=1024, stride=mx * 2) == moe.MOE_EUNSUPPORTED
+    assert call(wdt=moe.MOE_MXFP4, k=9, f=1024, stride=mx) == moe.MOE_EUNSUPPORTED  # k > 8
+    assert call(wdt=moe.MOE_MXFP4, stride=mx - 16) == moe.MOE_EINVAL
     assert call(wdt=moe.MOE_F32) == moe.MOE_EUNSUPPORTED
     assert call(d=8256) == moe.MOE_EUNSUPPORTED
     assert call(f=8256, k=1) == moe.MOE_EUNSUPPORTED
