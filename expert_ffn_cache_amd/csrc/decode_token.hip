@@ -214,21 +214,27 @@ __device__ __forceinline__ void wait_and_stage_h(const TokArgs& p, uint16_t* hs,
   if (!stage_h<UPW>(p, hs, epoch) && threadIdx.x == 0) set_status(p.status, MOE_ETIMEOUT);
 }
 
-// Down rows of output channel o of the selected experts j0 .. j0 + JG - 1 into registers.
+// Entries of the selected experts j0 .. j0 + JG - 1 (nullptr past k or for a missing
+// entry), in scalar registers.  The same pointers decide both which rows are loaded and
+// which are multiplied, so no load is left pending on a path that skips its use.
+template <int JG>
+__device__ __forceinline__ void down_entries(const TokArgs& p, const char* const* ent, int j0,
+                                             const char* (&e)[JG]) {
+#pragma unroll
+  for (int jj = 0; jj < JG; ++jj) e[jj] = j0 + jj < p.k ? uniform_ptr(ent[j0 + jj]) : nullptr;
+}
+
+// Down rows of output channel o of those experts into registers.
 template <int NCHF, int JG>
-__device__ __forceinline__ void down_load(const TokArgs& p, const char* const* ent, int j0, int o,
+__device__ __forceinline__ void down_load(const TokArgs& p, const char* const (&e)[JG], int o,
                                           u32x4 (&wv)[JG][NCHF]) {
   const int nck = p.f >> 3;
 #pragma unroll
   for (int jj = 0; jj < JG; ++jj) {
-    const int j = j0 + jj;
-    if (j < p.k) {
-      const char* e = uniform_ptr(ent[j]);
-      if (e) {
-        const char* row = e + (2 * (size_t)p.f * p.d + (size_t)o * p.f) * 2;
+    if (e[jj]) {
+      const char* row = e[jj] + (2 * (size_t)p.f * p.d + (size_t)o * p.f) * 2;
 #pragma unroll
-        for (int i = 0; i < NCHF; ++i) wv[jj][i] = ldrow(row, chunk_off(i, nck));
-      }
+      for (int i = 0; i < NCHF; ++i) wv[jj][i] = ldrow(row, chunk_off(i, nck));
     }
   }
 }
@@ -236,13 +242,13 @@ __device__ __forceinline__ void down_load(const TokArgs& p, const char* const* e
 // acc after adding w_j * (h_j . W_down_j[o]) for those experts, j ascending.
 template <int NCHF, int JG>
 __device__ __forceinline__ float down_dot(const TokArgs& p, const uint16_t* hs,
-                                          const char* const* ent, const float* wj, int j0,
+                                          const char* const (&e)[JG], const float* wj, int j0,
                                           const u32x4 (&wv)[JG][NCHF], float acc) {
   const int f = p.f, nck = f >> 3;
 #pragma unroll
   for (int jj = 0; jj < JG; ++jj) {
-    const int j = j0 + jj;
-    if (j < p.k && ent[j]) {
+    if (e[jj]) {
+      const int j = j0 + jj;
       float s = 0.f;
 #pragma unroll
       for (int i = 0; i < NCHF; ++i) s = dot8(lds_chunk(hs + j * f, i, nck), wv[jj][i], s);
@@ -260,13 +266,16 @@ __device__ __forceinline__ void down_item(const TokArgs& p, uint16_t* hs, const 
                                           const float* wj, int b, bool staged, uint32_t epoch) {
   const int o = b * kTokDownCh + wave_id();
   u32x4 wv[JG][NCHF];
-  down_load<NCHF, JG>(p, ent, 0, o, wv);
+  const char* e[JG];
+  down_entries<JG>(p, ent, 0, e);
+  down_load<NCHF, JG>(p, e, o, wv);
   __builtin_amdgcn_sched_barrier(0);  // the loads stay ahead of what follows
   if (!staged) wait_and_stage_h<UPW>(p, hs, epoch);
-  float acc = down_dot<NCHF, JG>(p, hs, ent, wj, 0, wv, 0.f);
+  float acc = down_dot<NCHF, JG>(p, hs, e, wj, 0, wv, 0.f);
   for (int j0 = JG; j0 < p.k; j0 += JG) {
-    down_load<NCHF, JG>(p, ent, j0, o, wv);
-    acc = down_dot<NCHF, JG>(p, hs, ent, wj, j0, wv, acc);
+    down_entries<JG>(p, ent, j0, e);
+    down_load<NCHF, JG>(p, e, o, wv);
+    acc = down_dot<NCHF, JG>(p, hs, e, wj, j0, wv, acc);
   }
   if ((threadIdx.x & 63) == 0) p.out[o] = acc;
 }
@@ -279,15 +288,15 @@ struct TokShared {
   uint32_t epoch;
 };
 
-// Every workgroup's start: wave 0 reads the epoch word and routes the token (or takes the
-// given ids and weights) while waves 1..3 stage x in LDS (NCHD: 16-byte chunks per lane of a
-// row, d <= 512 * NCHD); then the k entries are looked up.  Returns this launch's epoch.
+// Every workgroup's start: wave 0 reads the epoch word, routes the token (or takes the given
+// ids and weights) and looks up the k entries, while waves 1..3 stage x in LDS (NCHD:
+// 16-byte chunks per lane of a row, d <= 512 * NCHD).  Returns this launch's epoch.
 template <int NPL, int NCHD>
 __device__ __forceinline__ uint32_t tok_prologue(const TokArgs& p, uint16_t* xs, TokShared& sh) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int k = p.k;
-  uint32_t epoch = 0;
   if (wave == 0) {
+    uint32_t epoch = 0;
     if (tid == 0) epoch = coh_load(p.epoch_word) + 1u;  // this launch's epoch
     if (p.logits) {
       unsigned long long key[NPL];
@@ -297,6 +306,22 @@ __device__ __forceinline__ uint32_t tok_prologue(const TokArgs& p, uint16_t* xs,
       sh.id[lane] = p.topk_ids[lane];
       sh.w[lane] = p.topk_w[lane];
     }
+    if (lane < k) {  // the wave reads back its own LDS writes in order
+      const int e = sh.id[lane];
+      const char* ent = nullptr;
+      if (e >= 0 && e < p.E) {
+        const int s = p.expert_slot ? p.expert_slot[e] : e;
+        if (s >= 0 && (!p.slot_key || p.slot_key[s] == p.key_base + e))
+          ent = p.arena + (size_t)s * p.stride;
+      }
+      if (!ent) set_status(p.status, MOE_ERANGE);
+      sh.ent[lane] = ent;
+      if (blockIdx.x == 0 && p.logits) {
+        if (p.topk_ids) p.topk_ids[lane] = e;
+        if (p.topk_w) p.topk_w[lane] = sh.w[lane];
+      }
+    }
+    if (tid == 0) sh.epoch = epoch;
   } else {
     // every load in flight before the first LDS write
     constexpr int XR = (NCHD * 64 + kTokThreads - 65) / (kTokThreads - 64);
@@ -311,23 +336,6 @@ __device__ __forceinline__ uint32_t tok_prologue(const TokArgs& p, uint16_t* xs,
     for (int r = 0; r < XR; ++r) {
       const int q = tid - 64 + r * (kTokThreads - 64);
       if (q < nck) *(u32x4*)&xs[q * 8] = xv[r];
-    }
-  }
-  if (tid == 0) sh.epoch = epoch;
-  __syncthreads();
-  if (tid < k) {
-    const int e = sh.id[tid];
-    const char* ent = nullptr;
-    if (e >= 0 && e < p.E) {
-      const int s = p.expert_slot ? p.expert_slot[e] : e;
-      if (s >= 0 && (!p.slot_key || p.slot_key[s] == p.key_base + e))
-        ent = p.arena + (size_t)s * p.stride;
-    }
-    if (!ent) set_status(p.status, MOE_ERANGE);
-    sh.ent[tid] = ent;
-    if (blockIdx.x == 0 && p.logits) {
-      if (p.topk_ids) p.topk_ids[tid] = e;
-      if (p.topk_w) p.topk_w[tid] = sh.w[tid];
     }
   }
   __syncthreads();
@@ -375,6 +383,42 @@ void decode_token(TokArgs p) {
 // once) and the partial sums meeting in LDS: the split and order of the weight-streaming
 // MXFP4 kernels for one token, so the results are theirs bit for bit.
 
+// Tile kt of a strip (NMAT matrices), loaded whatever kt and the lane, so that every load of
+// a present expert is issued and used on every path: a tile past the strip (kt >= nk) reads
+// the strip's last tile and a lane past a short last tile its row's first block (both in
+// bounds); such values are zeroed where they are used (mx_tile_use).
+template <int NMAT>
+__device__ __forceinline__ void mx_tile_any(MxTile<NMAT>& t, const uint8_t* const (&cb)[NMAT],
+                                            const uint8_t* const (&sb)[NMAT], int kt, int nk,
+                                            int krem, int lane) {
+  const int q = lane >> 4;
+  const int kc = min(kt, nk - 1);
+  const bool ok = kt < nk && (kc != nk - 1 || krem == 0 || q < krem);
+  const int l = ok ? lane : (lane & 15);
+#pragma unroll
+  for (int m = 0; m < NMAT; ++m) {
+    t.c[m] = ldg16_nt(cb[m] + (size_t)kc * 1024 + l * 16);
+    t.s[m] = ldg_u8(sb[m] + (size_t)kc * 64 + l);
+  }
+}
+
+// acc[m] += the token row x tile kt of matrix m, with the tile's missing blocks as zeros (a
+// tile past the strip adds exact zeros).  xk: the activations (x or h_j) of the strip's row.
+template <int NMAT>
+__device__ __forceinline__ void mx_tile_use(const MxTile<NMAT>& t, const uint16_t* xk, int kt,
+                                            int nk, int krem, int lane, f32x4 (&acc)[NMAT]) {
+  const int q = lane >> 4;
+  const int kc = min(kt, nk - 1);
+  const bool ok = kt < nk && (kc != nk - 1 || krem == 0 || q < krem);
+  MxTile<NMAT> u;
+#pragma unroll
+  for (int m = 0; m < NMAT; ++m) {
+    u.c[m] = ok ? t.c[m] : u32x4{0u, 0u, 0u, 0u};
+    u.s[m] = ok ? t.s[m] : 0u;
+  }
+  mx_tile_mma<NMAT>(u, xk + kc * 128 + (ok ? 32 * q : 0), acc);
+}
+
 // Gate/up item (a, rt): units 16 rt .. 16 rt + 15 of the a-th selected expert.  GT: tiles
 // per wave per matrix (d <= 512 * GT).
 template <int GT>
@@ -382,31 +426,21 @@ __device__ __forceinline__ void mx_gateup_item(const TokArgs& p, const uint16_t*
                                                const char* const* ent, int item, uint32_t epoch) {
   const int nbg = p.f / 16;
   const int a = item / nbg, rt = item - a * nbg;
-  const int lane = threadIdx.x & 63, ks = wave_id(), q = lane >> 4;
-  const int K = p.d, nk = (K + 127) >> 7, krem = (K & 127) >> 5, kshort = krem ? nk - 1 : -1;
+  const int lane = threadIdx.x & 63, ks = wave_id();
+  const int K = p.d, nk = (K + 127) >> 7, krem = (K & 127) >> 5;
   const uint8_t* W = (const uint8_t*)uniform_ptr(ent[a]);
   MxTile<2> t[GT];
+  f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
   if (W) {
     const size_t fd = (size_t)p.f * K;
     const uint8_t* const cb[2] = {W + (size_t)rt * 8 * K, W + fd / 2 + (size_t)rt * 8 * K};
     const uint8_t* const sb[2] = {W + 3 * fd / 2 + (size_t)rt * (K / 2),
                                   W + 3 * fd / 2 + fd / 32 + (size_t)rt * (K / 2)};
 #pragma unroll
-    for (int r = 0; r < GT; ++r) {
-      const int kt = ks + 4 * r;
-      if (kt < nk) mx_load_tile<2>(t[r], cb, sb, kt, lane, kt != kshort || q < krem);
-    }
-  }
-  f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-  if (W) {
+    for (int r = 0; r < GT; ++r) mx_tile_any<2>(t[r], cb, sb, ks + 4 * r, nk, krem, lane);
+    __builtin_amdgcn_sched_barrier(0);  // the loads stay ahead of what follows
 #pragma unroll
-    for (int r = 0; r < GT; ++r) {
-      const int kt = ks + 4 * r;
-      if (kt < nk) {
-        const bool ok = kt != kshort || q < krem;
-        mx_tile_mma<2>(t[r], xs + kt * 128 + (ok ? 32 * q : 0), acc);
-      }
-    }
+    for (int r = 0; r < GT; ++r) mx_tile_use<2>(t[r], xs, ks + 4 * r, nk, krem, lane, acc);
   }
   mx_reduce<2, 4>(acc, 0, ks, lane);
   // lane l < 16 of wave 0 holds the token's row of unit 16 rt + l
@@ -424,21 +458,19 @@ template <int DT, int KMAX>
 __device__ __forceinline__ void mx_down_item(const TokArgs& p, uint16_t* hs,
                                              const char* const* ent, const float* wj, int rt,
                                              bool staged, uint32_t epoch) {
-  const int lane = threadIdx.x & 63, ks = wave_id(), q = lane >> 4;
-  const int K = p.f, nk = (K + 127) >> 7, krem = (K & 127) >> 5, kshort = krem ? nk - 1 : -1;
+  const int lane = threadIdx.x & 63, ks = wave_id();
+  const int K = p.f, nk = (K + 127) >> 7, krem = (K & 127) >> 5;
   const size_t fd = (size_t)K * p.d;
+  const uint8_t* W[KMAX];  // one pointer decides both loading and multiplying an expert
   MxTile<1> t[KMAX][DT];
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) {
-    const uint8_t* W = j < p.k ? (const uint8_t*)uniform_ptr(ent[j]) : nullptr;
-    if (W) {
-      const uint8_t* const cb[1] = {W + fd + (size_t)rt * 8 * K};
-      const uint8_t* const sb[1] = {W + 3 * fd / 2 + 2 * (fd / 32) + (size_t)rt * (K / 2)};
+    W[j] = j < p.k ? (const uint8_t*)uniform_ptr(ent[j]) : nullptr;
+    if (W[j]) {
+      const uint8_t* const cb[1] = {W[j] + fd + (size_t)rt * 8 * K};
+      const uint8_t* const sb[1] = {W[j] + 3 * fd / 2 + 2 * (fd / 32) + (size_t)rt * (K / 2)};
 #pragma unroll
-      for (int r = 0; r < DT; ++r) {
-        const int kt = ks + 4 * r;
-        if (kt < nk) mx_load_tile<1>(t[j][r], cb, sb, kt, lane, kt != kshort || q < krem);
-      }
+      for (int r = 0; r < DT; ++r) mx_tile_any<1>(t[j][r], cb, sb, ks + 4 * r, nk, krem, lane);
     }
   }
   __builtin_amdgcn_sched_barrier(0);  // the loads stay ahead of what follows
@@ -447,20 +479,13 @@ __device__ __forceinline__ void mx_down_item(const TokArgs& p, uint16_t* hs,
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) {
     if (j < p.k) {
-      const bool have = ent[j] != nullptr;
       f32x4 acc[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
-      if (have) {
+      if (W[j]) {
 #pragma unroll
-        for (int r = 0; r < DT; ++r) {
-          const int kt = ks + 4 * r;
-          if (kt < nk) {
-            const bool ok = kt != kshort || q < krem;
-            mx_tile_mma<1>(t[j][r], hs + j * K + kt * 128 + (ok ? 32 * q : 0), acc);
-          }
-        }
+        for (int r = 0; r < DT; ++r) mx_tile_use<1>(t[j][r], hs + j * K, ks + 4 * r, nk, krem, lane, acc);
       }
       mx_reduce<1, 4>(acc, 0, ks, lane);
-      if (have) o = fmaf(wj[j], acc[0][0], o);
+      if (W[j]) o = fmaf(wj[j], acc[0][0], o);
       __syncthreads();  // the partial sums are read before the next expert's are stored
     }
   }

@@ -7,11 +7,11 @@
 //
 // Each lane holds ceil(E/64) logits in registers (lane l owns experts l, l+64, ...).  Each
 // of the k rounds is a wave-wide max over a 64-bit key (order-preserving logit bits, then the
-// complemented expert id so that ties go to the lower id), taken as two 32-bit maxima (the
-// high word, then the low word among the lanes that hold that high word) with DPP moves and
+// complemented expert id so that ties go to the lower id), taken as 32-bit maxima (the high
+// word, then, only when several lanes hold it, the low word among them) with DPP moves and
 // scalar read-outs, so a round makes no LDS round trip; the owner lane retires the winner.
-// The softmax over the k winners is done in registers (lane j holds winner j) and written
-// coalesced.
+// The softmax over the k winners is summed in rank order as they come out; lane j writes
+// winner j.
 #pragma once
 
 #include "common.h"
@@ -46,37 +46,41 @@ __device__ __forceinline__ void route_keys(const float* __restrict__ row, int E,
 }
 
 // ids[j], w[j] (j < k) from a token's keys (consumed); also ids into ids2 when not null.
+// A round's winner is the largest high word; the low word (the complemented id) is reduced
+// over the wave only when several lanes hold that high word, so a round is usually one DPP
+// reduction.  The softmax denominator is summed in rank order as the winners come out.
 template <int NPL>
 __device__ __forceinline__ void route_pick(unsigned long long (&key)[NPL], int k,
                                            int32_t* __restrict__ ids, float* __restrict__ w,
                                            int32_t* ids2) {
   const int lane = threadIdx.x & 63;
-  float sel_v = 0.0f, top = 0.0f;
+  float top = 0.0f, sum = 0.0f, ex = 0.0f;
   int sel_id = 0;
   for (int r = 0; r < k; ++r) {
     unsigned long long mine = key[0];
 #pragma unroll
     for (int i = 1; i < NPL; ++i) mine = key[i] > mine ? key[i] : mine;
-    const uint32_t hi = wave_max_u32((uint32_t)(mine >> 32));
-    const uint32_t lo = wave_max_u32((uint32_t)(mine >> 32) == hi ? (uint32_t)mine : 0u);
-    const unsigned long long best = ((unsigned long long)hi << 32) | lo;
-    const int id = (int)(~(uint32_t)best);
-    const float v = from_order_bits((uint32_t)(best >> 32));
+    const uint32_t mhi = (uint32_t)(mine >> 32);
+    const uint32_t hi = wave_max_u32(mhi);
+    const unsigned long long at = __ballot(mhi == hi);
+    const uint32_t lo = __popcll(at) == 1
+                            ? __builtin_amdgcn_readlane((uint32_t)mine, __ffsll((long long)at) - 1)
+                            : wave_max_u32(mhi == hi ? (uint32_t)mine : 0u);
+    const int id = (int)(~lo);
+    const float v = from_order_bits(hi);
     if (r == 0) top = v;
+    const float e = expf(v - top);
+    sum += e;
     if (lane == (id & 63)) {
 #pragma unroll
       for (int i = 0; i < NPL; ++i)
         if (i == (id >> 6)) key[i] = 0ull;
     }
     if (lane == r) {
-      sel_v = v;
+      ex = e;
       sel_id = id;
     }
   }
-  const float ex = lane < k ? expf(sel_v - top) : 0.0f;
-  float sum = ex;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
   if (lane < k) {
     ids[lane] = sel_id;
     w[lane] = ex / sum;
