@@ -258,6 +258,18 @@ def bench_decode(args, torch, moe, T, alpha, arena, dtype=None):
         step_bytes=step_bytes, step_hbm_frac=step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS)
 
 
+def _sweep_entry(r):
+    """One decode-sweep record: single-layer graph replays, the same layers captured 16 to a
+    graph, and the dominant entry point (the expert FFN, or for one token the one-launch
+    layer) against the HBM roof."""
+    us16 = r["ms_per_layer_in_16_layer_graph"]
+    return dict(tok_s=r["tok_s"], us_per_layer=r["ms_per_step"] * 1e3,
+                tok_s_16_layer_graph=r["tok_s_16_layer_graph"],
+                us_per_layer_16_layer_graph=None if us16 is None else us16 * 1e3,
+                dominant=r["dominant"], ffn_us=r["ffn_ms"] * 1e3, unique_experts=r["U_mean"],
+                ffn_gbs=r["roofline"]["achieved"], hbm_frac=r["roofline"]["frac"])
+
+
 # ------------------------------------------------------------------------ prefill layer
 def bench_prefill(args, torch, moe, dtype=None):
     from gen import configs
@@ -734,10 +746,7 @@ def main():
             sweep = {}
             for T, alpha in ((1, 0.2), (64, 0.2), (8, 1.0), (64, 1.0), (128, 0.2), (128, 1.0)):
                 r = bench_decode(args, torch, moe, T, alpha, arena)
-                sweep[f"T{T}_alpha{alpha}"] = dict(
-                    tok_s=r["tok_s"], us_per_layer=r["ms_per_step"] * 1e3, ffn_us=r["ffn_ms"] * 1e3,
-                    unique_experts=r["U_mean"], ffn_gbs=r["roofline"]["achieved"],
-                    hbm_frac=r["roofline"]["frac"])
+                sweep[f"T{T}_alpha{alpha}"] = _sweep_entry(r)
                 log(f"[decode T={T} alpha={alpha}] {json.dumps(sweep[f'T{T}_alpha{alpha}'])}")
             extra["decode_sweep"] = sweep
         del arena
@@ -748,10 +757,7 @@ def main():
             mx = {}
             for T, alpha in ((8, 0.2), (1, 0.2), (64, 0.2), (8, 1.0), (64, 1.0)):
                 r = bench_decode(args, torch, moe, T, alpha, arena, gen.MXFP4)
-                mx[f"T{T}_alpha{alpha}"] = dict(
-                    tok_s=r["tok_s"], us_per_layer=r["ms_per_step"] * 1e3, ffn_us=r["ffn_ms"] * 1e3,
-                    unique_experts=r["U_mean"], ffn_gbs=r["roofline"]["achieved"],
-                    hbm_frac=r["roofline"]["frac"])
+                mx[f"T{T}_alpha{alpha}"] = _sweep_entry(r)
                 log(f"[decode mxfp4 T={T} alpha={alpha}] {json.dumps(mx[f'T{T}_alpha{alpha}'])}")
             extra["decode_mxfp4"] = mx
             del arena
