@@ -48,7 +48,7 @@ def _arena(arenas, w):
 # MXFP4 weights: the decode shape; rows shorter than a tile (K mod 128 = 64); one and eight
 # experts; E past 256
 SHAPES_MX = [(256, 6, 4096, 2048), (64, 6, 1024, 512), (37, 5, 320, 192), (300, 8, 2048, 1024),
-             (16, 1, 64, 2048), (130, 3, 4096, 64)]
+             (16, 1, 64, 2048), (130, 3, 4096, 64), (64, 8, 4096, 2048)]
 
 
 def _mx_split_is_four(k, d, f):
@@ -216,3 +216,34 @@ def test_many_calls_in_a_row_on_one_stream(arenas):
     for r, o in outs:
         assert torch.equal(o, refs[r])
     assert int(L.status.item()) == 0
+
+
+def test_one_launch_beside_a_long_launch_on_another_stream(arenas):
+    """The one-launch layer needs its workgroups resident together.  Started while a long
+    grouped GEMM (the T=8192 prefill FFN, milliseconds) holds the compute units from another
+    stream, its resident workgroups wait (bounded) until the GEMM's workgroups finish and the
+    rest of the grid is placed; the result is the same bits and no status is raised."""
+    E, k, d, f = 256, 6, 4096, 2048
+    w = _workload(E, k, d, f)
+    arena = _arena(arenas, w)
+    x = x_device(w, configs.gen_x(w))
+    lg = dev(configs.gen_logits(w, rotation=3))
+    L = MoeLayer(1, E, k, d, f)
+    ref = L.forward(x, lg, arena, w.entry_bytes).clone()
+    torch.cuda.synchronize()
+    # the prefill FFN on the same resident experts (weights of this workload), its own buffers
+    wp = configs.with_(configs.PREFILL, seed=w.seed)
+    P = MoeLayer(wp.T, E, k, d, f)
+    xp = x_device(wp, configs.gen_x(wp))
+    P.route_permute(dev(configs.gen_logits(wp)))
+    torch.cuda.synchronize()
+    side, main = torch.cuda.Stream(), torch.cuda.Stream()
+    for _ in range(3):
+        with torch.cuda.stream(side):
+            P.ffn(xp, arena, w.entry_bytes, stream=side)
+        with torch.cuda.stream(main):
+            L.out.zero_()
+            L.forward(x, lg, arena, w.entry_bytes, stream=main)
+        torch.cuda.synchronize()
+        assert torch.equal(L.out, ref)
+    assert int(L.status.item()) == 0 and int(P.status.item()) == 0
