@@ -15,7 +15,7 @@
 //           popcount of the lower lanes; the last lane of each id group
 //           advances the wave's running base.
 // When everything fits one chunk (decode), a single fused launch does it all; for a
-// handful of tokens moe_route_permute also folds the routing into that launch.
+// handful of tokens moe_route_permute routes and groups in one launch (route_group_tiny).
 #include "common.h"
 #include "route_dev.h"
 
@@ -26,7 +26,8 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kChunk = 1024;           // assignments per workgroup
 constexpr int kPerWave = kChunk / 4;   // 256 per wave, 4 steps of 64
-constexpr int kRoutePermuteMaxT = 16;  // tokens routed inside the fused launch (4 per wave)
+constexpr int kRoutePermuteMaxT = 16;  // tokens routed inside the fused launch (2 per wave)
+constexpr int kTinyThreads = 512;      // its workgroup: 8 waves
 
 __device__ __forceinline__ int id_bits(int E) {
   int b = 0;
@@ -223,31 +224,53 @@ __global__ __launch_bounds__(kThreads) void permute_rank(const int32_t* __restri
   permute_block<FUSED>(ids, A, E, ws, counts, offsets, perm, inv, status);
 }
 
-// Routing and grouping of a few tokens in one workgroup: wave w routes tokens w, w+4, ...
-// (route_dev.h; all of its logit rows are loaded before the first is ranked), keeping the
-// ids in LDS as well, then the workgroup groups the T*k assignments from LDS as
-// permute_rank<true> does from memory.
+// Routing and grouping of a few tokens (T <= 16, so T*k <= 256) in one workgroup of 8
+// waves: wave w routes tokens w and w + 8 (route_dev.h), keeping the ids in LDS as well;
+// then assignment a's position is its stable rank, the number of assignments b with
+// (id_b, b) < (id_a, a), and expert e's count and offset are the numbers of ids equal to and
+// below e, each counted straight from the ids in LDS (every wave reads the same id at once,
+// a broadcast).  With so few assignments this is shorter than the histogram, scan and
+// ballot ranking of permute_block, which pays barriers and shuffle chains whatever the size.
 template <int NPL>
-__global__ __launch_bounds__(kThreads) void route_permute_small(
+__global__ __launch_bounds__(kTinyThreads) void route_group_tiny(
     const float* __restrict__ logits, int T, int E, int k, int32_t* __restrict__ ids,
     float* __restrict__ w, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ perm, int32_t* __restrict__ inv, int32_t* status) {
-  constexpr int kTPW = kRoutePermuteMaxT / (kThreads / 64);  // tokens per wave
+    int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
   __shared__ int32_t s_ids[kRoutePermuteMaxT * kMaxK];
   const int wave = threadIdx.x >> 6;
-  unsigned long long key[kTPW][NPL];
+  unsigned long long key[2][NPL];
 #pragma unroll
-  for (int i = 0; i < kTPW; ++i) {
-    const int t = wave + 4 * i;
+  for (int i = 0; i < 2; ++i) {
+    const int t = wave + 8 * i;
     if (t < T) route_keys<NPL>(logits + (size_t)t * E, E, key[i]);
   }
 #pragma unroll
-  for (int i = 0; i < kTPW; ++i) {
-    const int t = wave + 4 * i;
+  for (int i = 0; i < 2; ++i) {
+    const int t = wave + 8 * i;
     if (t < T) route_pick<NPL>(key[i], k, ids + (size_t)t * k, w + (size_t)t * k, s_ids + t * k);
   }
   __syncthreads();
-  permute_block<true>(s_ids, T * k, E, nullptr, counts, offsets, perm, inv, status);
+  const int A = T * k;
+  for (int a = threadIdx.x; a < A; a += kTinyThreads) {
+    const int id = s_ids[a];
+    int r = 0;
+    for (int b = 0; b < A; ++b) {
+      const int ib = s_ids[b];
+      r += (ib < id) | ((ib == id) & (b < a));
+    }
+    perm[r] = a;
+    inv[a] = r;
+  }
+  for (int e = threadIdx.x; e <= E; e += kTinyThreads) {
+    int c = 0, below = 0;
+    for (int b = 0; b < A; ++b) {
+      const int ib = s_ids[b];
+      c += ib == e;
+      below += ib < e;
+    }
+    if (e < E) counts[e] = c;
+    offsets[e] = below;  // offsets[E] = A
+  }
 }
 
 }  // namespace
@@ -299,17 +322,17 @@ extern "C" int moe_route_permute(const float* logits, int T, int E, int k, int32
     return rc;
   }
   if (T > 0 && (!logits || !topk_ids || !topk_w || !perm || !inv)) return MOE_EINVAL;
-  const dim3 g(1), b(kThreads);
+  const dim3 g(1), b(kTinyThreads);
   if (E <= 64)
-    hipLaunchKernelGGL(route_permute_small<1>, g, b, 0, stream, logits, T, E, k, topk_ids, topk_w, counts, offsets, perm, inv, status);
+    hipLaunchKernelGGL(route_group_tiny<1>, g, b, 0, stream, logits, T, E, k, topk_ids, topk_w, counts, offsets, perm, inv);
   else if (E <= 128)
-    hipLaunchKernelGGL(route_permute_small<2>, g, b, 0, stream, logits, T, E, k, topk_ids, topk_w, counts, offsets, perm, inv, status);
+    hipLaunchKernelGGL(route_group_tiny<2>, g, b, 0, stream, logits, T, E, k, topk_ids, topk_w, counts, offsets, perm, inv);
   else if (E <= 256)
-    hipLaunchKernelGGL(route_permute_small<4>, g, b, 0, stream, logits, T, E, k, topk_ids, topk_w, counts, offsets, perm, inv, status);
+    hipLaunchKernelGGL(route_group_tiny<4>, g, b, 0, stream, logits, T, E, k, topk_ids, topk_w, counts, offsets, perm, inv);
   else if (E <= 512)
-    hipLaunchKernelGGL(route_permute_small<8>, g, b, 0, stream, logits, T, E, k, topk_ids, topk_w, counts, offsets, perm, inv, status);
+    hipLaunchKernelGGL(route_group_tiny<8>, g, b, 0, stream, logits, T, E, k, topk_ids, topk_w, counts, offsets, perm, inv);
   else
-    hipLaunchKernelGGL(route_permute_small<16>, g, b, 0, stream, logits, T, E, k, topk_ids, topk_w, counts, offsets, perm, inv, status);
+    hipLaunchKernelGGL(route_group_tiny<16>, g, b, 0, stream, logits, T, E, k, topk_ids, topk_w, counts, offsets, perm, inv);
   MOE_LAUNCH_CHECK();
   return MOE_OK;
 }
