@@ -220,3 +220,28 @@ def test_decode_token_arguments_are_checked_on_the_host():
     assert call(ws_bytes=hdr) == moe.MOE_EINVAL
     assert call(logits=None, ids=None) == moe.MOE_EINVAL
     assert call(logits=None, w=None) == moe.MOE_EINVAL
+
+
+def test_decode_token_supported_matches_the_library():
+    """The binding's shape test for the one-launch layer agrees with the library's host checks
+    over a grid of shapes and weight types: a call with no output pointer returns
+    MOE_EUNSUPPORTED exactly where the shape test says no, MOE_EINVAL (shape passed, missing
+    output) elsewhere; nothing is launched."""
+    from expert_ffn_cache_amd.layer import decode_token_supported
+    L = moe.lib()
+    A = 1 << 20  # stand-in address, never dereferenced
+    seen = {True: 0, False: 0}
+    for wdt in (moe.MOE_BF16, moe.MOE_MXFP4, moe.MOE_F32):
+        for k in (1, 6, 8, 9, 16):
+            for d in (64, 2048, 4096, 4160, 8192, 8256):
+                for f in (64, 1024, 2048, 2560, 4096, 8192):
+                    ok = decode_token_supported(1, k, d, f, moe.MOE_BF16, wdt, moe.MOE_F32)
+                    stride = ((max(moe.moe_entry_bytes(d, f, wdt), 16) + 15) // 16) * 16
+                    rc = L.moe_decode_token(A, A, 1024, k, d, f, None, A, stride, wdt, None, 0,
+                                            A, A, A, 1 << 30, None, None, None)
+                    assert rc == (moe.MOE_EINVAL if ok else moe.MOE_EUNSUPPORTED), (wdt, k, d, f)
+                    seen[ok] += 1
+    assert seen[True] > 20 and seen[False] > 20
+    assert not decode_token_supported(2, 6, 4096, 2048, moe.MOE_BF16, moe.MOE_BF16, moe.MOE_F32)
+    assert not decode_token_supported(1, 6, 4096, 2048, moe.MOE_F32, moe.MOE_BF16, moe.MOE_F32)
+    assert not decode_token_supported(1, 6, 4096, 2048, moe.MOE_BF16, moe.MOE_BF16, moe.MOE_BF16)

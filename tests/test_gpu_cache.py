@@ -570,3 +570,62 @@ def test_lru_split_and_resize_at_maximum_sizes():
         _compare_tables(dc, sim)
     assert evicted > 0
     assert int(dc.status.item()) == 0
+
+
+@pytest.mark.parametrize("dtype,graph,slots", [(gen.BF16, False, "table"), (gen.BF16, True, "lookup"),
+                                               (gen.MXFP4, True, "table")])
+def test_one_token_decode_through_cache_with_one_launch_layer(dtype, graph, slots):
+    """One token per step: route -> lookup -> device fill -> the one-launch layer on the
+    routed ids (grouping, FFN through key-checked slots, combine) for every layer, eager or
+    captured once and replayed with new logits.  Slots come from the layer's row of slot_of
+    or from the lookup's expert_slot.  Every layer's output equals the oracle and the
+    tables equal the sequential simulator's; 3 layers x 3 experts over 7 slots evict every
+    step."""
+    w = configs.Workload("lru_tok", seed=41, T=1, d=256, E=16, k=3, f=192, dtype=dtype, L=3,
+                         S=7, alpha=0.5)
+    pool = host_pool(w)
+    arena = torch.zeros((w.S, w.entry_elems), dtype=torch_dtype(w), device="cuda")
+    dc = DevCache(w.L, w.E, w.S, w.entry_bytes, arena, pool)
+    sim = LruSim(w.L, w.E, w.S)
+    layers = [MoeLayer(1, w.E, w.k, w.d, w.f, w_dtype=w.dtype) for _ in range(w.L)]
+    assert all(lay.fusable for lay in layers)
+    xs = [configs.gen_x(w, layer) for layer in range(w.L)]
+    xs_dev = [x_device(w, x) for x in xs]
+    tables = [oracle_table(w, range(w.E), layer) for layer in range(w.L)]
+    lg_buf = torch.zeros((w.L, 1, w.E), dtype=torch.float32, device="cuda")
+
+    def step_layers():
+        for layer, lay in enumerate(layers):
+            lay.route(lg_buf[layer])
+            dc.lookup(layer, lay.ids, 1, w.k)
+            moe.cache_fill_device(dc.desc, dc.fills, dc.n_fills, w.E)
+            es = dc.slot_of[layer * w.E:(layer + 1) * w.E] if slots == "table" else dc.expert_slot
+            lay.decode_token(xs_dev[layer], None, arena, w.entry_bytes, expert_slot=es,
+                             slot_key=dc.key_of, key_base=layer * w.E)
+
+    torch.cuda.synchronize()
+    if graph:
+        s = torch.cuda.Stream()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            step_layers()
+    for step in range(8):
+        lgs = [gen.routing_logits(w.seed, gen.TAG_LOGIT + layer * 0x10000 + step * 0x100, 1,
+                                  w.E, w.k) for layer in range(w.L)]
+        lg_buf.copy_(torch.from_numpy(np.stack(lgs)))
+        torch.cuda.synchronize()
+        if graph:
+            g.replay()
+        else:
+            step_layers()
+        torch.cuda.synchronize()
+        for layer, lay in enumerate(layers):
+            ids, _, ref = oracle.moe_layer(xs[layer], lgs[layer], w.k, tables[layer])
+            np.testing.assert_array_equal(lay.ids.cpu().numpy(), ids)
+            assert_close(lay.out.cpu().numpy().reshape(ref.shape), ref, bf16_tol(ref),
+                         f"step {step} layer {layer}")
+            sim.step(layer, ids.reshape(-1))
+            assert int(lay.status.item()) == 0, (step, layer)
+        _compare_tables(dc, sim)
+        assert int(dc.status.item()) == 0
+    assert sim.misses > w.L * w.k  # evictions happened after the cold start
