@@ -77,6 +77,48 @@ __device__ __forceinline__ void gu_mma(const GuStage<MC>& s, f32x4 (&ag)[MC], f3
   }
 }
 
+// One pass over up to 16 MC token rows m0.. of the expert (MC chunks of 16 rows).
+template <int MC>
+__device__ __forceinline__ void gu_pass(const FfnArgs& p, const uint16_t* pg, const uint16_t* pu,
+                                        int n0, int n, int m0, int i0, int col, int kg) {
+  const int d = p.d, nst = d >> 6;
+  const uint16_t* X = (const uint16_t*)p.x;
+  const uint16_t* px[MC];
+#pragma unroll
+  for (int mc = 0; mc < MC; ++mc) {
+    const int r = min(m0 + mc * 16 + col, n - 1);
+    px[mc] = X + (size_t)(p.perm[n0 + r] / p.k) * d + kg * 16;
+  }
+  const int live = (n - m0 + 15) >> 4;  // 16-row chunks with tokens
+  f32x4 ag[MC], au[MC];
+#pragma unroll
+  for (int mc = 0; mc < MC; ++mc) {
+    ag[mc] = f32x4{0.f, 0.f, 0.f, 0.f};
+    au[mc] = ag[mc];
+  }
+  GuStage<MC> s0, s1;
+  gu_load(s0, pg, pu, px, 0);
+  for (int st = 0; st < nst; st += 2) {
+    gu_load(s1, pg, pu, px, min(st + 1, nst - 1) * 64);
+    gu_mma(s0, ag, au, live);
+    gu_load(s0, pg, pu, px, min(st + 2, nst - 1) * 64);
+    if (st + 1 < nst) gu_mma(s1, ag, au, live);
+  }
+  // lane holds C[4*kg + i][col] of each 16x16 tile: token rows, unit columns
+  uint16_t* H = (uint16_t*)p.h;
+#pragma unroll
+  for (int mc = 0; mc < MC; ++mc) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = m0 + mc * 16 + kg * 4 + i;
+      if (m < n)
+        H[(size_t)(n0 + m) * p.f + i0 + col] = f32_to_bf16(silu(ag[mc][i]) * au[mc][i]);
+    }
+  }
+}
+
+// MC: 16-row chunks per pass at most; a pass with fewer rows left takes the 1- or 2-chunk
+// form, so no token fragment is loaded for a chunk without tokens.
 template <int MC>
 __global__ __launch_bounds__(256) void gemv_gateup(FfnArgs p) {
   const int nrb = p.f >> 6;
@@ -87,44 +129,13 @@ __global__ __launch_bounds__(256) void gemv_gateup(FfnArgs p) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, kg = lane >> 4;
   const int i0 = rb * 64 + wave * 16;
-  const int d = p.d, nst = d >> 6;
-  const uint16_t* pg = it.w + (size_t)(i0 + col) * d + kg * 16;
-  const uint16_t* pu = pg + (size_t)p.f * d;
-  const uint16_t* X = (const uint16_t*)p.x;
-  uint16_t* H = (uint16_t*)p.h;
-
+  const uint16_t* pg = it.w + (size_t)(i0 + col) * p.d + kg * 16;
+  const uint16_t* pu = pg + (size_t)p.f * p.d;
   for (int m0 = 0; m0 < n; m0 += 16 * MC) {
-    const uint16_t* px[MC];
-#pragma unroll
-    for (int mc = 0; mc < MC; ++mc) {
-      const int r = min(m0 + mc * 16 + col, n - 1);
-      px[mc] = X + (size_t)(p.perm[n0 + r] / p.k) * d + kg * 16;
-    }
-    const int live = (n - m0 + 15) >> 4;  // 16-row chunks with tokens
-    f32x4 ag[MC], au[MC];
-#pragma unroll
-    for (int mc = 0; mc < MC; ++mc) {
-      ag[mc] = f32x4{0.f, 0.f, 0.f, 0.f};
-      au[mc] = ag[mc];
-    }
-    GuStage<MC> s0, s1;
-    gu_load(s0, pg, pu, px, 0);
-    for (int st = 0; st < nst; st += 2) {
-      gu_load(s1, pg, pu, px, min(st + 1, nst - 1) * 64);
-      gu_mma(s0, ag, au, live);
-      gu_load(s0, pg, pu, px, min(st + 2, nst - 1) * 64);
-      if (st + 1 < nst) gu_mma(s1, ag, au, live);
-    }
-    // lane holds C[4*kg + i][col] of each 16x16 tile: token rows, unit columns
-#pragma unroll
-    for (int mc = 0; mc < MC; ++mc) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = m0 + mc * 16 + kg * 4 + i;
-        if (m < n)
-          H[(size_t)(n0 + m) * p.f + i0 + col] = f32_to_bf16(silu(ag[mc][i]) * au[mc][i]);
-      }
-    }
+    const int chunks = (n - m0 + 15) >> 4;
+    if (MC >= 4 && chunks > 2) gu_pass<(MC >= 4 ? 4 : 1)>(p, pg, pu, n0, n, m0, i0, col, kg);
+    else if (MC >= 2 && chunks == 2) gu_pass<(MC >= 2 ? 2 : 1)>(p, pg, pu, n0, n, m0, i0, col, kg);
+    else gu_pass<1>(p, pg, pu, n0, n, m0, i0, col, kg);
   }
 }
 
@@ -160,6 +171,43 @@ __device__ __forceinline__ void dn_mma(const DnStage<MC>& s, f32x4 (&acc)[MC], i
 }
 
 template <int MC, int YDT>
+__device__ __forceinline__ void dn_pass(const FfnArgs& p, const uint16_t* pw, int n0, int n,
+                                        int m0, int o0, int col, int kg) {
+  const int f = p.f, nst = f >> 6;
+  const uint16_t* H = (const uint16_t*)p.h;
+  const uint16_t* ph[MC];
+#pragma unroll
+  for (int mc = 0; mc < MC; ++mc) {
+    const int r = min(m0 + mc * 16 + col, n - 1);
+    ph[mc] = H + (size_t)(n0 + r) * f + kg * 16;
+  }
+  const int live = (n - m0 + 15) >> 4;
+  f32x4 acc[MC];
+#pragma unroll
+  for (int mc = 0; mc < MC; ++mc) acc[mc] = f32x4{0.f, 0.f, 0.f, 0.f};
+  DnStage<MC> s0, s1;
+  dn_load(s0, pw, ph, 0);
+  for (int st = 0; st < nst; st += 2) {
+    dn_load(s1, pw, ph, min(st + 1, nst - 1) * 64);
+    dn_mma(s0, acc, live);
+    dn_load(s0, pw, ph, min(st + 2, nst - 1) * 64);
+    if (st + 1 < nst) dn_mma(s1, acc, live);
+  }
+#pragma unroll
+  for (int mc = 0; mc < MC; ++mc) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = m0 + mc * 16 + kg * 4 + i;
+      if (m < n) {
+        const size_t o = (size_t)(n0 + m) * p.d + o0 + col;
+        if (YDT == MOE_F32) ((float*)p.y)[o] = acc[mc][i];
+        else ((uint16_t*)p.y)[o] = f32_to_bf16(acc[mc][i]);
+      }
+    }
+  }
+}
+
+template <int MC, int YDT>
 __global__ __launch_bounds__(256) void gemv_down(FfnArgs p) {
   const int nrb = p.d >> 6;
   const int a = blockIdx.x / nrb, rb = blockIdx.x - a * nrb;
@@ -169,41 +217,12 @@ __global__ __launch_bounds__(256) void gemv_down(FfnArgs p) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, kg = lane >> 4;
   const int o0 = rb * 64 + wave * 16;
-  const int f = p.f, nst = f >> 6;
-  const uint16_t* pw = it.w + 2 * (size_t)f * p.d + (size_t)(o0 + col) * f + kg * 16;
-  const uint16_t* H = (const uint16_t*)p.h;
-
+  const uint16_t* pw = it.w + 2 * (size_t)p.f * p.d + (size_t)(o0 + col) * p.f + kg * 16;
   for (int m0 = 0; m0 < n; m0 += 16 * MC) {
-    const uint16_t* ph[MC];
-#pragma unroll
-    for (int mc = 0; mc < MC; ++mc) {
-      const int r = min(m0 + mc * 16 + col, n - 1);
-      ph[mc] = H + (size_t)(n0 + r) * f + kg * 16;
-    }
-    const int live = (n - m0 + 15) >> 4;
-    f32x4 acc[MC];
-#pragma unroll
-    for (int mc = 0; mc < MC; ++mc) acc[mc] = f32x4{0.f, 0.f, 0.f, 0.f};
-    DnStage<MC> s0, s1;
-    dn_load(s0, pw, ph, 0);
-    for (int st = 0; st < nst; st += 2) {
-      dn_load(s1, pw, ph, min(st + 1, nst - 1) * 64);
-      dn_mma(s0, acc, live);
-      dn_load(s0, pw, ph, min(st + 2, nst - 1) * 64);
-      if (st + 1 < nst) dn_mma(s1, acc, live);
-    }
-#pragma unroll
-    for (int mc = 0; mc < MC; ++mc) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = m0 + mc * 16 + kg * 4 + i;
-        if (m < n) {
-          const size_t o = (size_t)(n0 + m) * p.d + o0 + col;
-          if (YDT == MOE_F32) ((float*)p.y)[o] = acc[mc][i];
-          else ((uint16_t*)p.y)[o] = f32_to_bf16(acc[mc][i]);
-        }
-      }
-    }
+    const int chunks = (n - m0 + 15) >> 4;
+    if (MC >= 4 && chunks > 2) dn_pass<(MC >= 4 ? 4 : 1), YDT>(p, pw, n0, n, m0, o0, col, kg);
+    else if (MC >= 2 && chunks == 2) dn_pass<(MC >= 2 ? 2 : 1), YDT>(p, pw, n0, n, m0, o0, col, kg);
+    else dn_pass<1, YDT>(p, pw, n0, n, m0, o0, col, kg);
   }
 }
 
