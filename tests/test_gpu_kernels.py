@@ -246,6 +246,51 @@ def test_ffn_decode_dot_and_mfma_split(T, E, k, d, f, ydt):
     assert_close(y, ref, bf16_tol(ref), f"y_perm T={T} E={E} d={d} f={f}")
 
 
+def _ids_with_counts(counts, T, k):
+    """ids [T][k] in which expert e is picked by exactly counts[e] tokens (k distinct experts
+    per token: the sorted pick list is dealt column by column, and no expert has T or more
+    rows, so no token gets one expert twice)."""
+    picks = np.repeat(np.arange(len(counts)), counts).astype(np.int32)
+    assert picks.size == T * k and max(counts) < T
+    ids = picks.reshape(k, T).T.copy()
+    assert all(len(set(r)) == k for r in ids.tolist())
+    return ids
+
+
+@pytest.mark.parametrize("T,counts", [
+    (130, [3, 5, 16, 17, 32, 33, 48, 64, 42, 0, 0, 0]),
+    (130, [3, 5, 16, 17, 33, 65, 97, 24, 0, 0, 0, 0]),
+    (30, [1, 4, 5, 16, 17, 0, 15, 2]),
+])
+@pytest.mark.parametrize("ydt", [moe.MOE_F32, moe.MOE_BF16])
+def test_ffn_gemv_row_counts_at_chunk_boundaries(T, counts, ydt):
+    """The MFMA weight-streaming kernels take 16, 32 or 64 token rows per pass (the fewest
+    16-row chunks a pass needs, up to the call's limit); experts with rows on both sides of
+    each boundary and with several passes (65, 97 rows) against the oracle; experts with up
+    to 4 rows take the dot-product kernels of the same call."""
+    k = 2
+    w = configs.Workload("gemv_rows", seed=29, T=T, d=512, E=len(counts), k=k, f=256,
+                         dtype=gen.BF16, alpha=0.0)
+    ids = _ids_with_counts(counts, T, k)
+    x = configs.gen_x(w)
+    counts_o, offsets, perm, inv = oracle.permute(ids, w.E)
+    np.testing.assert_array_equal(counts_o, counts)
+    arena = device_arena_all_experts(w)
+    nws = moe.moe_expert_ffn_workspace_bytes(T, k, w.f, w.act_dtype)
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+    ytd = torch.float32 if ydt == moe.MOE_F32 else torch.bfloat16
+    y = torch.full((T * k, w.d), float("nan"), dtype=ytd, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    moe.moe_expert_ffn(x_device(w, x), w.act_dtype, dev(perm), dev(offsets), T, k, w.E, w.d, w.f,
+                       None, arena, w.entry_bytes, w.dtype, None, None, 0, ws, nws, y, ydt,
+                       moe.MOE_PATH_GEMV, status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    table = oracle_table(w, sorted(set(ids.ravel().tolist())))
+    ref = oracle.expert_ffn(x, ids, table, perm)
+    assert_close(np_of(y), ref, bf16_tol(ref), f"y_perm T={T} counts={counts}")
+
+
 @pytest.mark.parametrize("ydt", [moe.MOE_F32, moe.MOE_BF16])
 def test_ffn_split_stale_slot_skips_only_that_expert(ydt):
     """Key-checked slots on the row-split path (T=48: more items than the looping launches'
