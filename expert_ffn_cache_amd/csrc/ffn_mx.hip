@@ -143,13 +143,87 @@ __device__ __forceinline__ void mx_stage(uint16_t* lds, const uint16_t* src, int
   __syncthreads();
 }
 
-// Gate/up: workgroup = 4/KS strips of 16 units of one expert.
-template <int KS>
-__global__ __launch_bounds__(256) void mx_gateup(FfnArgs p) {
+// One launch for both projections (up to kMxMaxRows tokens): gate/up workgroups come first
+// in the grid and publish h as 8-byte entries, units 2c and 2c + 1 of a row (bf16, low half
+// first) in the low word and kMxTag in the high word, each written with one device-coherent
+// single-copy-atomic store; a down workgroup reads its expert's entries device-coherently
+// and uses them once every one carries the tag.  The eight L2 caches are not coherent with
+// one another, and this keeps the exchange free of cache maintenance (see the single-token
+// launch, which exchanges h the same way).  The entries are zeroed by a small kernel before
+// the launch, so the tag is the same on every call.  Workgroups are dispatched in grid order,
+// so every gate/up workgroup has started before any down workgroup and none of them waits:
+// each wait ends.  It is bounded all the same (MOE_ETIMEOUT).
+constexpr uint32_t kMxTag = 1u;
+constexpr unsigned kMxSpinLimit = 1u << 18;  // polls of a row block of h (well over a second)
+
+__device__ __forceinline__ uint64_t mx_coh_load64(const uint64_t* a) {
+  return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void mx_coh_store64(uint64_t* a, uint64_t v) {
+  __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// nt rows of h (K units each, entries of rows row0 ..) into LDS at row stride K + 8, once
+// every entry carries the tag: each thread loads its entries (eight in flight) and writes the
+// values, and the workgroup repeats until no thread found an untagged one.
+__device__ __forceinline__ void mx_stage_ent(uint16_t* lds, const uint64_t* hent, int K, int nt,
+                                             int row0, int32_t* status) {
+  const int ne = K >> 1, n = nt * ne;
+  const uint64_t* src = hent + (size_t)row0 * ne;
+  uint32_t* dst = (uint32_t*)lds;
+  __syncthreads();  // the previous pass's readers are done
+  for (unsigned polls = 1;; ++polls) {
+    int stale = 0;
+    for (int c0 = 0; c0 < n; c0 += 8 * 256) {
+      uint64_t v[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) v[r] = mx_coh_load64(src + min(c0 + r * 256 + (int)threadIdx.x, n - 1));
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const int c = c0 + r * 256 + threadIdx.x;
+        if (c < n) {
+          const int t = c / ne, q = c - t * ne;
+          stale |= (uint32_t)(v[r] >> 32) != kMxTag;
+          dst[t * ((K + 8) >> 1) + q] = (uint32_t)v[r];
+        }
+      }
+    }
+    if (!__syncthreads_or(stale)) return;
+    if (polls >= kMxSpinLimit) {
+      if (threadIdx.x == 0) set_status(status, MOE_ETIMEOUT);
+      return;
+    }
+    __builtin_amdgcn_s_sleep(8);
+  }
+}
+
+// Partial sums of the KS waves of each strip through red ([3][NMAT][64] in LDS), as
+// mx_reduce does through its own array.
+template <int NMAT, int KS>
+__device__ __forceinline__ void mx_reduce_buf(f32x4 (&acc)[NMAT], int strip, int ks, int lane,
+                                              f32x4* red) {
+  if (KS == 1) return;
+  if (ks > 0) {
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m) red[((strip * (KS - 1) + ks - 1) * NMAT + m) * 64 + lane] = acc[m];
+  }
+  __syncthreads();
+  if (ks == 0) {
+#pragma unroll
+    for (int j = 1; j < KS; ++j)
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m) acc[m] += red[((strip * (KS - 1) + j - 1) * NMAT + m) * 64 + lane];
+  }
+}
+
+// Gate/up: workgroup = 4/KS strips of 16 units of one expert.  ENT: h as tagged entries,
+// partial sums through red.
+template <int KS, bool ENT>
+__device__ __forceinline__ void gu_body(const FfnArgs& p, int bid, f32x4* red) {
   extern __shared__ __attribute__((aligned(16))) uint16_t xs[];
   constexpr int TR = 4 / KS;
   const int nb = p.f / (16 * TR);
-  const int a = blockIdx.x / nb, sb0 = blockIdx.x - a * nb;
+  const int a = bid / nb, sb0 = bid - a * nb;
   const MxItem it = mx_item(p, a);
   if (it.e < 0 || !it.w) return;
   const int n0 = p.offsets[it.e], n = p.offsets[it.e + 1] - n0;
@@ -170,25 +244,38 @@ __global__ __launch_bounds__(256) void mx_gateup(FfnArgs p) {
     mx_stage(xs, (const uint16_t*)p.x, K, nt, [&](int t) { return p.perm[n0 + m0 + t] / p.k; });
     f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
     mx_ring_run<2, KS>(ring, cb, sb, xs + min(col, nt - 1) * (K + 8), ks, nk, krem, lane, acc);
-    mx_reduce<2, KS>(acc, strip, ks, lane);
+    if (ENT) mx_reduce_buf<2, KS>(acc, strip, ks, lane, red);
+    else mx_reduce<2, KS>(acc, strip, ks, lane);
     if (ks == 0) {
       // lane holds C[4 kg + i][col]: token rows 4 kg + i, unit 16 rt + col
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = 4 * kg + i;
-        if (t < nt) H[(size_t)(n0 + m0 + t) * p.f + 16 * rt + col] = f32_to_bf16(silu(acc[0][i]) * acc[1][i]);
+        const uint32_t hv = f32_to_bf16(silu(acc[0][i]) * acc[1][i]);
+        if (ENT) {
+          const uint32_t nv = (uint32_t)__shfl_xor((int)hv, 1);  // unit 16 rt + (col ^ 1)
+          if (t < nt && !(col & 1))
+            mx_coh_store64((uint64_t*)p.h + ((size_t)(n0 + m0 + t) * p.f + 16 * rt + col) / 2,
+                           (uint64_t)(hv | nv << 16) | (uint64_t)kMxTag << 32);
+        } else if (t < nt) {
+          H[(size_t)(n0 + m0 + t) * p.f + 16 * rt + col] = (uint16_t)hv;
+        }
       }
     }
   }
 }
 
-// Down: workgroup = 4/KS strips of 16 output channels of one expert.
-template <int KS, int YDT>
-__global__ __launch_bounds__(256) void mx_down(FfnArgs p) {
+template <int KS>
+__global__ __launch_bounds__(256) void mx_gateup(FfnArgs p) { gu_body<KS, false>(p, blockIdx.x, nullptr); }
+
+// Down: workgroup = 4/KS strips of 16 output channels of one expert.  ENT: h read from the
+// tagged entries, partial sums through red.
+template <int KS, int YDT, bool ENT>
+__device__ __forceinline__ void dn_body(const FfnArgs& p, int bid, f32x4* red) {
   extern __shared__ __attribute__((aligned(16))) uint16_t hs[];
   constexpr int TR = 4 / KS;
   const int nb = p.d / (16 * TR);
-  const int a = blockIdx.x / nb, sb0 = blockIdx.x - a * nb;
+  const int a = bid / nb, sb0 = bid - a * nb;
   const MxItem it = mx_item(p, a);
   if (it.e < 0 || !it.w) return;
   const int n0 = p.offsets[it.e], n = p.offsets[it.e + 1] - n0;
@@ -204,10 +291,12 @@ __global__ __launch_bounds__(256) void mx_down(FfnArgs p) {
     const int nt = min(kMxNTL, n - m0);
     MxTile<1> ring[kMxAhead];
     mx_ring_fill<1, KS>(ring, cb, sb, ks, nk, krem, lane);
-    mx_stage(hs, (const uint16_t*)p.h, K, nt, [&](int t) { return n0 + m0 + t; });
+    if (ENT) mx_stage_ent(hs, (const uint64_t*)p.h, K, nt, n0 + m0, p.status);
+    else mx_stage(hs, (const uint16_t*)p.h, K, nt, [&](int t) { return n0 + m0 + t; });
     f32x4 acc[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
     mx_ring_run<1, KS>(ring, cb, sb, hs + min(col, nt - 1) * (K + 8), ks, nk, krem, lane, acc);
-    mx_reduce<1, KS>(acc, strip, ks, lane);
+    if (ENT) mx_reduce_buf<1, KS>(acc, strip, ks, lane, red);
+    else mx_reduce<1, KS>(acc, strip, ks, lane);
     if (ks == 0) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -220,6 +309,23 @@ __global__ __launch_bounds__(256) void mx_down(FfnArgs p) {
       }
     }
   }
+}
+
+template <int KS, int YDT>
+__global__ __launch_bounds__(256) void mx_down(FfnArgs p) { dn_body<KS, YDT, false>(p, blockIdx.x, nullptr); }
+
+// Both projections in one grid: n_gu gate/up workgroups (one wave per strip), then the
+// down workgroups (KSD waves per strip).
+template <int KSD, int YDT>
+__global__ __launch_bounds__(256) void mx_ffn1(FfnArgs p, int n_gu) {
+  __shared__ f32x4 red[3 * 64];
+  if ((int)blockIdx.x < n_gu) gu_body<1, true>(p, blockIdx.x, red);
+  else dn_body<KSD, YDT, true>(p, blockIdx.x - n_gu, red);
+}
+
+__global__ __launch_bounds__(256) void mx_ent_clear(uint64_t* ent, long n) {
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long)gridDim.x * 256)
+    mx_coh_store64(ent + i, 0);
 }
 
 // Waves per strip: one (a wave streams whole strips, no partial sums) unless that leaves
@@ -251,6 +357,12 @@ void launch_dn_ks(const FfnArgs& p, int experts, hipStream_t stream) {
   }
 }
 
+template <int KSD>
+void launch_one(const FfnArgs& p, int y_dtype, dim3 grid, size_t lds, hipStream_t stream, int n_gu) {
+  if (y_dtype == MOE_F32) hipLaunchKernelGGL((mx_ffn1<KSD, MOE_F32>), grid, dim3(256), lds, stream, p, n_gu);
+  else hipLaunchKernelGGL((mx_ffn1<KSD, MOE_BF16>), grid, dim3(256), lds, stream, p, n_gu);
+}
+
 }  // namespace
 
 bool ffn_mx_supported(int d, int f) {
@@ -269,6 +381,31 @@ int launch_ffn_mx(const FfnArgs& p, int y_dtype, hipStream_t stream, int experts
   MOE_LAUNCH_CHECK();
   if (y_dtype == MOE_F32) launch_dn_ks<MOE_F32>(p, experts, stream);
   else launch_dn_ks<MOE_BF16>(p, experts, stream);
+  MOE_LAUNCH_CHECK();
+  return MOE_OK;
+}
+
+// One launch only where gate/up has a wave per strip (min(E, T k) * f >= 65536, e.g. from
+// T = 6 at top 6 and f = 2048): with fewer strips the split-strip bodies hold 3 workgroups
+// per CU and the clearing launch is not paid back (T = 2 and 4 at d = 4096, f = 2048: 3%
+// slower), so those calls take the two launches.
+int launch_ffn_mx_one(const FfnArgs& p, int T, int y_dtype, hipStream_t stream, int experts) {
+  if (experts <= 0) return MOE_OK;
+  if (mx_ks(experts, p.f) != 1) return launch_ffn_mx(p, y_dtype, stream, experts);
+  const long n = (long)T * p.k * p.f / 2;  // h entries, one per two units of a row
+  hipLaunchKernelGGL(mx_ent_clear, dim3((unsigned)std::min<long>(1024, (n + 1023) / 1024)), dim3(256), 0,
+                     stream, (uint64_t*)p.h, n);
+  MOE_LAUNCH_CHECK();
+  const int ksd = mx_ks(experts, p.d);
+  const int n_gu = experts * (p.f / 64);
+  const int n_dn = experts * (p.d / (16 * (4 / ksd)));
+  const dim3 grid(n_gu + n_dn);
+  const size_t lds = (size_t)kMxNTL * (std::max(p.d, p.f) + 8) * 2;
+  switch (ksd) {
+    case 1: launch_one<1>(p, y_dtype, grid, lds, stream, n_gu); break;
+    case 2: launch_one<2>(p, y_dtype, grid, lds, stream, n_gu); break;
+    default: launch_one<4>(p, y_dtype, grid, lds, stream, n_gu); break;
+  }
   MOE_LAUNCH_CHECK();
   return MOE_OK;
 }

@@ -150,7 +150,9 @@ int moe_route_permute(const float* logits, int T, int E, int k, int32_t* topk_id
  * K/2*(r/16) + 64*(b/4) + 16*(b%4) + r%16. */
 size_t moe_entry_bytes(int d, int f, int w_dtype);
 
-/* Workspace bytes moe_expert_ffn needs (the SwiGLU intermediate, [T*k][f]). */
+/* Workspace bytes for moe_expert_ffn: the SwiGLU intermediate [T*k][f] (2 bytes per unit,
+ * 4 with MOE_F32 activations), and up to 16 tokens with MOE_BF16 activations 4 bytes per
+ * unit, room for the one-launch MXFP4 path (see moe_expert_ffn's ws). */
 size_t moe_expert_ffn_workspace_bytes(int T, int k, int f, int act_dtype);
 
 #define MOE_PATH_AUTO 0 /* chosen from T*k/E on the host: the grouped GEMM above 2 rows per \
@@ -179,7 +181,13 @@ size_t moe_expert_ffn_workspace_bytes(int T, int k, int f, int act_dtype);
  *  slot_key (nullable, device, [S]): when given, a slot whose key is not
  *  key_base + e, or a negative slot, sets *status = MOE_ERANGE and that
  *  expert's rows are not written (stale-cache detection).
- *  ws: at least moe_expert_ffn_workspace_bytes(T, k, f, act_dtype). */
+ *  ws: 16-byte aligned, at least T*k*f*2 bytes (4 with MOE_F32 activations), or
+ *  MOE_EINVAL.  With MOE_MXFP4 weights on the weight-streaming path, T <= 16,
+ *  min(E, T*k)*f >= 65536 and at least T*k*f*4 bytes (what
+ *  moe_expert_ffn_workspace_bytes returns there), both projections run in one launch that
+ *  exchanges h through tagged entries in ws (zeroed by a small kernel first); the results
+ *  are bit-identical to the two-launch form a smaller ws takes.  A bounded wait inside that
+ *  launch that gives up sets *status = MOE_ETIMEOUT (y_perm is then undefined). */
 int moe_expert_ffn(const void* x, int act_dtype, const int32_t* perm, const int32_t* offsets,
                    int T, int k, int E, int d, int f, const int32_t* expert_slot,
                    const void* arena, size_t entry_stride, int w_dtype,
@@ -193,8 +201,10 @@ int moe_expert_ffn(const void* x, int act_dtype, const int32_t* perm, const int3
  * moe_expert_ffn_noalloc_max_bytes() bytes (8 MiB) on each GPU, held from the library's load
  * until the process ends; nothing is allocated by the call (its first call on a device looks
  * up that device's array address once).  Every other argument, result and error is as for
- * moe_expert_ffn.  A call whose intermediate (moe_expert_ffn_workspace_bytes(T, k, f,
- * act_dtype)) exceeds the array returns MOE_ETOOBIG before anything is enqueued.  All calls on
+ * moe_expert_ffn, which it calls with the array as ws (so calls of up to 16 tokens whose
+ * tagged entries fit take the one-launch MXFP4 path).  A call whose intermediate (T*k*f*2
+ * bytes, 4 with MOE_F32 activations) exceeds the array returns MOE_ETOOBIG before anything
+ * is enqueued.  All calls on
  * one GPU share its array and each overwrites it: calls that may overlap in time on one GPU
  * (different streams, or different host threads) race and give undefined results; order them
  * on one stream.  No part of the array needs to start at zero. */

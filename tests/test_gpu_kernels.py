@@ -379,6 +379,89 @@ def test_ffn_mxfp4_gemm_parity(T, E, k, d, f, alpha, path, ydt):
     assert_close(y, ref, bf16_tol(ref), f"y_perm mxfp4 gemm T={T} d={d} f={f}")
 
 
+def _mx_ffn_call(w, x, perm, offsets, arena, ws, nws, ydt, slots=None, keys=None):
+    """One MXFP4 moe_expert_ffn call on the weight-streaming path with nws workspace bytes;
+    returns (y_perm as numpy, status)."""
+    ytd = torch.float32 if ydt == moe.MOE_F32 else torch.bfloat16
+    y = torch.full((w.T * w.k, w.d), float("nan"), dtype=ytd, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    moe.moe_expert_ffn(x_device(w, x), w.act_dtype, dev(perm), dev(offsets), w.T, w.k, w.E, w.d,
+                       w.f, slots, arena, w.entry_bytes, w.dtype, None, keys, 0, ws, nws, y, ydt,
+                       moe.MOE_PATH_AUTO, status)
+    torch.cuda.synchronize()
+    return np_of(y), int(status.item())
+
+
+@pytest.mark.parametrize("T,E,k,d,f,alpha", [
+    (8, 256, 6, 4096, 2048, 0.2),   # the decode layer: a wave per strip on both projections
+    (8, 256, 6, 4096, 2048, 1.0),
+    (8, 256, 6, 1024, 2048, 1.0),   # down strips split over 2 waves
+    (8, 256, 6, 320, 1472, 0.5),    # over 4 waves; short last tiles on both projections
+    (13, 256, 4, 1088, 1536, 0.5),  # experts with more than 4 rows: several staging passes
+    (16, 128, 8, 512, 2048, 1.0),
+    (2, 64, 6, 1024, 512, 0.5),     # too few gate/up strips: both calls take two launches
+    (1, 16, 6, 512, 256, 0.5)])
+@pytest.mark.parametrize("ydt", [moe.MOE_F32, moe.MOE_BF16])
+def test_ffn_mxfp4_one_launch_matches_two_launches(T, E, k, d, f, alpha, ydt):
+    """MXFP4 calls of up to 16 tokens whose workspace holds h as tagged entries run gate/up
+    and down in one launch when gate/up has a wave per strip (min(E, T*k)*f >= 65536); with
+    only the plain intermediate they take two launches.  Both give the same bits and equal the
+    oracle within the bf16 rule.  A second one-launch call on the same workspace with other
+    token rows (same routing) is checked too: the first call's entries carry the same tag, so
+    only the clearing before each launch keeps them out."""
+    w = configs.Workload("mx_one", seed=71 + T, T=T, d=d, E=E, k=k, f=f, dtype=gen.MXFP4,
+                         alpha=alpha)
+    lg = configs.gen_logits(w)
+    ids, _ = oracle.route(lg, w.k)
+    counts, offsets, perm, inv = oracle.permute(ids, w.E)
+    arena = device_arena_all_experts(w)
+    A = w.T * w.k
+    nws = moe.moe_expert_ffn_workspace_bytes(w.T, w.k, w.f, w.act_dtype)
+    assert nws >= A * w.f * 4
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+    table = oracle_table(w, sorted(set(ids.ravel().tolist())))
+    for call in range(2):
+        x = configs.gen_x(configs.with_(w, seed=w.seed + 1000 * call))
+        y1, st1 = _mx_ffn_call(w, x, perm, offsets, arena, ws, nws, ydt)
+        y2, st2 = _mx_ffn_call(w, x, perm, offsets, arena, ws, A * w.f * 2, ydt)
+        assert st1 == 0 and st2 == 0
+        assert np.array_equal(y1.view(np.uint8), y2.view(np.uint8)), f"call {call}"
+        ref = oracle.expert_ffn(x, ids, table, perm)
+        assert_close(y1, ref, bf16_tol(ref), f"one launch T={T} call {call}")
+    del arena
+
+
+@pytest.mark.parametrize("T", [8, 16])
+def test_ffn_mxfp4_one_launch_stale_slot_skips_only_that_expert(T):
+    """Key-checked slots on the one-launch path: a stale slot sets MOE_ERANGE and leaves that
+    expert's rows unwritten, and its down workgroups return without waiting for entries that
+    no gate/up workgroup writes; every other row equals the oracle."""
+    w = configs.Workload("mx_one_stale", seed=83 + T, T=T, d=1024, E=64, k=6, f=2048,
+                         dtype=gen.MXFP4, alpha=0.5)
+    x = configs.gen_x(w)
+    ids, _ = oracle.route(configs.gen_logits(w), w.k)
+    counts, offsets, perm, inv = oracle.permute(ids, w.E)
+    used = [e for e in range(w.E) if counts[e] > 0]
+    stale = {used[0], used[len(used) // 2]}
+    keys = np.arange(w.E, dtype=np.int32)
+    for e in stale:
+        keys[e] = -7
+    arena = device_arena_all_experts(w)
+    A = w.T * w.k
+    nws = moe.moe_expert_ffn_workspace_bytes(w.T, w.k, w.f, w.act_dtype)
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+    yv, st = _mx_ffn_call(w, x, perm, offsets, arena, ws, nws, moe.MOE_F32,
+                          slots=dev(np.arange(w.E, dtype=np.int32)), keys=dev(keys))
+    assert st == moe.MOE_ERANGE
+    bad = np.zeros(A, dtype=bool)
+    for e in stale:
+        bad[offsets[e]:offsets[e + 1]] = True
+    assert bad.any() and (~bad).any() and np.isnan(yv[bad]).all()
+    ref = oracle.expert_ffn(x, ids, oracle_table(w, sorted(set(ids.ravel().tolist()))), perm)
+    assert_close(yv[~bad], ref[~bad], bf16_tol(ref), "rows of the other experts")
+    del arena
+
+
 def test_ffn_gemm_wide_n_tiles():
     w = configs.Workload("gemm_wide", seed=22, T=400, d=384, E=6, k=2, f=448, dtype=gen.BF16,
                          alpha=1.0)

@@ -140,13 +140,16 @@ def test_prefill_layer_full_size_sampled_mxfp4():
     del arena
 
 
-@pytest.mark.parametrize("T,E,dtype", [(8, 32, gen.BF16), (24, 256, gen.BF16), (48, 256, gen.BF16),
-                                       (300, 32, gen.BF16), (8, 32, gen.MXFP4), (300, 32, gen.MXFP4)])
-def test_layer_is_deterministic_and_graph_replayable(T, E, dtype):
+@pytest.mark.parametrize("T,E,f,dtype", [(8, 32, 256, gen.BF16), (24, 256, 256, gen.BF16),
+                                         (48, 256, 256, gen.BF16), (300, 32, 256, gen.BF16),
+                                         (8, 32, 256, gen.MXFP4), (8, 64, 2048, gen.MXFP4),
+                                         (13, 64, 2048, gen.MXFP4), (300, 32, 256, gen.MXFP4)])
+def test_layer_is_deterministic_and_graph_replayable(T, E, f, dtype):
     """Two eager runs are bit-identical; a captured graph replayed on new logits matches eager
     on every replay (one-item and looping weight-streaming launches, grouped GEMM; bf16 and
-    MXFP4 experts)."""
-    w = configs.with_(configs.DECODE, T=T, E=E, d=512, f=256, dtype=dtype)
+    MXFP4 experts, at f = 2048 both MXFP4 projections in one launch after its clearing
+    kernel)."""
+    w = configs.with_(configs.DECODE, T=T, E=E, d=512, f=f, dtype=dtype)
     x = x_device(w, configs.gen_x(w))
     arena = device_arena_all_experts(w)
     L = MoeLayer(w.T, w.E, w.k, w.d, w.f, w_dtype=w.dtype)
@@ -201,11 +204,12 @@ def test_layer_random_shapes(T, E, k, d, f, alpha, dtype):
 
 
 @pytest.mark.parametrize("dtype", [gen.BF16, gen.MXFP4])
-@pytest.mark.parametrize("T", [1, 8, 16, 100, 200, 600])
+@pytest.mark.parametrize("T", [1, 8, 16, 100, 200, 600, 2100])
 def test_layer_at_maximum_experts_and_k(T, dtype):
     """The library's limits, E = 1024 experts and k = 16, through every path: one-launch
     routing (T <= 16), weight streaming, the row split, and the grouped GEMMs (bf16 above
-    2048 assignments, MXFP4 above 8192), against the oracle."""
+    2048 assignments, MXFP4 above 8192 on 64-row tiles and from 32768 on 256-row tiles,
+    whose weight strips here lie partly past f = 64 and d = 128), against the oracle."""
     _check_layer(T, 1024, 16, 128, 64, 0.5, dtype)
 
 
