@@ -58,6 +58,26 @@ def test_noalloc_ffn_equals_workspace_ffn_on_consecutive_calls(dtype):
         del arena
 
 
+def test_noalloc_ffn_one_launch_mxfp4_equals_workspace_ffn():
+    """MXFP4 decode calls whose tagged h entries fit the array (T=8 and then T=6, f=2048) run
+    both projections in one launch inside the array, as moe_expert_ffn does with a workspace
+    of moe_expert_ffn_workspace_bytes: the same bits, within the bf16 rule of the oracle."""
+    for T in (8, 6):
+        w = configs.Workload("noalloc_one", seed=91 + T, T=T, d=512, E=64, k=6, f=2048,
+                             dtype=gen.MXFP4, alpha=0.5)
+        assert min(w.E, w.T * w.k) * w.f >= 65536
+        assert w.T * w.k * w.f * 4 <= moe.moe_expert_ffn_noalloc_max_bytes()
+        x, lg = configs.gen_x(w), configs.gen_logits(w)
+        arena = device_arena_all_experts(w)
+        L, y_ws, y_na = _ffn_both_ways(w, x, lg, arena, moe.MOE_F32)
+        assert torch.equal(y_na, y_ws), T
+        ids, _ = oracle.route(lg, w.k)
+        counts, offsets, perm, inv = oracle.permute(ids, w.E)
+        ref = oracle.expert_ffn(x, ids, oracle_table(w, sorted(set(ids.ravel().tolist()))), perm)
+        assert_close(y_na.cpu().numpy(), ref, bf16_tol(ref), f"noalloc one launch T={T}")
+        del arena
+
+
 def test_noalloc_ffn_refuses_an_intermediate_beyond_its_array():
     """T*k*f past the fixed array: MOE_ETOOBIG before anything is enqueued (y untouched)."""
     w = configs.Workload("noalloc_big", seed=67, T=2048, d=256, E=16, k=4, f=1024,
