@@ -151,10 +151,10 @@ __device__ __forceinline__ void mx_stage(uint16_t* lds, const uint16_t* src, int
 // one another, and this keeps the exchange free of cache maintenance (see the single-token
 // launch, which exchanges h the same way).  The entries are zeroed by a small kernel before
 // the launch, so the tag is the same on every call.  Workgroups are dispatched in grid order,
-// so every gate/up workgroup has started before any down workgroup and none of them waits:
-// each wait ends.  It is bounded all the same (MOE_ETIMEOUT).
+// so every gate/up workgroup is dispatched before any down workgroup, and gate/up workgroups
+// never wait: every wait ends.  It is bounded all the same (MOE_ETIMEOUT).
 constexpr uint32_t kMxTag = 1u;
-constexpr unsigned kMxSpinLimit = 1u << 18;  // polls of a row block of h (well over a second)
+constexpr unsigned kMxSpinLimit = 1u << 18;  // polls of a row block of h (about a second)
 
 __device__ __forceinline__ uint64_t mx_coh_load64(const uint64_t* a) {
   return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
