@@ -47,6 +47,11 @@ def test_workspace_sizes():
     assert moe.moe_permute_workspace_bytes(8192, 6, 256) % 256 == 0
     assert moe.moe_expert_ffn_workspace_bytes(8192, 6, 2048, moe.MOE_BF16) == 8192 * 6 * 2048 * 2
     assert moe.moe_expert_ffn_workspace_bytes(16, 2, 512, moe.MOE_F32) == 16 * 2 * 512 * 4
+    # up to 16 tokens with bf16 activations: room for h as tagged 8-byte entries (4 bytes per
+    # unit), which the one-launch MXFP4 path needs; above that the plain bf16 intermediate
+    assert moe.moe_expert_ffn_workspace_bytes(16, 6, 2048, moe.MOE_BF16) == 16 * 6 * 2048 * 4
+    assert moe.moe_expert_ffn_workspace_bytes(1, 6, 2048, moe.MOE_BF16) == 6 * 2048 * 4
+    assert moe.moe_expert_ffn_workspace_bytes(17, 6, 2048, moe.MOE_BF16) == 17 * 6 * 2048 * 2
 
 
 def _rc(fn, *args):
@@ -78,6 +83,14 @@ def test_host_validation_codes():
     short = list(args); short[11] = 100
     assert L.moe_expert_ffn(*short) == moe.MOE_EINVAL
     assert L.moe_expert_ffn(*args) == moe.MOE_EINVAL  # null buffers
+    # a workspace smaller than the plain intermediate (T*k*f bf16) is refused before any launch,
+    # whatever the weights (aligned stand-in addresses: nothing is dereferenced on this path)
+    for wdt, eb in ((moe.MOE_BF16, 3 * 4096 * 2048 * 2),
+                    (moe.MOE_MXFP4, moe.moe_entry_bytes(4096, 2048, moe.MOE_MXFP4))):
+        small = list(args); small[11] = eb; small[12] = wdt
+        small[0] = small[2] = small[3] = small[10] = small[16] = small[18] = 1 << 20
+        small[17] = 8 * 6 * 2048 * 2 - 1
+        assert L.moe_expert_ffn(*small) == moe.MOE_EINVAL
     # MXFP4 weights: bf16 activations only; entries at least moe_entry_bytes; both paths
     mx = list(args); mx[12] = moe.MOE_MXFP4; mx[11] = moe.moe_entry_bytes(4096, 2048, moe.MOE_MXFP4)
     mx_short = list(mx); mx_short[11] -= 16
