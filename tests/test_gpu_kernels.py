@@ -525,6 +525,24 @@ def test_ffn_zero_tokens_writes_nothing(path, dtype):
     assert int(status.item()) == 0 and torch.isnan(y).all()
 
 
+def test_ffn_mxfp4_one_launch_expert_mask_selects_experts():
+    """expert_mask on the one-launch MXFP4 path (T=8, f=2048: a wave per gate/up strip):
+    the flagged experts' rows equal the oracle, every other row is left as it was, and the
+    masked experts' down workgroups wait for nothing."""
+    w = configs.Workload("masked_one", seed=59, T=8, d=512, E=256, k=6, f=2048,
+                         dtype=gen.MXFP4, alpha=0.5)
+    assert min(w.E, w.T * w.k) * w.f >= 65536
+    mask = np.zeros(w.E, dtype=bool)
+    mask[np.random.default_rng(7).permutation(w.E)[: w.E // 3]] = True
+    y, ref, offsets = _ffn_masked(w, moe.MOE_PATH_AUTO, mask)
+    on = np.zeros(w.T * w.k, dtype=bool)
+    for e in np.flatnonzero(mask):
+        on[offsets[e]:offsets[e + 1]] = True
+    assert on.any() and (~on).any()
+    assert np.isnan(y[~on]).all()
+    assert_close(y[on], ref[on], bf16_tol(ref), "masked experts, one launch")
+
+
 @pytest.mark.parametrize("dtype", [gen.BF16, gen.MXFP4])
 @pytest.mark.parametrize("T,path", [(8, moe.MOE_PATH_GEMV), (48, moe.MOE_PATH_GEMV),
                                     (100, moe.MOE_PATH_GEMV), (300, moe.MOE_PATH_GEMM)])
