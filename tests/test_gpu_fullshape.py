@@ -164,18 +164,20 @@ def _tables_equal(dc, sim):
 
 
 @pytest.mark.timeout(1200)
-def test_lru_decode_real_shape_through_fills():
+@pytest.mark.parametrize("dtype", [gen.BF16, gen.MXFP4])
+def test_lru_decode_real_shape_through_fills(dtype):
     """The multi-layer decode workload at its real shape: 16 layers x 256 experts, top-6,
-    d=2048, f=1024, bf16, 1024 slots, batch 8, Markov routing (p=0.7) from the benchmark's
-    seed, and the real pinned pool (4096 entries, 51.5 GB, layer-major; the entries the eight
-    steps fill are generated, the others are never read).  Eight decode steps from a cold
+    d=2048, f=1024, bf16 or MXFP4 entries, 1024 slots, batch 8, Markov routing (p=0.7) from
+    the benchmark's seed, and the real pinned pool (4096 entries, 51.5 GB bf16 or 13.7 GB
+    MXFP4, layer-major; the entries the eight steps fill are generated, the others are never
+    read).  Eight decode steps from a cold
     cache, the last two with evictions.  Even steps run as the benchmark's host-driven loop
     (lookup, fill list read on the host, cache_fill on a copy stream while the FFN of the hits
     runs, then the FFN of the misses); odd steps as its graph loop (hit/miss masks on the
     device, cache_fill_device on a side stream while the FFN of the hits runs).  Every call:
     expert_slot and fill records equal LruSim's; every layer's output equals the oracle's;
     all tables equal the simulator's after every step."""
-    w = configs.LRU_DECODE
+    w = configs.with_(configs.LRU_DECODE, dtype=dtype)
     steps = 8
     ids_all, lg_all = gen.markov_routing(w.seed, steps, w.L, w.T, w.E, w.k, w.p_stay, w.zipf_s)
     sim = LruSim(w.L, w.E, w.S)
@@ -193,7 +195,7 @@ def test_lru_decode_real_shape_through_fills():
     dc = dict(slot_of=torch.empty(w.L * w.E, **i32), key_of=torch.empty(w.S, **i32),
               stamp=torch.empty(w.S, **i64), clock=torch.empty(1, **i64),
               stats=torch.empty(4, **i64), status=torch.zeros(1, **i32),
-              arena=torch.empty((w.S, w.entry_elems), dtype=torch.bfloat16, device="cuda"))
+              arena=torch.empty((w.S, w.entry_elems), dtype=torch_dtype(w), device="cuda"))
     desc = moe.moe_cache_t(w.L, w.E, w.S, w.L * w.E, w.entry_bytes,
                            *(dc[n].data_ptr() for n in ("slot_of", "key_of", "stamp", "clock",
                                                         "stats", "status", "arena")),
@@ -251,7 +253,10 @@ def test_lru_decode_real_shape_through_fills():
             used = sorted(set(ids.ravel().tolist()))
             for e in used:
                 if (l, e) not in weights:
-                    weights[(l, e)] = configs.gen_expert(w, l, e)
+                    m = configs.gen_expert(w, l, e)
+                    if w.dtype == gen.MXFP4:  # the exact dequantised weights
+                        m = tuple(oracle.mxfp4_dequant(c, sc).astype(np.float32) for c, sc in m)
+                    weights[(l, e)] = m
             table = oracle.ExpertTable(w.E, {e: weights[(l, e)] for e in used})
             _, _, ref = oracle.moe_layer(xs[l], lg_all[s, l], w.k, table)
             assert_close(lay.out.cpu().numpy(), ref, bf16_tol(ref), f"step {s} layer {l}")
