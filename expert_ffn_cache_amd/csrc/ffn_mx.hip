@@ -32,7 +32,15 @@
 namespace moe {
 namespace {
 
-constexpr int kMxNTL = 4;    // token rows staged per pass
+// Token rows staged per pass.  Each pass streams the expert's weights again, and an expert
+// has at most T rows; 4 rows (32.8 KB at d = 4096) keep 4 workgroups per CU.  Above 16 tokens
+// (where experts with more rows go to the grouped GEMM) this kernel's experts have up to 16
+// rows, and 6 rows per pass (49 KB, 3 workgroups per CU) pay for the lost workgroup: d = 4096,
+// f = 2048, top 6, FFN at Zipf 0.2: T = 32 270 -> 263 us, T = 64 421 -> 398 us; Zipf 1: T = 32
+// 193 -> 179 us, T = 64 217 -> 199 us.  Up to 16 tokens the fourth workgroup is worth more at
+// Zipf 0.2 (T = 12: 132 against 138 us, T = 16: 163 against 170), though not when skewed
+// (Zipf 1, T = 16: 119 against 97).  launch_ffn_mx_few takes those calls.
+constexpr int kMxNTL = 4, kMxNTLWide = 6;
 constexpr int kMxAhead = 4;  // tiles in flight per wave
 
 // One wave's share of a strip: tiles ks, ks + KS, ... of the nk tiles over K (the last
@@ -218,7 +226,7 @@ __device__ __forceinline__ void mx_reduce_buf(f32x4 (&acc)[NMAT], int strip, int
 
 // Gate/up: workgroup = 4/KS strips of 16 units of one expert.  ENT: h as tagged entries,
 // partial sums through red.
-template <int KS, bool ENT>
+template <int KS, bool ENT, int NTL>
 __device__ __forceinline__ void gu_body(const FfnArgs& p, int bid, f32x4* red) {
   extern __shared__ __attribute__((aligned(16))) uint16_t xs[];
   constexpr int TR = 4 / KS;
@@ -237,8 +245,8 @@ __device__ __forceinline__ void gu_body(const FfnArgs& p, int bid, f32x4* red) {
                                 W + 3 * fd / 2 + fd / 32 + (size_t)rt * (K / 2)};
   uint16_t* H = (uint16_t*)p.h;
   const int col = lane & 15, kg = lane >> 4;
-  for (int m0 = 0; m0 < n; m0 += kMxNTL) {
-    const int nt = min(kMxNTL, n - m0);
+  for (int m0 = 0; m0 < n; m0 += NTL) {
+    const int nt = min(NTL, n - m0);
     MxTile<2> ring[kMxAhead];
     mx_ring_fill<2, KS>(ring, cb, sb, ks, nk, krem, lane);
     mx_stage(xs, (const uint16_t*)p.x, K, nt, [&](int t) { return p.perm[n0 + m0 + t] / p.k; });
@@ -265,12 +273,12 @@ __device__ __forceinline__ void gu_body(const FfnArgs& p, int bid, f32x4* red) {
   }
 }
 
-template <int KS>
-__global__ __launch_bounds__(256) void mx_gateup(FfnArgs p) { gu_body<KS, false>(p, blockIdx.x, nullptr); }
+template <int KS, int NTL>
+__global__ __launch_bounds__(256) void mx_gateup(FfnArgs p) { gu_body<KS, false, NTL>(p, blockIdx.x, nullptr); }
 
 // Down: workgroup = 4/KS strips of 16 output channels of one expert.  ENT: h read from the
 // tagged entries, partial sums through red.
-template <int KS, int YDT, bool ENT>
+template <int KS, int YDT, bool ENT, int NTL>
 __device__ __forceinline__ void dn_body(const FfnArgs& p, int bid, f32x4* red) {
   extern __shared__ __attribute__((aligned(16))) uint16_t hs[];
   constexpr int TR = 4 / KS;
@@ -287,8 +295,8 @@ __device__ __forceinline__ void dn_body(const FfnArgs& p, int bid, f32x4* red) {
   const uint8_t* const cb[1] = {W + fd + (size_t)rt * 8 * K};
   const uint8_t* const sb[1] = {W + 3 * fd / 2 + 2 * (fd / 32) + (size_t)rt * (K / 2)};
   const int col = lane & 15, kg = lane >> 4;
-  for (int m0 = 0; m0 < n; m0 += kMxNTL) {
-    const int nt = min(kMxNTL, n - m0);
+  for (int m0 = 0; m0 < n; m0 += NTL) {
+    const int nt = min(NTL, n - m0);
     MxTile<1> ring[kMxAhead];
     mx_ring_fill<1, KS>(ring, cb, sb, ks, nk, krem, lane);
     if (ENT) mx_stage_ent(hs, (const uint64_t*)p.h, K, nt, n0 + m0, p.status);
@@ -311,16 +319,16 @@ __device__ __forceinline__ void dn_body(const FfnArgs& p, int bid, f32x4* red) {
   }
 }
 
-template <int KS, int YDT>
-__global__ __launch_bounds__(256) void mx_down(FfnArgs p) { dn_body<KS, YDT, false>(p, blockIdx.x, nullptr); }
+template <int KS, int YDT, int NTL>
+__global__ __launch_bounds__(256) void mx_down(FfnArgs p) { dn_body<KS, YDT, false, NTL>(p, blockIdx.x, nullptr); }
 
 // Both projections in one grid: n_gu gate/up workgroups (one wave per strip), then the
 // down workgroups (KSD waves per strip).
-template <int KSD, int YDT>
+template <int KSD, int YDT, int NTL>
 __global__ __launch_bounds__(256) void mx_ffn1(FfnArgs p, int n_gu) {
   __shared__ f32x4 red[3 * 64];
-  if ((int)blockIdx.x < n_gu) gu_body<1, true>(p, blockIdx.x, red);
-  else dn_body<KSD, YDT, true>(p, blockIdx.x - n_gu, red);
+  if ((int)blockIdx.x < n_gu) gu_body<1, true, NTL>(p, blockIdx.x, red);
+  else dn_body<KSD, YDT, true, NTL>(p, blockIdx.x - n_gu, red);
 }
 
 __global__ __launch_bounds__(256) void mx_ent_clear(uint64_t* ent, long n) {
@@ -336,31 +344,43 @@ int mx_ks(int experts, int R) {
   return strips / 4 >= 1024 ? 1 : strips / 2 >= 1024 ? 2 : 4;
 }
 
-template <int KS>
+template <int KS, int NTL>
 void launch_gu(const FfnArgs& p, int experts, hipStream_t stream) {
   const dim3 grid(experts * (p.f / (16 * (4 / KS))));
-  hipLaunchKernelGGL(mx_gateup<KS>, grid, dim3(256), (size_t)kMxNTL * (p.d + 8) * 2, stream, p);
+  hipLaunchKernelGGL((mx_gateup<KS, NTL>), grid, dim3(256), (size_t)NTL * (p.d + 8) * 2, stream, p);
 }
 
-template <int KS, int YDT>
+template <int KS, int YDT, int NTL>
 void launch_dn(const FfnArgs& p, int experts, hipStream_t stream) {
   const dim3 grid(experts * (p.d / (16 * (4 / KS))));
-  hipLaunchKernelGGL((mx_down<KS, YDT>), grid, dim3(256), (size_t)kMxNTL * (p.f + 8) * 2, stream, p);
+  hipLaunchKernelGGL((mx_down<KS, YDT, NTL>), grid, dim3(256), (size_t)NTL * (p.f + 8) * 2, stream, p);
 }
 
-template <int YDT>
+template <int YDT, int NTL>
 void launch_dn_ks(const FfnArgs& p, int experts, hipStream_t stream) {
   switch (mx_ks(experts, p.d)) {
-    case 1: launch_dn<1, YDT>(p, experts, stream); break;
-    case 2: launch_dn<2, YDT>(p, experts, stream); break;
-    default: launch_dn<4, YDT>(p, experts, stream); break;
+    case 1: launch_dn<1, YDT, NTL>(p, experts, stream); break;
+    case 2: launch_dn<2, YDT, NTL>(p, experts, stream); break;
+    default: launch_dn<4, YDT, NTL>(p, experts, stream); break;
   }
 }
 
-template <int KSD>
+template <int NTL>
+void launch_two(const FfnArgs& p, int y_dtype, hipStream_t stream, int experts) {
+  switch (mx_ks(experts, p.f)) {
+    case 1: launch_gu<1, NTL>(p, experts, stream); break;
+    case 2: launch_gu<2, NTL>(p, experts, stream); break;
+    default: launch_gu<4, NTL>(p, experts, stream); break;
+  }
+  if (hipPeekAtLastError() != hipSuccess) return;
+  if (y_dtype == MOE_F32) launch_dn_ks<MOE_F32, NTL>(p, experts, stream);
+  else launch_dn_ks<MOE_BF16, NTL>(p, experts, stream);
+}
+
+template <int KSD, int NTL>
 void launch_one(const FfnArgs& p, int y_dtype, dim3 grid, size_t lds, hipStream_t stream, int n_gu) {
-  if (y_dtype == MOE_F32) hipLaunchKernelGGL((mx_ffn1<KSD, MOE_F32>), grid, dim3(256), lds, stream, p, n_gu);
-  else hipLaunchKernelGGL((mx_ffn1<KSD, MOE_BF16>), grid, dim3(256), lds, stream, p, n_gu);
+  if (y_dtype == MOE_F32) hipLaunchKernelGGL((mx_ffn1<KSD, MOE_F32, NTL>), grid, dim3(256), lds, stream, p, n_gu);
+  else hipLaunchKernelGGL((mx_ffn1<KSD, MOE_BF16, NTL>), grid, dim3(256), lds, stream, p, n_gu);
 }
 
 }  // namespace
@@ -373,14 +393,19 @@ bool ffn_mx_supported(int d, int f) {
 
 int launch_ffn_mx(const FfnArgs& p, int y_dtype, hipStream_t stream, int experts) {
   if (experts <= 0) return MOE_OK;
-  switch (mx_ks(experts, p.f)) {
-    case 1: launch_gu<1>(p, experts, stream); break;
-    case 2: launch_gu<2>(p, experts, stream); break;
-    default: launch_gu<4>(p, experts, stream); break;
-  }
+  launch_two<kMxNTL>(p, y_dtype, stream, experts);
   MOE_LAUNCH_CHECK();
-  if (y_dtype == MOE_F32) launch_dn_ks<MOE_F32>(p, experts, stream);
-  else launch_dn_ks<MOE_BF16>(p, experts, stream);
+  return MOE_OK;
+}
+
+// The experts with at most 16 rows of a call above 16 tokens: 6 token rows per pass where
+// they fit the LDS, else 4.
+int launch_ffn_mx_few(const FfnArgs& p, int y_dtype, hipStream_t stream, int experts) {
+  if (experts <= 0) return MOE_OK;
+  if ((size_t)kMxNTLWide * (std::max(p.d, p.f) + 8) * 2 <= 65536)
+    launch_two<kMxNTLWide>(p, y_dtype, stream, experts);
+  else
+    launch_two<kMxNTL>(p, y_dtype, stream, experts);
   MOE_LAUNCH_CHECK();
   return MOE_OK;
 }
@@ -402,9 +427,9 @@ int launch_ffn_mx_one(const FfnArgs& p, int T, int y_dtype, hipStream_t stream, 
   const dim3 grid(n_gu + n_dn);
   const size_t lds = (size_t)kMxNTL * (std::max(p.d, p.f) + 8) * 2;
   switch (ksd) {
-    case 1: launch_one<1>(p, y_dtype, grid, lds, stream, n_gu); break;
-    case 2: launch_one<2>(p, y_dtype, grid, lds, stream, n_gu); break;
-    default: launch_one<4>(p, y_dtype, grid, lds, stream, n_gu); break;
+    case 1: launch_one<1, kMxNTL>(p, y_dtype, grid, lds, stream, n_gu); break;
+    case 2: launch_one<2, kMxNTL>(p, y_dtype, grid, lds, stream, n_gu); break;
+    default: launch_one<4, kMxNTL>(p, y_dtype, grid, lds, stream, n_gu); break;
   }
   MOE_LAUNCH_CHECK();
   return MOE_OK;

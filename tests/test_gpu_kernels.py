@@ -291,6 +291,41 @@ def test_ffn_gemv_row_counts_at_chunk_boundaries(T, counts, ydt):
     assert_close(np_of(y), ref, bf16_tol(ref), f"y_perm T={T} counts={counts}")
 
 
+
+@pytest.mark.parametrize("T,k,d,f,counts", [
+    (12, 4, 512, 4096, [1, 2, 3, 4, 5, 6, 7, 8, 11, 1, 0, 0, 0, 0, 0, 0]),  # 4 rows, one launch
+    (9, 2, 256, 128, [8, 6, 1, 2, 1, 0]),                                   # 4 rows, two launches
+    (40, 3, 320, 192, [1, 5, 6, 7, 11, 12, 13, 16, 17, 32, 0, 0]),          # 6 rows, + grouped GEMM
+    (24, 4, 512, 1024, [6, 12, 13, 16, 1, 7, 18, 23, 0, 0]),                 # 6 rows, + grouped GEMM
+])
+@pytest.mark.parametrize("ydt", [moe.MOE_F32, moe.MOE_BF16])
+def test_ffn_mxfp4_row_counts_at_pass_boundaries(T, k, d, f, counts, ydt):
+    """The MXFP4 weight-streaming kernels stage 4 token rows per pass up to 16 tokens (one
+    launch with h exchanged as tagged entries, or two launches) and 6 above (beside the
+    grouped GEMM, which takes the experts with more than 16 rows): experts with 1 to 16 rows,
+    on both sides of each pass boundary and with up to 3 passes, every row against the oracle
+    on the exactly dequantised weights."""
+    w = configs.Workload("mx_rows", seed=31, T=T, d=d, E=len(counts), k=k, f=f,
+                         dtype=gen.MXFP4, alpha=0.0)
+    ids = _ids_with_counts(counts, T, k)
+    x = configs.gen_x(w)
+    counts_o, offsets, perm, inv = oracle.permute(ids, w.E)
+    np.testing.assert_array_equal(counts_o, counts)
+    arena = device_arena_all_experts(w)
+    nws = moe.moe_expert_ffn_workspace_bytes(T, k, w.f, w.act_dtype)
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+    ytd = torch.float32 if ydt == moe.MOE_F32 else torch.bfloat16
+    y = torch.full((T * k, w.d), float("nan"), dtype=ytd, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    moe.moe_expert_ffn(x_device(w, x), w.act_dtype, dev(perm), dev(offsets), T, k, w.E, w.d, w.f,
+                       None, arena, w.entry_bytes, w.dtype, None, None, 0, ws, nws, y, ydt,
+                       moe.MOE_PATH_AUTO, status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    table = oracle_table(w, sorted(set(ids.ravel().tolist())))
+    ref = oracle.expert_ffn(x, ids, table, perm)
+    assert_close(np_of(y), ref, bf16_tol(ref), f"y_perm mxfp4 T={T} counts={counts}")
+
 @pytest.mark.parametrize("ydt", [moe.MOE_F32, moe.MOE_BF16])
 def test_ffn_split_stale_slot_skips_only_that_expert(ydt):
     """Key-checked slots on the row-split path (T=48: more items than the looping launches'
