@@ -28,8 +28,6 @@ namespace moe {
 // Both MXFP4 projections in one launch after a small clearing kernel (ffn_mx.hip); p.h is a
 // workspace of T*k*f/2 eight-byte entries (T * k * f * 4 bytes).
 int launch_ffn_mx_one(const FfnArgs& p, int T, int y_dtype, hipStream_t stream, int experts);
-// The MXFP4 weight-streaming kernels for the few-row experts of a call above 16 tokens.
-int launch_ffn_mx_few(const FfnArgs& p, int y_dtype, hipStream_t stream, int experts);
 }  // namespace moe
 
 namespace {
@@ -159,15 +157,15 @@ extern "C" int moe_expert_ffn(const void* x, int act_dtype, const int32_t* perm,
     // at Zipf 1 12% faster; bit-identical).
     if (T <= kMxMaxRows && ws_bytes >= (size_t)A * f * 4) return launch_ffn_mx_one(p, T, y_dtype, stream, experts);
     // An expert has at most T rows (a token picks it once).  The weight-streaming MXFP4
-    // kernels stage 4 or 6 token rows per pass and stream the expert's weights once per pass, so
-    // above kMxMaxRows rows an expert goes to the grouped GEMM, which streams them once per
-    // 64 rows and pays a fixed start-up per workgroup instead.  At most A / (kMxMaxRows + 1)
+    // kernels stream an expert's weights once for up to 16 rows (once per 16 rows beyond), so
+    // above kMxMaxRows rows an expert goes to the grouped GEMM, which streams them once per 64
+    // or 256 rows and pays a fixed start-up per workgroup instead.  At most A / (kMxMaxRows + 1)
     // experts have more rows.
     if (T <= kMxMaxRows) return launch_ffn_mx(p, y_dtype, stream, experts);
     FfnArgs few = p, many = p;
     few.nmax = kMxMaxRows;
     many.nmin = kMxMaxRows + 1;
-    int rc = launch_ffn_mx_few(few, y_dtype, stream, experts);
+    int rc = launch_ffn_mx(few, y_dtype, stream, experts);
     if (rc == MOE_OK) rc = launch_ffn_mx_gemm(many, T, y_dtype, stream, std::max(1, A / (kMxMaxRows + 1)));
     return rc;
   }

@@ -25,6 +25,7 @@
 // taking tiles ks, ks + KS, ...; their partial sums meet in LDS and the strip's first wave
 // writes the result.
 #include <algorithm>
+#include <type_traits>
 
 #include "ffn_args.h"
 #include "mx_dev.h"
@@ -32,33 +33,51 @@
 namespace moe {
 namespace {
 
-// Token rows staged per pass.  Each pass streams the expert's weights again, and an expert
-// has at most T rows; 4 rows (32.8 KB at d = 4096) keep 4 workgroups per CU.  Above 16 tokens
-// (where experts with more rows go to the grouped GEMM) this kernel's experts have up to 16
-// rows, and 6 rows per pass (49 KB, 3 workgroups per CU) pay for the lost workgroup: d = 4096,
-// f = 2048, top 6, FFN at Zipf 0.2: T = 32 270 -> 263 us, T = 64 421 -> 398 us; Zipf 1: T = 32
-// 193 -> 179 us, T = 64 217 -> 199 us.  Up to 16 tokens the fourth workgroup is worth more at
-// Zipf 0.2 (T = 12: 132 against 138 us, T = 16: 163 against 170), though not when skewed
-// (Zipf 1, T = 16: 119 against 97).  launch_ffn_mx_few takes those calls.
-constexpr int kMxNTL = 4, kMxNTLWide = 6;
+// An expert's token rows are staged in LDS in blocks over slices of the contraction: up to 4
+// rows over all of K, up to 8 over each half, up to 16 over each quarter (the same 33 KB at
+// K = 4096, so 4 workgroups per CU whatever the row count), the accumulators carrying over from
+// slice to slice.  An expert with up to 16 rows thus streams its weights once, and the
+// MFMA's 16 token columns do the work of 9-16 rows in one stream; with 4 rows per pass over all
+// of K it streamed them once per 4 rows.  Slices are whole tiles; fewer slices are taken where
+// the staged block would not fit 64 KB of LDS.
+__host__ __device__ constexpr int mx_slice_tiles(int nk, int C) { return (nk + C - 1) / C; }
+__host__ __device__ constexpr int mx_slice_stride(int K, int C) {  // LDS row stride (elements)
+  return C == 1 ? K + 8 : mx_slice_tiles((K + 127) >> 7, C) * 128 + 8;
+}
+__host__ __device__ constexpr int mx_block_elems(int K, int C) { return 4 * C * mx_slice_stride(K, C); }
+__host__ __device__ constexpr int mx_max_slices(int K) {
+  return mx_block_elems(K, 4) <= 32768 ? 4 : mx_block_elems(K, 2) <= 32768 ? 2 : 1;
+}
+// slices for an expert of n rows (4 rows per slice count), and the LDS a launch stages in
+__host__ __device__ constexpr int mx_slices(int n, int K) {
+  return n <= 4 ? 1 : n <= 8 && mx_max_slices(K) >= 2 ? 2 : mx_max_slices(K);
+}
+__host__ __device__ constexpr size_t mx_stage_bytes(int K) {
+  const int cm = mx_max_slices(K);
+  int e = mx_block_elems(K, 1);
+  if (cm >= 2 && mx_block_elems(K, 2) > e) e = mx_block_elems(K, 2);
+  if (cm >= 4 && mx_block_elems(K, 4) > e) e = mx_block_elems(K, 4);
+  return 2 * (size_t)e;
+}
 constexpr int kMxAhead = 4;  // tiles in flight per wave
 
-// One wave's share of a strip: tiles ks, ks + KS, ... of the nk tiles over K (the last
-// one short when krem = (K mod 128) / 32 > 0), kMxAhead of them in flight in `ring`.
-// mx_ring_fill issues the first loads (before the token rows are staged, so the two
-// overlap); mx_ring_run multiplies every tile and issues the rest.  xrow: start of the
-// lane's staged row; cb/sb: the strip's codes and scales.
+// One wave's share of a strip's tiles t0 .. t1 - 1 (one slice): tiles t0 + ks, t0 + ks + KS,
+// ... of the nk tiles over K (the last one short when krem = (K mod 128) / 32 > 0), kMxAhead
+// of them in flight in `ring`.  mx_ring_fill issues the first loads (before the token rows
+// are staged, so the two overlap); mx_ring_run multiplies every tile and issues the rest.
+// xrow: start of the lane's staged row (the slice's elements); cb/sb: the strip's codes and
+// scales.
 template <int NMAT, int KS>
 __device__ __forceinline__ void mx_ring_fill(MxTile<NMAT> (&ring)[kMxAhead],
                                              const uint8_t* const (&cb)[NMAT],
-                                             const uint8_t* const (&sb)[NMAT], int ks, int nk,
-                                             int krem, int lane) {
+                                             const uint8_t* const (&sb)[NMAT], int ks, int t0,
+                                             int t1, int nk, int krem, int lane) {
   const int q = lane >> 4;
-  const int ntw = nk > ks ? (nk - ks + KS - 1) / KS : 0;
+  const int ntw = t1 - t0 > ks ? (t1 - t0 - ks + KS - 1) / KS : 0;
   const int kshort = krem ? nk - 1 : -1;
 #pragma unroll
   for (int r = 0; r < kMxAhead; ++r) {
-    const int kt = ks + KS * r;
+    const int kt = t0 + ks + KS * r;
     if (r < ntw) mx_load_tile<NMAT>(ring[r], cb, sb, kt, lane, kt != kshort || q < krem);
   }
 }
@@ -67,18 +86,19 @@ template <int NMAT, int KS>
 __device__ __forceinline__ void mx_ring_run(MxTile<NMAT> (&ring)[kMxAhead],
                                             const uint8_t* const (&cb)[NMAT],
                                             const uint8_t* const (&sb)[NMAT], const uint16_t* xrow,
-                                            int ks, int nk, int krem, int lane, f32x4 (&acc)[NMAT]) {
+                                            int ks, int t0, int t1, int nk, int krem, int lane,
+                                            f32x4 (&acc)[NMAT]) {
   const int q = lane >> 4;
-  const int ntw = nk > ks ? (nk - ks + KS - 1) / KS : 0;  // tiles of this wave
-  const int kshort = krem ? nk - 1 : -1;                  // index of a short last tile
+  const int ntw = t1 - t0 > ks ? (t1 - t0 - ks + KS - 1) / KS : 0;  // tiles of this wave
+  const int kshort = krem ? nk - 1 : -1;                            // index of a short last tile
   for (int i = 0; i < ntw; i += kMxAhead) {
 #pragma unroll
     for (int r = 0; r < kMxAhead; ++r) {
       const int ii = i + r;
       if (ii < ntw) {
-        const int kt = ks + KS * ii;
+        const int kt = t0 + ks + KS * ii;
         const bool ok = kt != kshort || q < krem;
-        mx_tile_mma<NMAT>(ring[r], xrow + kt * 128 + (ok ? 32 * q : 0), acc);
+        mx_tile_mma<NMAT>(ring[r], xrow + (kt - t0) * 128 + (ok ? 32 * q : 0), acc);
         const int kn = kt + KS * kMxAhead;
         if (ii + kMxAhead < ntw) mx_load_tile<NMAT>(ring[r], cb, sb, kn, lane, kn != kshort || q < krem);
       }
@@ -137,16 +157,17 @@ __device__ __forceinline__ MxItem mx_item(const FfnArgs& p, int a) {
   return MxItem{s_e, (const uint8_t*)s_w};
 }
 
-// nt token rows of K bf16 into LDS at row stride K + 8 (the 16-byte pad spreads the rows
-// that one MFMA operand read touches over distinct banks).
+// Elements e0 .. e0 + len - 1 of nt token rows of K bf16 into LDS at row stride `stride`
+// (K + 8 or a slice's tiles + 8: the 16-byte pad spreads the rows that one MFMA operand read
+// touches over distinct banks).
 template <typename RowOf>
-__device__ __forceinline__ void mx_stage(uint16_t* lds, const uint16_t* src, int K, int nt,
-                                         RowOf src_row) {
-  const int nck = K >> 3;
-  __syncthreads();  // the previous pass's readers are done
+__device__ __forceinline__ void mx_stage(uint16_t* lds, const uint16_t* src, int K, int e0,
+                                         int len, int stride, int nt, RowOf src_row) {
+  const int nck = len >> 3;
+  __syncthreads();  // the previous slice's readers are done
   for (int c = threadIdx.x; c < nt * nck; c += blockDim.x) {
     const int t = c / nck, k8 = c - t * nck;
-    *(u32x4*)&lds[t * (K + 8) + k8 * 8] = ldg16(src + (size_t)src_row(t) * K + k8 * 8);
+    *(u32x4*)&lds[t * stride + k8 * 8] = ldg16(src + (size_t)src_row(t) * K + e0 + k8 * 8);
   }
   __syncthreads();
 }
@@ -171,28 +192,39 @@ __device__ __forceinline__ void mx_coh_store64(uint64_t* a, uint64_t v) {
   __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// nt rows of h (K units each, entries of rows row0 ..) into LDS at row stride K + 8, once
-// every entry carries the tag: each thread loads its entries (eight in flight) and writes the
-// values, and the workgroup repeats until no thread found an untagged one.
-__device__ __forceinline__ void mx_stage_ent(uint16_t* lds, const uint64_t* hent, int K, int nt,
-                                             int row0, int32_t* status) {
-  const int ne = K >> 1, n = nt * ne;
-  const uint64_t* src = hent + (size_t)row0 * ne;
+// Units e0 .. e0 + len - 1 of nt rows of h (K units each, entries of rows row0 ..) into LDS
+// at row stride `stride`, once every entry carries the tag: each thread loads its entries
+// (eight in flight) and writes the values, and the workgroup repeats until no thread found an
+// untagged one.
+template <bool WHOLE>
+__device__ __forceinline__ void mx_stage_ent(uint16_t* lds, const uint64_t* hent, int K, int e0,
+                                             int len, int stride, int nt, int row0,
+                                             int32_t* status) {
+  const int ne = K >> 1, nes = len >> 1, n = nt * nes;
+  const uint64_t* src = hent + (size_t)row0 * ne + (e0 >> 1);
   uint32_t* dst = (uint32_t*)lds;
-  __syncthreads();  // the previous pass's readers are done
+  __syncthreads();  // the previous slice's readers are done
   for (unsigned polls = 1;; ++polls) {
     int stale = 0;
     for (int c0 = 0; c0 < n; c0 += 8 * 256) {
       uint64_t v[8];
 #pragma unroll
-      for (int r = 0; r < 8; ++r) v[r] = mx_coh_load64(src + min(c0 + r * 256 + (int)threadIdx.x, n - 1));
+      for (int r = 0; r < 8; ++r) {
+        const int c = min(c0 + r * 256 + (int)threadIdx.x, n - 1);
+        if (WHOLE) {  // rows are contiguous
+          v[r] = mx_coh_load64(src + c);
+        } else {
+          const int t = c / nes;
+          v[r] = mx_coh_load64(src + (size_t)t * ne + (c - t * nes));
+        }
+      }
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
         const int c = c0 + r * 256 + threadIdx.x;
         if (c < n) {
-          const int t = c / ne, q = c - t * ne;
+          const int t = c / nes, q = c - t * nes;
           stale |= (uint32_t)(v[r] >> 32) != kMxTag;
-          dst[t * ((K + 8) >> 1) + q] = (uint32_t)v[r];
+          dst[t * (stride >> 1) + q] = (uint32_t)v[r];
         }
       }
     }
@@ -226,7 +258,7 @@ __device__ __forceinline__ void mx_reduce_buf(f32x4 (&acc)[NMAT], int strip, int
 
 // Gate/up: workgroup = 4/KS strips of 16 units of one expert.  ENT: h as tagged entries,
 // partial sums through red.
-template <int KS, bool ENT, int NTL>
+template <int KS, bool ENT>
 __device__ __forceinline__ void gu_body(const FfnArgs& p, int bid, f32x4* red) {
   extern __shared__ __attribute__((aligned(16))) uint16_t xs[];
   constexpr int TR = 4 / KS;
@@ -245,13 +277,29 @@ __device__ __forceinline__ void gu_body(const FfnArgs& p, int bid, f32x4* red) {
                                 W + 3 * fd / 2 + fd / 32 + (size_t)rt * (K / 2)};
   uint16_t* H = (uint16_t*)p.h;
   const int col = lane & 15, kg = lane >> 4;
-  for (int m0 = 0; m0 < n; m0 += NTL) {
-    const int nt = min(NTL, n - m0);
-    MxTile<2> ring[kMxAhead];
-    mx_ring_fill<2, KS>(ring, cb, sb, ks, nk, krem, lane);
-    mx_stage(xs, (const uint16_t*)p.x, K, nt, [&](int t) { return p.perm[n0 + m0 + t] / p.k; });
+  // blocks of up to 4 C rows, each over C slices of K (compiled per C, so one slice is the
+  // plain pass over all of K)
+  auto blocks = [&](auto c_tag) {
+  constexpr int C = decltype(c_tag)::value;
+  const int rb = 4 * C, tps = mx_slice_tiles(nk, C), stride = mx_slice_stride(K, C);
+  for (int m0 = 0; m0 < n; m0 += rb) {
+    const int nt = min(rb, n - m0);
+    auto row_of = [&](int t) { return p.perm[n0 + m0 + t] / p.k; };
     f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-    mx_ring_run<2, KS>(ring, cb, sb, xs + min(col, nt - 1) * (K + 8), ks, nk, krem, lane, acc);
+    if constexpr (C == 1) {
+      MxTile<2> ring[kMxAhead];
+      mx_ring_fill<2, KS>(ring, cb, sb, ks, 0, nk, nk, krem, lane);
+      mx_stage(xs, (const uint16_t*)p.x, K, 0, K, K + 8, nt, row_of);
+      mx_ring_run<2, KS>(ring, cb, sb, xs + min(col, nt - 1) * (K + 8), ks, 0, nk, nk, krem, lane, acc);
+    } else {
+      for (int t0 = 0; t0 < nk; t0 += tps) {
+        const int t1 = min(nk, t0 + tps), e0 = t0 * 128, len = min(K, t1 * 128) - e0;
+        MxTile<2> ring[kMxAhead];
+        mx_ring_fill<2, KS>(ring, cb, sb, ks, t0, t1, nk, krem, lane);
+        mx_stage(xs, (const uint16_t*)p.x, K, e0, len, stride, nt, row_of);
+        mx_ring_run<2, KS>(ring, cb, sb, xs + min(col, nt - 1) * stride, ks, t0, t1, nk, krem, lane, acc);
+      }
+    }
     if (ENT) mx_reduce_buf<2, KS>(acc, strip, ks, lane, red);
     else mx_reduce<2, KS>(acc, strip, ks, lane);
     if (ks == 0) {
@@ -271,14 +319,20 @@ __device__ __forceinline__ void gu_body(const FfnArgs& p, int bid, f32x4* red) {
       }
     }
   }
+  };
+  switch (mx_slices(n, K)) {
+    case 1: blocks(std::integral_constant<int, 1>{}); break;
+    case 2: blocks(std::integral_constant<int, 2>{}); break;
+    default: blocks(std::integral_constant<int, 4>{}); break;
+  }
 }
 
-template <int KS, int NTL>
-__global__ __launch_bounds__(256) void mx_gateup(FfnArgs p) { gu_body<KS, false, NTL>(p, blockIdx.x, nullptr); }
+template <int KS>
+__global__ __launch_bounds__(256) void mx_gateup(FfnArgs p) { gu_body<KS, false>(p, blockIdx.x, nullptr); }
 
 // Down: workgroup = 4/KS strips of 16 output channels of one expert.  ENT: h read from the
 // tagged entries, partial sums through red.
-template <int KS, int YDT, bool ENT, int NTL>
+template <int KS, int YDT, bool ENT>
 __device__ __forceinline__ void dn_body(const FfnArgs& p, int bid, f32x4* red) {
   extern __shared__ __attribute__((aligned(16))) uint16_t hs[];
   constexpr int TR = 4 / KS;
@@ -295,14 +349,29 @@ __device__ __forceinline__ void dn_body(const FfnArgs& p, int bid, f32x4* red) {
   const uint8_t* const cb[1] = {W + fd + (size_t)rt * 8 * K};
   const uint8_t* const sb[1] = {W + 3 * fd / 2 + 2 * (fd / 32) + (size_t)rt * (K / 2)};
   const int col = lane & 15, kg = lane >> 4;
-  for (int m0 = 0; m0 < n; m0 += NTL) {
-    const int nt = min(NTL, n - m0);
-    MxTile<1> ring[kMxAhead];
-    mx_ring_fill<1, KS>(ring, cb, sb, ks, nk, krem, lane);
-    if (ENT) mx_stage_ent(hs, (const uint64_t*)p.h, K, nt, n0 + m0, p.status);
-    else mx_stage(hs, (const uint16_t*)p.h, K, nt, [&](int t) { return n0 + m0 + t; });
+  auto blocks = [&](auto c_tag) {  // as in gate/up
+  constexpr int C = decltype(c_tag)::value;
+  const int rb = 4 * C, tps = mx_slice_tiles(nk, C), stride = mx_slice_stride(K, C);
+  for (int m0 = 0; m0 < n; m0 += rb) {
+    const int nt = min(rb, n - m0);
+    auto row_of = [&](int t) { return n0 + m0 + t; };
     f32x4 acc[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
-    mx_ring_run<1, KS>(ring, cb, sb, hs + min(col, nt - 1) * (K + 8), ks, nk, krem, lane, acc);
+    if constexpr (C == 1) {
+      MxTile<1> ring[kMxAhead];
+      mx_ring_fill<1, KS>(ring, cb, sb, ks, 0, nk, nk, krem, lane);
+      if (ENT) mx_stage_ent<true>(hs, (const uint64_t*)p.h, K, 0, K, K + 8, nt, n0 + m0, p.status);
+      else mx_stage(hs, (const uint16_t*)p.h, K, 0, K, K + 8, nt, row_of);
+      mx_ring_run<1, KS>(ring, cb, sb, hs + min(col, nt - 1) * (K + 8), ks, 0, nk, nk, krem, lane, acc);
+    } else {
+      for (int t0 = 0; t0 < nk; t0 += tps) {
+        const int t1 = min(nk, t0 + tps), e0 = t0 * 128, len = min(K, t1 * 128) - e0;
+        MxTile<1> ring[kMxAhead];
+        mx_ring_fill<1, KS>(ring, cb, sb, ks, t0, t1, nk, krem, lane);
+        if (ENT) mx_stage_ent<false>(hs, (const uint64_t*)p.h, K, e0, len, stride, nt, n0 + m0, p.status);
+        else mx_stage(hs, (const uint16_t*)p.h, K, e0, len, stride, nt, row_of);
+        mx_ring_run<1, KS>(ring, cb, sb, hs + min(col, nt - 1) * stride, ks, t0, t1, nk, krem, lane, acc);
+      }
+    }
     if (ENT) mx_reduce_buf<1, KS>(acc, strip, ks, lane, red);
     else mx_reduce<1, KS>(acc, strip, ks, lane);
     if (ks == 0) {
@@ -317,18 +386,24 @@ __device__ __forceinline__ void dn_body(const FfnArgs& p, int bid, f32x4* red) {
       }
     }
   }
+  };
+  switch (mx_slices(n, K)) {
+    case 1: blocks(std::integral_constant<int, 1>{}); break;
+    case 2: blocks(std::integral_constant<int, 2>{}); break;
+    default: blocks(std::integral_constant<int, 4>{}); break;
+  }
 }
 
-template <int KS, int YDT, int NTL>
-__global__ __launch_bounds__(256) void mx_down(FfnArgs p) { dn_body<KS, YDT, false, NTL>(p, blockIdx.x, nullptr); }
+template <int KS, int YDT>
+__global__ __launch_bounds__(256) void mx_down(FfnArgs p) { dn_body<KS, YDT, false>(p, blockIdx.x, nullptr); }
 
 // Both projections in one grid: n_gu gate/up workgroups (one wave per strip), then the
 // down workgroups (KSD waves per strip).
-template <int KSD, int YDT, int NTL>
+template <int KSD, int YDT>
 __global__ __launch_bounds__(256) void mx_ffn1(FfnArgs p, int n_gu) {
   __shared__ f32x4 red[3 * 64];
-  if ((int)blockIdx.x < n_gu) gu_body<1, true, NTL>(p, blockIdx.x, red);
-  else dn_body<KSD, YDT, true, NTL>(p, blockIdx.x - n_gu, red);
+  if ((int)blockIdx.x < n_gu) gu_body<1, true>(p, blockIdx.x, red);
+  else dn_body<KSD, YDT, true>(p, blockIdx.x - n_gu, red);
 }
 
 __global__ __launch_bounds__(256) void mx_ent_clear(uint64_t* ent, long n) {
@@ -344,43 +419,31 @@ int mx_ks(int experts, int R) {
   return strips / 4 >= 1024 ? 1 : strips / 2 >= 1024 ? 2 : 4;
 }
 
-template <int KS, int NTL>
+template <int KS>
 void launch_gu(const FfnArgs& p, int experts, hipStream_t stream) {
   const dim3 grid(experts * (p.f / (16 * (4 / KS))));
-  hipLaunchKernelGGL((mx_gateup<KS, NTL>), grid, dim3(256), (size_t)NTL * (p.d + 8) * 2, stream, p);
+  hipLaunchKernelGGL(mx_gateup<KS>, grid, dim3(256), mx_stage_bytes(p.d), stream, p);
 }
 
-template <int KS, int YDT, int NTL>
+template <int KS, int YDT>
 void launch_dn(const FfnArgs& p, int experts, hipStream_t stream) {
   const dim3 grid(experts * (p.d / (16 * (4 / KS))));
-  hipLaunchKernelGGL((mx_down<KS, YDT, NTL>), grid, dim3(256), (size_t)NTL * (p.f + 8) * 2, stream, p);
+  hipLaunchKernelGGL((mx_down<KS, YDT>), grid, dim3(256), mx_stage_bytes(p.f), stream, p);
 }
 
-template <int YDT, int NTL>
+template <int YDT>
 void launch_dn_ks(const FfnArgs& p, int experts, hipStream_t stream) {
   switch (mx_ks(experts, p.d)) {
-    case 1: launch_dn<1, YDT, NTL>(p, experts, stream); break;
-    case 2: launch_dn<2, YDT, NTL>(p, experts, stream); break;
-    default: launch_dn<4, YDT, NTL>(p, experts, stream); break;
+    case 1: launch_dn<1, YDT>(p, experts, stream); break;
+    case 2: launch_dn<2, YDT>(p, experts, stream); break;
+    default: launch_dn<4, YDT>(p, experts, stream); break;
   }
 }
 
-template <int NTL>
-void launch_two(const FfnArgs& p, int y_dtype, hipStream_t stream, int experts) {
-  switch (mx_ks(experts, p.f)) {
-    case 1: launch_gu<1, NTL>(p, experts, stream); break;
-    case 2: launch_gu<2, NTL>(p, experts, stream); break;
-    default: launch_gu<4, NTL>(p, experts, stream); break;
-  }
-  if (hipPeekAtLastError() != hipSuccess) return;
-  if (y_dtype == MOE_F32) launch_dn_ks<MOE_F32, NTL>(p, experts, stream);
-  else launch_dn_ks<MOE_BF16, NTL>(p, experts, stream);
-}
-
-template <int KSD, int NTL>
+template <int KSD>
 void launch_one(const FfnArgs& p, int y_dtype, dim3 grid, size_t lds, hipStream_t stream, int n_gu) {
-  if (y_dtype == MOE_F32) hipLaunchKernelGGL((mx_ffn1<KSD, MOE_F32, NTL>), grid, dim3(256), lds, stream, p, n_gu);
-  else hipLaunchKernelGGL((mx_ffn1<KSD, MOE_BF16, NTL>), grid, dim3(256), lds, stream, p, n_gu);
+  if (y_dtype == MOE_F32) hipLaunchKernelGGL((mx_ffn1<KSD, MOE_F32>), grid, dim3(256), lds, stream, p, n_gu);
+  else hipLaunchKernelGGL((mx_ffn1<KSD, MOE_BF16>), grid, dim3(256), lds, stream, p, n_gu);
 }
 
 }  // namespace
@@ -388,24 +451,19 @@ void launch_one(const FfnArgs& p, int y_dtype, dim3 grid, size_t lds, hipStream_
 bool ffn_mx_supported(int d, int f) {
   // strips of 16 rows grouped 4/KS per workgroup (d, f multiples of 64 cover every KS);
   // staged rows must fit the LDS (64 KB per workgroup)
-  return d % 64 == 0 && f % 64 == 0 && (size_t)kMxNTL * (std::max(d, f) + 8) * 2 <= 65536;
+  return d % 64 == 0 && f % 64 == 0 && std::max(mx_stage_bytes(d), mx_stage_bytes(f)) <= 65536;
 }
 
 int launch_ffn_mx(const FfnArgs& p, int y_dtype, hipStream_t stream, int experts) {
   if (experts <= 0) return MOE_OK;
-  launch_two<kMxNTL>(p, y_dtype, stream, experts);
+  switch (mx_ks(experts, p.f)) {
+    case 1: launch_gu<1>(p, experts, stream); break;
+    case 2: launch_gu<2>(p, experts, stream); break;
+    default: launch_gu<4>(p, experts, stream); break;
+  }
   MOE_LAUNCH_CHECK();
-  return MOE_OK;
-}
-
-// The experts with at most 16 rows of a call above 16 tokens: 6 token rows per pass where
-// they fit the LDS, else 4.
-int launch_ffn_mx_few(const FfnArgs& p, int y_dtype, hipStream_t stream, int experts) {
-  if (experts <= 0) return MOE_OK;
-  if ((size_t)kMxNTLWide * (std::max(p.d, p.f) + 8) * 2 <= 65536)
-    launch_two<kMxNTLWide>(p, y_dtype, stream, experts);
-  else
-    launch_two<kMxNTL>(p, y_dtype, stream, experts);
+  if (y_dtype == MOE_F32) launch_dn_ks<MOE_F32>(p, experts, stream);
+  else launch_dn_ks<MOE_BF16>(p, experts, stream);
   MOE_LAUNCH_CHECK();
   return MOE_OK;
 }
@@ -425,11 +483,11 @@ int launch_ffn_mx_one(const FfnArgs& p, int T, int y_dtype, hipStream_t stream, 
   const int n_gu = experts * (p.f / 64);
   const int n_dn = experts * (p.d / (16 * (4 / ksd)));
   const dim3 grid(n_gu + n_dn);
-  const size_t lds = (size_t)kMxNTL * (std::max(p.d, p.f) + 8) * 2;
+  const size_t lds = std::max(mx_stage_bytes(p.d), mx_stage_bytes(p.f));
   switch (ksd) {
-    case 1: launch_one<1, kMxNTL>(p, y_dtype, grid, lds, stream, n_gu); break;
-    case 2: launch_one<2, kMxNTL>(p, y_dtype, grid, lds, stream, n_gu); break;
-    default: launch_one<4, kMxNTL>(p, y_dtype, grid, lds, stream, n_gu); break;
+    case 1: launch_one<1>(p, y_dtype, grid, lds, stream, n_gu); break;
+    case 2: launch_one<2>(p, y_dtype, grid, lds, stream, n_gu); break;
+    default: launch_one<4>(p, y_dtype, grid, lds, stream, n_gu); break;
   }
   MOE_LAUNCH_CHECK();
   return MOE_OK;

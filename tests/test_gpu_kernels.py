@@ -293,18 +293,21 @@ def test_ffn_gemv_row_counts_at_chunk_boundaries(T, counts, ydt):
 
 
 @pytest.mark.parametrize("T,k,d,f,counts", [
-    (12, 4, 512, 4096, [1, 2, 3, 4, 5, 6, 7, 8, 11, 1, 0, 0, 0, 0, 0, 0]),  # 4 rows, one launch
-    (9, 2, 256, 128, [8, 6, 1, 2, 1, 0]),                                   # 4 rows, two launches
-    (40, 3, 320, 192, [1, 5, 6, 7, 11, 12, 13, 16, 17, 32, 0, 0]),          # 6 rows, + grouped GEMM
-    (24, 4, 512, 1024, [6, 12, 13, 16, 1, 7, 18, 23, 0, 0]),                 # 6 rows, + grouped GEMM
+    (12, 4, 512, 4096, [1, 2, 3, 4, 5, 6, 7, 8, 11, 1, 0, 0, 0, 0, 0, 0]),  # one launch
+    (9, 2, 256, 128, [8, 6, 1, 2, 1, 0]),                                   # two launches
+    (40, 3, 320, 192, [1, 5, 6, 7, 11, 12, 13, 16, 17, 32, 0, 0]),          # + grouped GEMM
+    (24, 4, 512, 1024, [6, 12, 13, 16, 1, 7, 18, 23, 0, 0]),                 # + grouped GEMM
+    (12, 2, 7936, 64, [11, 9, 4]),    # K = 7936: at most 2 slices; 4 waves per strip
 ])
 @pytest.mark.parametrize("ydt", [moe.MOE_F32, moe.MOE_BF16])
 def test_ffn_mxfp4_row_counts_at_pass_boundaries(T, k, d, f, counts, ydt):
-    """The MXFP4 weight-streaming kernels stage 4 token rows per pass up to 16 tokens (one
-    launch with h exchanged as tagged entries, or two launches) and 6 above (beside the
-    grouped GEMM, which takes the experts with more than 16 rows): experts with 1 to 16 rows,
-    on both sides of each pass boundary and with up to 3 passes, every row against the oracle
-    on the exactly dequantised weights."""
+    """The MXFP4 weight-streaming kernels stage an expert's rows in blocks over slices of the
+    contraction (up to 4 rows over all of K, 8 over each half, 16 over each quarter, fewer
+    slices where the block would not fit the LDS, as at K = 7936): experts with 1 to 16 rows
+    on both sides of each block size, a short last tile inside a slice (K = 320, 192, 64),
+    through the one-launch form (h exchanged as tagged entries), the two-launch form with one
+    or four waves per strip and, above 16 tokens, beside the grouped GEMM that takes the
+    experts with more rows; every row against the oracle on the exactly dequantised weights."""
     w = configs.Workload("mx_rows", seed=31, T=T, d=d, E=len(counts), k=k, f=f,
                          dtype=gen.MXFP4, alpha=0.0)
     ids = _ids_with_counts(counts, T, k)
