@@ -34,7 +34,9 @@ namespace {
 
 constexpr int kDotMaxT = 8;     // up to this many tokens per call every expert takes the dot path
 constexpr int kDotMaxRows = 4;  // rows per expert the dot path takes when splitting
-constexpr int kMxMaxRows = 16;  // rows an MXFP4 expert may have on the weight-streaming path
+// MXFP4: tokens per call of the one-launch form; above twice as many, the most rows an expert
+// may have on the weight-streaming path
+constexpr int kMxMaxRows = 16;
 // AUTO path: bf16 experts take the grouped GEMM above this many rows per expert on average
 // (T*k / E), MXFP4 experts above kMxGemmMinRowsPerExpert (their streaming path, with the row
 // split above, stays ahead to about 5 rows per expert at Zipf 0.2 and beyond 8 when skewed).
@@ -157,11 +159,15 @@ extern "C" int moe_expert_ffn(const void* x, int act_dtype, const int32_t* perm,
     // at Zipf 1 12% faster; bit-identical).
     if (T <= kMxMaxRows && ws_bytes >= (size_t)A * f * 4) return launch_ffn_mx_one(p, T, y_dtype, stream, experts);
     // An expert has at most T rows (a token picks it once).  The weight-streaming MXFP4
-    // kernels stream an expert's weights once for up to 16 rows (once per 16 rows beyond), so
-    // above kMxMaxRows rows an expert goes to the grouped GEMM, which streams them once per 64
-    // or 256 rows and pays a fixed start-up per workgroup instead.  At most A / (kMxMaxRows + 1)
-    // experts have more rows.
-    if (T <= kMxMaxRows) return launch_ffn_mx(p, y_dtype, stream, experts);
+    // kernels stream an expert's weights once for up to 16 rows (once per 16 rows beyond).  Up
+    // to 2 * kMxMaxRows tokens every expert stays there (at most two streams; d = 4096, f = 2048,
+    // top 6, Zipf 1: T = 24 150 -> 112 us, T = 32 153 -> 129 us against sending the experts above
+    // 16 rows to the grouped GEMM; Zipf 0.2 2% faster); above that, experts with more than kMxMaxRows rows go
+    // to the grouped GEMM, which streams them once per 64 or 256 rows and pays a fixed start-up
+    // per workgroup instead (at T = 64, Zipf 1, moving that split to 32 rows costs 33%: the
+    // streaming launch that runs first grows while the GEMM still waits behind it).  At most
+    // A / (kMxMaxRows + 1) experts have more rows.
+    if (T <= 2 * kMxMaxRows) return launch_ffn_mx(p, y_dtype, stream, experts);
     FfnArgs few = p, many = p;
     few.nmax = kMxMaxRows;
     many.nmin = kMxMaxRows + 1;

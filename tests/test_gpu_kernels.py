@@ -295,8 +295,9 @@ def test_ffn_gemv_row_counts_at_chunk_boundaries(T, counts, ydt):
 @pytest.mark.parametrize("T,k,d,f,counts", [
     (12, 4, 512, 4096, [1, 2, 3, 4, 5, 6, 7, 8, 11, 1, 0, 0, 0, 0, 0, 0]),  # one launch
     (9, 2, 256, 128, [8, 6, 1, 2, 1, 0]),                                   # two launches
-    (40, 3, 320, 192, [1, 5, 6, 7, 11, 12, 13, 16, 17, 32, 0, 0]),          # + grouped GEMM
-    (24, 4, 512, 1024, [6, 12, 13, 16, 1, 7, 18, 23, 0, 0]),                 # + grouped GEMM
+    (40, 3, 320, 192, [1, 5, 6, 7, 11, 12, 13, 16, 17, 32, 0, 0, 0, 0, 0, 0]),  # + grouped GEMM
+    (32, 2, 256, 256, [31, 17, 16, 0, 0, 0, 0, 0]),                          # 2 blocks, no GEMM
+    (24, 4, 512, 1024, [6, 12, 13, 16, 1, 7, 18, 23, 0, 0, 0, 0]),           # 2 blocks of 16
     (12, 2, 7936, 64, [11, 9, 4]),    # K = 7936: at most 2 slices; 4 waves per strip
 ])
 @pytest.mark.parametrize("ydt", [moe.MOE_F32, moe.MOE_BF16])
@@ -306,8 +307,9 @@ def test_ffn_mxfp4_row_counts_at_pass_boundaries(T, k, d, f, counts, ydt):
     slices where the block would not fit the LDS, as at K = 7936): experts with 1 to 16 rows
     on both sides of each block size, a short last tile inside a slice (K = 320, 192, 64),
     through the one-launch form (h exchanged as tagged entries), the two-launch form with one
-    or four waves per strip and, above 16 tokens, beside the grouped GEMM that takes the
-    experts with more rows; every row against the oracle on the exactly dequantised weights."""
+    or four waves per strip (up to 32 tokens every expert, 17 to 31 rows in two blocks of 16)
+    and, above 32 tokens, beside the grouped GEMM that takes the experts with more than 16
+    rows; every row against the oracle on the exactly dequantised weights."""
     w = configs.Workload("mx_rows", seed=31, T=T, d=d, E=len(counts), k=k, f=f,
                          dtype=gen.MXFP4, alpha=0.0)
     ids = _ids_with_counts(counts, T, k)
@@ -388,10 +390,10 @@ def test_ffn_mxfp4_parity(T, E, k, d, f, ydt):
 
 
 @pytest.mark.parametrize("T,E,k,d,f,alpha", [(64, 64, 4, 512, 256, 1.0), (48, 256, 6, 1088, 320, 1.0),
-                                             (32, 32, 4, 320, 192, 0.5)])
+                                             (40, 32, 4, 320, 192, 0.5)])
 @pytest.mark.parametrize("ydt", [moe.MOE_F32, moe.MOE_BF16])
 def test_ffn_mxfp4_row_split_parity(T, E, k, d, f, alpha, ydt):
-    """MXFP4 decode-shaped calls above 16 tokens: experts with at most 16 rows stay on the
+    """MXFP4 decode-shaped calls above 32 tokens: experts with at most 16 rows stay on the
     weight-streaming kernels, the others go to the grouped GEMM; both groups are present and
     every row equals the oracle."""
     w = configs.Workload("mx_split", seed=27, T=T, d=d, E=E, k=k, f=f, dtype=gen.MXFP4, alpha=alpha)
