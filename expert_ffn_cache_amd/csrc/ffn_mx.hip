@@ -48,7 +48,8 @@ __host__ __device__ constexpr int mx_block_elems(int K, int C) { return 4 * C * 
 __host__ __device__ constexpr int mx_max_slices(int K) {
   return mx_block_elems(K, 4) <= 32768 ? 4 : mx_block_elems(K, 2) <= 32768 ? 2 : 1;
 }
-// slices for an expert of n rows (4 rows per slice count), and the LDS a launch stages in
+// slices for an expert of n rows (a block holds 4 rows per slice), and the LDS bytes a launch
+// stages the rows in
 __host__ __device__ constexpr int mx_slices(int n, int K) {
   return n <= 4 ? 1 : n <= 8 && mx_max_slices(K) >= 2 ? 2 : mx_max_slices(K);
 }
@@ -280,45 +281,45 @@ __device__ __forceinline__ void gu_body(const FfnArgs& p, int bid, f32x4* red) {
   // blocks of up to 4 C rows, each over C slices of K (compiled per C, so one slice is the
   // plain pass over all of K)
   auto blocks = [&](auto c_tag) {
-  constexpr int C = decltype(c_tag)::value;
-  const int rb = 4 * C, tps = mx_slice_tiles(nk, C), stride = mx_slice_stride(K, C);
-  for (int m0 = 0; m0 < n; m0 += rb) {
-    const int nt = min(rb, n - m0);
-    auto row_of = [&](int t) { return p.perm[n0 + m0 + t] / p.k; };
-    f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-    if constexpr (C == 1) {
-      MxTile<2> ring[kMxAhead];
-      mx_ring_fill<2, KS>(ring, cb, sb, ks, 0, nk, nk, krem, lane);
-      mx_stage(xs, (const uint16_t*)p.x, K, 0, K, K + 8, nt, row_of);
-      mx_ring_run<2, KS>(ring, cb, sb, xs + min(col, nt - 1) * (K + 8), ks, 0, nk, nk, krem, lane, acc);
-    } else {
-      for (int t0 = 0; t0 < nk; t0 += tps) {
-        const int t1 = min(nk, t0 + tps), e0 = t0 * 128, len = min(K, t1 * 128) - e0;
+    constexpr int C = decltype(c_tag)::value;
+    const int rb = 4 * C, tps = mx_slice_tiles(nk, C), stride = mx_slice_stride(K, C);
+    for (int m0 = 0; m0 < n; m0 += rb) {
+      const int nt = min(rb, n - m0);
+      auto row_of = [&](int t) { return p.perm[n0 + m0 + t] / p.k; };
+      f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+      if constexpr (C == 1) {
         MxTile<2> ring[kMxAhead];
-        mx_ring_fill<2, KS>(ring, cb, sb, ks, t0, t1, nk, krem, lane);
-        mx_stage(xs, (const uint16_t*)p.x, K, e0, len, stride, nt, row_of);
-        mx_ring_run<2, KS>(ring, cb, sb, xs + min(col, nt - 1) * stride, ks, t0, t1, nk, krem, lane, acc);
+        mx_ring_fill<2, KS>(ring, cb, sb, ks, 0, nk, nk, krem, lane);
+        mx_stage(xs, (const uint16_t*)p.x, K, 0, K, K + 8, nt, row_of);
+        mx_ring_run<2, KS>(ring, cb, sb, xs + min(col, nt - 1) * (K + 8), ks, 0, nk, nk, krem, lane, acc);
+      } else {
+        for (int t0 = 0; t0 < nk; t0 += tps) {
+          const int t1 = min(nk, t0 + tps), e0 = t0 * 128, len = min(K, t1 * 128) - e0;
+          MxTile<2> ring[kMxAhead];
+          mx_ring_fill<2, KS>(ring, cb, sb, ks, t0, t1, nk, krem, lane);
+          mx_stage(xs, (const uint16_t*)p.x, K, e0, len, stride, nt, row_of);
+          mx_ring_run<2, KS>(ring, cb, sb, xs + min(col, nt - 1) * stride, ks, t0, t1, nk, krem, lane, acc);
+        }
       }
-    }
-    if (ENT) mx_reduce_buf<2, KS>(acc, strip, ks, lane, red);
-    else mx_reduce<2, KS>(acc, strip, ks, lane);
-    if (ks == 0) {
-      // lane holds C[4 kg + i][col]: token rows 4 kg + i, unit 16 rt + col
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = 4 * kg + i;
-        const uint32_t hv = f32_to_bf16(silu(acc[0][i]) * acc[1][i]);
-        if (ENT) {
-          const uint32_t nv = (uint32_t)__shfl_xor((int)hv, 1);  // unit 16 rt + (col ^ 1)
-          if (t < nt && !(col & 1))
-            mx_coh_store64((uint64_t*)p.h + ((size_t)(n0 + m0 + t) * p.f + 16 * rt + col) / 2,
-                           (uint64_t)(hv | nv << 16) | (uint64_t)kMxTag << 32);
-        } else if (t < nt) {
-          H[(size_t)(n0 + m0 + t) * p.f + 16 * rt + col] = (uint16_t)hv;
+      if (ENT) mx_reduce_buf<2, KS>(acc, strip, ks, lane, red);
+      else mx_reduce<2, KS>(acc, strip, ks, lane);
+      if (ks == 0) {
+        // lane holds C[4 kg + i][col]: token rows 4 kg + i, unit 16 rt + col
+  #pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = 4 * kg + i;
+          const uint32_t hv = f32_to_bf16(silu(acc[0][i]) * acc[1][i]);
+          if (ENT) {
+            const uint32_t nv = (uint32_t)__shfl_xor((int)hv, 1);  // unit 16 rt + (col ^ 1)
+            if (t < nt && !(col & 1))
+              mx_coh_store64((uint64_t*)p.h + ((size_t)(n0 + m0 + t) * p.f + 16 * rt + col) / 2,
+                             (uint64_t)(hv | nv << 16) | (uint64_t)kMxTag << 32);
+          } else if (t < nt) {
+            H[(size_t)(n0 + m0 + t) * p.f + 16 * rt + col] = (uint16_t)hv;
+          }
         }
       }
     }
-  }
   };
   switch (mx_slices(n, K)) {
     case 1: blocks(std::integral_constant<int, 1>{}); break;
@@ -350,42 +351,42 @@ __device__ __forceinline__ void dn_body(const FfnArgs& p, int bid, f32x4* red) {
   const uint8_t* const sb[1] = {W + 3 * fd / 2 + 2 * (fd / 32) + (size_t)rt * (K / 2)};
   const int col = lane & 15, kg = lane >> 4;
   auto blocks = [&](auto c_tag) {  // as in gate/up
-  constexpr int C = decltype(c_tag)::value;
-  const int rb = 4 * C, tps = mx_slice_tiles(nk, C), stride = mx_slice_stride(K, C);
-  for (int m0 = 0; m0 < n; m0 += rb) {
-    const int nt = min(rb, n - m0);
-    auto row_of = [&](int t) { return n0 + m0 + t; };
-    f32x4 acc[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
-    if constexpr (C == 1) {
-      MxTile<1> ring[kMxAhead];
-      mx_ring_fill<1, KS>(ring, cb, sb, ks, 0, nk, nk, krem, lane);
-      if (ENT) mx_stage_ent<true>(hs, (const uint64_t*)p.h, K, 0, K, K + 8, nt, n0 + m0, p.status);
-      else mx_stage(hs, (const uint16_t*)p.h, K, 0, K, K + 8, nt, row_of);
-      mx_ring_run<1, KS>(ring, cb, sb, hs + min(col, nt - 1) * (K + 8), ks, 0, nk, nk, krem, lane, acc);
-    } else {
-      for (int t0 = 0; t0 < nk; t0 += tps) {
-        const int t1 = min(nk, t0 + tps), e0 = t0 * 128, len = min(K, t1 * 128) - e0;
+    constexpr int C = decltype(c_tag)::value;
+    const int rb = 4 * C, tps = mx_slice_tiles(nk, C), stride = mx_slice_stride(K, C);
+    for (int m0 = 0; m0 < n; m0 += rb) {
+      const int nt = min(rb, n - m0);
+      auto row_of = [&](int t) { return n0 + m0 + t; };
+      f32x4 acc[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
+      if constexpr (C == 1) {
         MxTile<1> ring[kMxAhead];
-        mx_ring_fill<1, KS>(ring, cb, sb, ks, t0, t1, nk, krem, lane);
-        if (ENT) mx_stage_ent<false>(hs, (const uint64_t*)p.h, K, e0, len, stride, nt, n0 + m0, p.status);
-        else mx_stage(hs, (const uint16_t*)p.h, K, e0, len, stride, nt, row_of);
-        mx_ring_run<1, KS>(ring, cb, sb, hs + min(col, nt - 1) * stride, ks, t0, t1, nk, krem, lane, acc);
+        mx_ring_fill<1, KS>(ring, cb, sb, ks, 0, nk, nk, krem, lane);
+        if (ENT) mx_stage_ent<true>(hs, (const uint64_t*)p.h, K, 0, K, K + 8, nt, n0 + m0, p.status);
+        else mx_stage(hs, (const uint16_t*)p.h, K, 0, K, K + 8, nt, row_of);
+        mx_ring_run<1, KS>(ring, cb, sb, hs + min(col, nt - 1) * (K + 8), ks, 0, nk, nk, krem, lane, acc);
+      } else {
+        for (int t0 = 0; t0 < nk; t0 += tps) {
+          const int t1 = min(nk, t0 + tps), e0 = t0 * 128, len = min(K, t1 * 128) - e0;
+          MxTile<1> ring[kMxAhead];
+          mx_ring_fill<1, KS>(ring, cb, sb, ks, t0, t1, nk, krem, lane);
+          if (ENT) mx_stage_ent<false>(hs, (const uint64_t*)p.h, K, e0, len, stride, nt, n0 + m0, p.status);
+          else mx_stage(hs, (const uint16_t*)p.h, K, e0, len, stride, nt, row_of);
+          mx_ring_run<1, KS>(ring, cb, sb, hs + min(col, nt - 1) * stride, ks, t0, t1, nk, krem, lane, acc);
+        }
       }
-    }
-    if (ENT) mx_reduce_buf<1, KS>(acc, strip, ks, lane, red);
-    else mx_reduce<1, KS>(acc, strip, ks, lane);
-    if (ks == 0) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = 4 * kg + i;
-        if (t < nt) {
-          const size_t o = (size_t)(n0 + m0 + t) * p.d + 16 * rt + col;
-          if (YDT == MOE_F32) ((float*)p.y)[o] = acc[0][i];
-          else ((uint16_t*)p.y)[o] = f32_to_bf16(acc[0][i]);
+      if (ENT) mx_reduce_buf<1, KS>(acc, strip, ks, lane, red);
+      else mx_reduce<1, KS>(acc, strip, ks, lane);
+      if (ks == 0) {
+  #pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = 4 * kg + i;
+          if (t < nt) {
+            const size_t o = (size_t)(n0 + m0 + t) * p.d + 16 * rt + col;
+            if (YDT == MOE_F32) ((float*)p.y)[o] = acc[0][i];
+            else ((uint16_t*)p.y)[o] = f32_to_bf16(acc[0][i]);
+          }
         }
       }
     }
-  }
   };
   switch (mx_slices(n, K)) {
     case 1: blocks(std::integral_constant<int, 1>{}); break;
